@@ -1,0 +1,248 @@
+"""Thin ctypes binding of libattn_mi355x.so (include/attn.h).
+
+Argument marshalling only: shapes, strides, device pointers and the current
+HIP stream go to the C ABI; every step of the computation runs in the
+library's HIP kernels.  torch is used for device memory and streams.  There is
+no fallback: if the library is missing, every call raises.
+
+    o, lse = fwd(q, k, v, causal=False, offset=0, seqlens_q=None, seqlens_k=None)
+    dq, dk, dv = bwd(q, k, v, o, lse, do, causal=..., offset=..., ...)
+
+Tensors are [B, H, n, d] with unit stride in d (any batch/head/row strides that
+are multiples of 8 elements), dtype torch.bfloat16 or torch.float32, on the GPU.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libattn_mi355x.so")
+
+OK = 0
+INVALID_ARG = 1
+EMPTY_ROW = 2
+UNSUPPORTED = 3
+WORKSPACE = 4
+HIP = 5
+F32 = 0
+BF16 = 1
+
+# every symbol the header declares
+EXPORTS = ("attn_validate", "attn_bwd_workspace_size", "attn_fwd", "attn_bwd",
+           "attn_status_string", "attn_version")
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        msg = status_string(status) if _lib_or_none() else f"status {status}"
+        super().__init__(f"{what}: {msg} (status {status})" if what else f"{msg} (status {status})")
+
+
+class Mask(ctypes.Structure):
+    _fields_ = [("causal", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("causal_offset", ctypes.c_int64),
+                ("seqlens_q", ctypes.POINTER(ctypes.c_int32)),
+                ("seqlens_k", ctypes.POINTER(ctypes.c_int32))]
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H_q", ctypes.c_int32), ("H_kv", ctypes.c_int32),
+                ("n_q", ctypes.c_int32), ("n_k", ctypes.c_int32),
+                ("d_h", ctypes.c_int32), ("d_v", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3),
+                ("v_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3)]
+
+
+_LIB = None
+
+
+def _lib_or_none():
+    return _LIB
+
+
+def lib():
+    """Load the library (once).  Raises if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m exact_masked_scaled_amd.build` (there is no fallback path)")
+    L = ctypes.CDLL(LIB_PATH)
+    P, M = ctypes.POINTER(Problem), ctypes.POINTER(Mask)
+    vp = ctypes.c_void_p
+    L.attn_validate.argtypes = [P, M]
+    L.attn_validate.restype = ctypes.c_int
+    L.attn_bwd_workspace_size.argtypes = [P]
+    L.attn_bwd_workspace_size.restype = ctypes.c_size_t
+    L.attn_fwd.argtypes = [P, M, vp, vp, vp, vp, vp, vp]
+    L.attn_fwd.restype = ctypes.c_int
+    L.attn_bwd.argtypes = [P, M, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.attn_bwd.restype = ctypes.c_int
+    L.attn_status_string.argtypes = [ctypes.c_int]
+    L.attn_status_string.restype = ctypes.c_char_p
+    L.attn_version.argtypes = []
+    L.attn_version.restype = ctypes.c_int32
+    _LIB = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().attn_status_string(int(status)).decode()
+
+
+# ---------------------------------------------------------------------------
+# problem / mask construction (plain integers; usable without a GPU)
+# ---------------------------------------------------------------------------
+
+def make_problem(B, H_q, H_kv, n_q, n_k, d_h, d_v, dtype, q_stride=None, k_stride=None,
+                 v_stride=None, o_stride=None) -> Problem:
+    def contig(H, n, d):
+        return (H * n * d, n * d, d)
+    p = Problem()
+    p.B, p.H_q, p.H_kv, p.n_q, p.n_k, p.d_h, p.d_v, p.dtype = B, H_q, H_kv, n_q, n_k, d_h, d_v, dtype
+    p.q_stride[:] = q_stride or contig(H_q, n_q, d_h)
+    p.k_stride[:] = k_stride or contig(H_kv, n_k, d_h)
+    p.v_stride[:] = v_stride or contig(H_kv, n_k, d_v)
+    p.o_stride[:] = o_stride or contig(H_q, n_q, d_v)
+    return p
+
+
+def make_mask(causal=False, offset=0, seqlens_q: Optional[Sequence[int]] = None,
+              seqlens_k: Optional[Sequence[int]] = None):
+    """Returns (Mask, keepalive) -- the host length arrays must outlive the call."""
+    m = Mask()
+    m.causal = 1 if causal else 0
+    m.reserved = 0
+    m.causal_offset = int(offset)
+    keep = []
+    for name, lens in (("seqlens_q", seqlens_q), ("seqlens_k", seqlens_k)):
+        if lens is None:
+            setattr(m, name, None)
+        else:
+            arr = (ctypes.c_int32 * len(lens))(*[int(x) for x in lens])
+            keep.append(arr)
+            setattr(m, name, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)))
+    return m, keep
+
+
+def validate(prob: Problem, mask: Mask) -> int:
+    return int(lib().attn_validate(ctypes.byref(prob), ctypes.byref(mask)))
+
+
+def workspace_size(prob: Problem) -> int:
+    return int(lib().attn_bwd_workspace_size(ctypes.byref(prob)))
+
+
+# ---------------------------------------------------------------------------
+# torch entry points
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _check4(name, t, dtype):
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be [B, H, n, d]")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.shape[-1] > 0 and t.stride(-1) != 1:
+        raise ValueError(f"{name} must have unit stride in its last dimension")
+
+
+def _strides(t):
+    return tuple(int(s) for s in t.stride()[:3])
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else ctypes.c_void_p(0)
+
+
+def _problem_from(q, k, v, o_like_stride=None):
+    B, H_q, n_q, d_h = q.shape
+    _, H_kv, n_k, d_v = v.shape
+    return make_problem(B, H_q, H_kv, n_q, n_k, d_h, d_v, _dtype_code(q), _strides(q), _strides(k),
+                        _strides(v), o_like_stride)
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def fwd(q, k, v, *, causal=False, offset=0, seqlens_q=None, seqlens_k=None, out=None, lse=None,
+        stream=None):
+    """O [B,H_q,n_q,d_v] (dtype of q) and lse [B,H_q,n_q] float32."""
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check4(name, t, q.dtype)
+    B, H_q, n_q, _ = q.shape
+    d_v = v.shape[-1]
+    if out is None:
+        out = torch.empty(B, H_q, n_q, d_v, dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty(B, H_q, n_q, dtype=torch.float32, device=q.device)
+    _check4("out", out, q.dtype)
+    if not lse.is_contiguous() or lse.dtype != torch.float32:
+        raise ValueError("lse must be contiguous float32")
+    prob = _problem_from(q, k, v, _strides(out))
+    mask, keep = make_mask(causal, offset, seqlens_q, seqlens_k)
+    st = lib().attn_fwd(ctypes.byref(prob), ctypes.byref(mask), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                        _ptr(lse), _stream(stream))
+    del keep
+    if st != OK:
+        raise AttnError(st, "attn_fwd")
+    return out, lse
+
+
+def bwd(q, k, v, o, lse, do, *, causal=False, offset=0, seqlens_q=None, seqlens_k=None,
+        dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """G_Q, G_K, G_V.  ``do`` must have the strides of ``o``; outputs are
+    allocated contiguous unless given (then with the strides of q / k / v)."""
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check4(name, t, q.dtype)
+    if do.stride() != o.stride():
+        raise ValueError("do must have the strides of o")
+    if dq is None:
+        dq = torch.empty_like(q, memory_format=torch.contiguous_format)
+        if dq.stride() != q.stride():
+            raise ValueError("q must be contiguous when dq is not given")
+    if dk is None:
+        dk = torch.empty_like(k)
+        if dk.stride() != k.stride():
+            raise ValueError("k must be contiguous when dk is not given")
+    if dv is None:
+        dv = torch.empty_like(v)
+        if dv.stride() != v.stride():
+            raise ValueError("v must be contiguous when dv is not given")
+    prob = _problem_from(q, k, v, _strides(o))
+    need = workspace_size(prob)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    mask, keep = make_mask(causal, offset, seqlens_q, seqlens_k)
+    st = lib().attn_bwd(ctypes.byref(prob), ctypes.byref(mask), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                        _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                        ctypes.c_size_t(workspace.numel()), _stream(stream))
+    del keep
+    if st != OK:
+        raise AttnError(st, "attn_bwd")
+    return dq, dk, dv

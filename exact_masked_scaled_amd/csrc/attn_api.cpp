@@ -1,0 +1,171 @@
+// Host side of the C ABI declared in include/attn.h: argument checks, kernel
+// argument packing, batch chunking and launch order.  Pure C++; the HIP
+// launches live in the kernel translation units.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "attn_internal.h"
+
+using namespace attn;
+
+namespace {
+
+constexpr size_t kWsAlign = 256;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t esize(int dtype) { return dtype == ATTN_BF16 ? 2 : 4; }
+
+// Fill everything but pointers and lengths.
+void fill_common(KernelParams& kp, const attn_problem& p, const attn_mask& m) {
+  memset(&kp, 0, sizeof(kp));
+  kp.q_sb = p.q_stride[0]; kp.q_sh = p.q_stride[1]; kp.q_sr = p.q_stride[2];
+  kp.k_sb = p.k_stride[0]; kp.k_sh = p.k_stride[1]; kp.k_sr = p.k_stride[2];
+  kp.v_sb = p.v_stride[0]; kp.v_sh = p.v_stride[1]; kp.v_sr = p.v_stride[2];
+  kp.o_sb = p.o_stride[0]; kp.o_sh = p.o_stride[1]; kp.o_sr = p.o_stride[2];
+  kp.H_q = p.H_q; kp.H_kv = p.H_kv; kp.n_q = p.n_q; kp.n_k = p.n_k;
+  kp.group = p.H_q / p.H_kv;
+  kp.causal = m.causal;
+  // j <= i + off with off >= n_k is no restriction at all; offsets below zero
+  // only reach here when no row is active.
+  kp.offset = (int32_t)std::min<int64_t>(std::max<int64_t>(m.causal_offset, 0), p.n_k);
+  kp.scale = (float)(1.0 / sqrt((double)p.d_h));
+  kp.scale_log2 = (float)(1.4426950408889634 / sqrt((double)p.d_h));
+  kp.has_lens = (m.seqlens_q != nullptr || m.seqlens_k != nullptr) ? 1 : 0;
+}
+
+// Sequence chunk [b0, b0 + nb): lengths and unit counts.
+void fill_chunk(KernelParams& kp, const attn_problem& p, const attn_mask& m, int b0, int nb) {
+  kp.B = nb;
+  if (kp.has_lens) {
+    for (int i = 0; i < nb; ++i) {
+      kp.lens_q[i] = m.seqlens_q ? m.seqlens_q[b0 + i] : p.n_q;
+      kp.lens_k[i] = m.seqlens_k ? m.seqlens_k[b0 + i] : p.n_k;
+    }
+  }
+  kp.groups = nb * p.H_kv;
+  kp.xcd_map = (kp.groups % 8 == 0) ? 1 : 0;
+}
+
+template <typename T>
+const T* off(const T* base, int64_t elems, size_t es) {
+  return base ? (const T*)((const char*)base + elems * (int64_t)es) : nullptr;
+}
+template <typename T>
+T* off(T* base, int64_t elems, size_t es) {
+  return base ? (T*)((char*)base + elems * (int64_t)es) : nullptr;
+}
+
+int chunk_size(const KernelParams& kp, int B) { return kp.has_lens ? kMaxBatchChunk : std::max(B, 1); }
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_validate(const attn_problem* prob, const attn_mask* mask) {
+  return validate_problem(prob, mask);
+}
+
+size_t attn_bwd_workspace_size(const attn_problem* prob) {
+  if (prob == nullptr || prob->B < 0 || prob->H_q < 0 || prob->n_q < 0 || prob->d_h < 0) return 0;
+  const size_t rows = (size_t)prob->B * (size_t)prob->H_q * (size_t)prob->n_q;
+  return align_up(rows * sizeof(float), kWsAlign) + rows * (size_t)prob->d_h * sizeof(float);
+}
+
+attn_status attn_fwd(const attn_problem* prob, const attn_mask* mask, const void* Q, const void* K,
+                     const void* V, void* O, float* lse, void* stream) {
+  attn_status st = validate_problem(prob, mask);
+  if (st != ATTN_OK) return st;
+  const attn_problem& p = *prob;
+  const attn_mask& m = *mask;
+  if (p.B == 0 || p.n_q == 0) return ATTN_OK;
+  if (!Q || !O || !lse || !aligned16(Q) || !aligned16(O) || !aligned16(lse)) return ATTN_ERR_INVALID_ARG;
+  if (p.n_k > 0 && (!K || !V || !aligned16(K) || !aligned16(V))) return ATTN_ERR_INVALID_ARG;
+  const size_t es = esize(p.dtype);
+  KernelParams kp;
+  fill_common(kp, p, m);
+  const int nqblk = (p.n_q + fwd_block_rows(p.dtype) - 1) / fwd_block_rows(p.dtype);
+  const int cs = chunk_size(kp, p.B);
+  for (int b0 = 0; b0 < p.B; b0 += cs) {
+    const int nb = std::min(cs, p.B - b0);
+    fill_chunk(kp, p, m, b0, nb);
+    kp.per_group = kp.group * nqblk;
+    kp.q = off(Q, b0 * p.q_stride[0], es);
+    kp.k = off(K, b0 * p.k_stride[0], es);
+    kp.v = off(V, b0 * p.v_stride[0], es);
+    kp.o_out = off(O, b0 * p.o_stride[0], es);
+    kp.lse = lse + (int64_t)b0 * p.H_q * p.n_q;
+    if (launch_fwd(kp, p.dtype, p.d_h, p.d_v, stream) != 0) return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
+attn_status attn_bwd(const attn_problem* prob, const attn_mask* mask, const void* Q, const void* K,
+                     const void* V, const void* O, const float* lse, const void* dO, void* dQ, void* dK,
+                     void* dV, void* workspace, size_t workspace_bytes, void* stream) {
+  attn_status st = validate_problem(prob, mask);
+  if (st != ATTN_OK) return st;
+  const attn_problem& p = *prob;
+  const attn_mask& m = *mask;
+  if (p.B == 0 || (p.n_q == 0 && p.n_k == 0)) return ATTN_OK;
+  const bool has_q = p.n_q > 0, has_k = p.n_k > 0;
+  if (has_q && (!Q || !O || !lse || !dO || !dQ || !aligned16(Q) || !aligned16(O) || !aligned16(lse) ||
+                !aligned16(dO) || !aligned16(dQ)))
+    return ATTN_ERR_INVALID_ARG;
+  if (has_k && (!K || !V || !dK || !dV || !aligned16(K) || !aligned16(V) || !aligned16(dK) ||
+                !aligned16(dV)))
+    return ATTN_ERR_INVALID_ARG;
+  const size_t need = attn_bwd_workspace_size(prob);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || ((uintptr_t)workspace % kWsAlign) != 0))
+    return ATTN_ERR_WORKSPACE;
+  const size_t es = esize(p.dtype);
+  const size_t rows = (size_t)p.B * p.H_q * p.n_q;
+  float* delta = (float*)workspace;
+  float* dq_acc = (float*)((char*)workspace + align_up(rows * sizeof(float), kWsAlign));
+  KernelParams kp;
+  fill_common(kp, p, m);
+  const int nkblk = (p.n_k + bwd_block_keys(p.dtype) - 1) / bwd_block_keys(p.dtype);
+  const int cs = chunk_size(kp, p.B);
+  for (int b0 = 0; b0 < p.B; b0 += cs) {
+    const int nb = std::min(cs, p.B - b0);
+    fill_chunk(kp, p, m, b0, nb);
+    kp.per_group = nkblk;
+    const int64_t row0 = (int64_t)b0 * p.H_q * p.n_q;
+    kp.q = off(Q, b0 * p.q_stride[0], es);
+    kp.k = off(K, b0 * p.k_stride[0], es);
+    kp.v = off(V, b0 * p.v_stride[0], es);
+    kp.o = off(O, b0 * p.o_stride[0], es);
+    kp.dout = off(dO, b0 * p.o_stride[0], es);
+    kp.lse = const_cast<float*>(lse) + (lse ? row0 : 0);
+    kp.delta = delta ? delta + row0 : nullptr;
+    kp.dq_acc = dq_acc ? dq_acc + row0 * p.d_h : nullptr;
+    kp.dq = off(dQ, b0 * p.q_stride[0], es);
+    kp.dk = off(dK, b0 * p.k_stride[0], es);
+    kp.dv = off(dV, b0 * p.v_stride[0], es);
+    if (launch_bwd_pre(kp, p.dtype, p.d_h, p.d_v, stream) != 0) return ATTN_ERR_HIP;
+    if (launch_bwd_main(kp, p.dtype, p.d_h, p.d_v, stream) != 0) return ATTN_ERR_HIP;
+    if (launch_bwd_dq(kp, p.dtype, p.d_h, stream) != 0) return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
+const char* attn_status_string(attn_status s) {
+  switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID_ARG: return "invalid argument";
+    case ATTN_ERR_EMPTY_ROW: return "an active query row has an empty visible set";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported head width or dtype";
+    case ATTN_ERR_WORKSPACE: return "backward workspace missing, too small or misaligned";
+    case ATTN_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int32_t attn_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,161 @@
+// Device-side building blocks for the gfx950 attention kernels.
+//
+// MFMA shapes used (CDNA4):
+//   bf16: v_mfma_f32_32x32x16_bf16   A 32x16, B 16x32, C 32x32 float32
+//   fp32: v_mfma_f32_32x32x2_f32     issued 8 times per 16-wide k chunk
+// Lane layouts (verified on the device):
+//   A operand:  lane l holds A[m = l % 32][k in chunk(l / 32)]
+//   B operand:  lane l holds B[k in chunk(l / 32)][n = l % 32]
+//   C result:   lane l holds C[m][n = l % 32] for m = 8*(e/4) + 4*(l/32) + e%4,
+//               e = 0..15 (the "C-layout" k order).
+// A 16-wide k chunk of an operand is 8 values per lane.  Two k orders are used:
+//   row order:  k = 8*(l/32) + e          (contiguous 16-byte row reads)
+//   C order:    k = 8*(e/4) + 4*(l/32) + e%4
+// Both operands of one product always use the same order, so any order is a
+// valid split of the sum over k; the C order is the one a C-layout result has
+// when it is fed back as an operand, and the one the LDS transpose read
+// (ds_read_b64_tr_b16) produces.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+#define ATTN_LDS __attribute__((address_space(3)))
+
+template <typename T> struct Op;
+template <> struct Op<__bf16> { using type = bf16x8; };
+template <> struct Op<float> { using type = f32x8; };
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// ---------------------------------------------------------------- MFMA
+__device__ __forceinline__ void mma(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x16& acc, const f32x8& a, const f32x8& b) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], b[e], acc, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- conversions
+template <typename T> __device__ __forceinline__ typename Op<T>::type to_op(const float* x);
+template <> __device__ __forceinline__ bf16x8 to_op<__bf16>(const float* x) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (__bf16)x[e];  // v_cvt_pk_bf16_f32: nearest-even
+  return r;
+}
+template <> __device__ __forceinline__ f32x8 to_op<float>(const float* x) {
+  f32x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = x[e];
+  return r;
+}
+
+template <typename T> __device__ __forceinline__ typename Op<T>::type zero_op() {
+  typename Op<T>::type r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (T)0.0f;
+  return r;
+}
+
+// ---------------------------------------------------------------- 8-element row reads
+// 8 consecutive elements starting at p (16-byte aligned): one or two b128 reads.
+template <typename T> __device__ __forceinline__ typename Op<T>::type ld8(const T* p);
+template <> __device__ __forceinline__ bf16x8 ld8<__bf16>(const __bf16* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+template <> __device__ __forceinline__ f32x8 ld8<float>(const float* p) {
+  f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+  f32x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+  r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+  return r;
+}
+
+// ---------------------------------------------------------------- transposed reads
+// Operand chunk in C order from a row-major LDS matrix X[k][n] (n contiguous,
+// row stride `ld` elements): lane l receives X[kb + 8*(e/4) + 4*(l/32) + e%4]
+// [nb + l % 32] for e = 0..7.  Usable as an A operand (m = n index) or a B
+// operand (n index), contracting over k.
+//
+// bf16: two ds_read_b64_tr_b16.  Within each 16-lane group the instruction
+// hands lane t element e' of the 64-bit word read by source lane 4*e' + t/4,
+// column t % 4; so source lane s points at row (s / 4), columns 4*(s % 4).
+template <typename T> __device__ __forceinline__ typename Op<T>::type ld_tr(const T* X, int ld, int kb, int nb);
+template <> __device__ __forceinline__ bf16x8 ld_tr<__bf16>(const __bf16* X, int ld, int kb, int nb) {
+  const int l = lane_id();
+  const int s = l & 15, grp = l >> 4;
+  const __bf16* p0 = X + (kb + 4 * (grp >> 1) + (s >> 2)) * ld + nb + 16 * (grp & 1) + 4 * (s & 3);
+  const __bf16* p1 = p0 + 8 * ld;
+  i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4*)(p0));
+  i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4*)(p1));
+  union { i16x4 v[2]; bf16x8 b; } u;
+  u.v[0] = lo;
+  u.v[1] = hi;
+  return u.b;
+}
+template <> __device__ __forceinline__ f32x8 ld_tr<float>(const float* X, int ld, int kb, int nb) {
+  const int l = lane_id();
+  const float* p = X + (kb + 4 * (l >> 5)) * ld + nb + (l & 31);
+  f32x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = p[(8 * (e >> 2) + (e & 3)) * ld];
+  return r;
+}
+
+// ---------------------------------------------------------------- cross-lane
+// Value of lane l ^ 32 (v_permlane32_swap: swaps the upper half of the first
+// operand with the lower half of the second).
+__device__ __forceinline__ float partner32(float x) {
+  const unsigned u = __float_as_uint(x);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const unsigned lo = r[0], hi = r[1];
+  return __uint_as_float((lane_id() < 32) ? hi : lo);
+}
+
+// ---------------------------------------------------------------- stores
+template <typename T> __device__ __forceinline__ void st4(T* p, float a, float b, float c, float d);
+template <> __device__ __forceinline__ void st4<__bf16>(__bf16* p, float a, float b, float c, float d) {
+  bf16x4 v;
+  v[0] = (__bf16)a; v[1] = (__bf16)b; v[2] = (__bf16)c; v[3] = (__bf16)d;
+  *reinterpret_cast<bf16x4*>(p) = v;
+}
+template <> __device__ __forceinline__ void st4<float>(float* p, float a, float b, float c, float d) {
+  f32x4 v;
+  v[0] = a; v[1] = b; v[2] = c; v[3] = d;
+  *reinterpret_cast<f32x4*>(p) = v;
+}
+
+// ---------------------------------------------------------------- work mapping
+// Work is grouped in units (a sequence and a KV head) of `per_group` items.
+// With xcd_map, unit u runs on XCD u % 8: workgroups are dealt to the 8 XCDs
+// round-robin, so slot `wg / 8` of XCD `wg % 8` takes the slot-th item of that
+// XCD's units, and all items of one unit share one XCD's L2.  Returns false
+// for the padding workgroups of a unit count that is not a multiple of 8.
+__device__ __forceinline__ bool map_work(int wg, int groups, int per_group, int xcd_map,
+                                         int& unit, int& item) {
+  if (!xcd_map) {
+    unit = wg / per_group;
+    item = wg - unit * per_group;
+    return unit < groups;
+  }
+  const int xcd = wg & 7, slot = wg >> 3;
+  const int t = slot / per_group;
+  item = slot - t * per_group;
+  unit = xcd + 8 * t;
+  return unit < groups;
+}
+
+}  // namespace attn

@@ -1,0 +1,263 @@
+// Forward kernel: O = softmax_V(Q K^T / sqrt(d_h)) V and the per-row
+// logsumexp ("Appendix A.10 - Attention matrices and backpropagation",
+// glenzli.com, eqs. A.10.1-A.10.3; the visible sets of secs. A.10.1/A.10.6).
+//
+// One workgroup = 4 waves = 128 query rows of one (sequence, query head); a
+// wave owns 32 rows.  Keys stream through LDS in tiles of 64 (double
+// buffered).  Per tile a wave computes the TRANSPOSED score tile
+// S^T = K Q^T on MFMA, so that a lane owns one query row (lane % 32) and its
+// row statistics need one cross-lane exchange (with lane ^ 32).  The
+// probabilities then feed O^T += V^T P^T directly as the B operand (their
+// C-layout order is the operand's k order); V^T comes from LDS through the
+// transpose read.  The softmax is the max-subtracted one of eq. A.10.2,
+// evaluated online: a running max m and sum l per row, rescaling the
+// accumulator when m grows.  Whole key tiles beyond a row block's visible
+// range are skipped; tiles that straddle the causal diagonal or the key
+// length get an element mask.
+#include "attn_device.h"
+#include "attn_internal.h"
+
+namespace attn {
+
+template <typename T, int DH, int DV>
+struct FwdCfg {
+  static constexpr int NW = 4;            // waves per workgroup
+  static constexpr int BM = 32 * NW;      // query rows per workgroup
+  static constexpr int BN = 64;           // keys per tile
+  static constexpr int PAD = 32 / (int)sizeof(T);  // 32 bytes of row padding in LDS
+  static constexpr int KS = DH + PAD;     // LDS row stride of K tiles (elements)
+  static constexpr int VS = DV + PAD;     // LDS row stride of V tiles
+  static constexpr int CH_K = DH * (int)sizeof(T) / 16;   // 16-byte chunks per K row
+  static constexpr int CH_V = DV * (int)sizeof(T) / 16;
+  static constexpr int LOAD_K = BN * CH_K / (64 * NW);    // chunks per thread per tile
+  static constexpr int LOAD_V = BN * CH_V / (64 * NW);
+};
+
+// Row i sees keys j < kmax(i).
+__device__ __forceinline__ int key_limit(int i, int Lk, int causal, int off) {
+  return causal ? min(Lk, i + off + 1) : Lk;
+}
+
+template <typename T, int DH, int DV>
+__global__ __launch_bounds__(256, 2) void fwd_kernel(const KernelParams p) {
+  using C = FwdCfg<T, DH, DV>;
+  using op_t = typename Op<T>::type;
+  __shared__ __attribute__((aligned(16))) T k_lds[2][C::BN * C::KS];
+  __shared__ __attribute__((aligned(16))) T v_lds[2][C::BN * C::VS];
+
+  const int nqblk = (p.n_q + C::BM - 1) / C::BM;
+  int unit, item;
+  if (!map_work(blockIdx.x, p.groups, p.per_group, p.xcd_map, unit, item)) return;
+  const int b = unit / p.H_kv, g = unit - (unit / p.H_kv) * p.H_kv;
+  // heavy (late) row blocks first; all query heads of the unit interleaved
+  const int qb = nqblk - 1 - item / p.group;
+  const int r = g * p.group + item % p.group;
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int Lq = p.has_lens ? p.lens_q[b] : p.n_q;
+  const int Lk = p.has_lens ? p.lens_k[b] : p.n_k;
+  const int q_lo = qb * C::BM;
+
+  const T* Qb = (const T*)p.q + b * p.q_sb + r * p.q_sh;
+  const T* Kb = (const T*)p.k + b * p.k_sb + g * p.k_sh;
+  const T* Vb = (const T*)p.v + b * p.v_sb + g * p.v_sh;
+  T* Ob = (T*)p.o_out + b * p.o_sb + r * p.o_sh;
+  float* lse_b = p.lse + ((int64_t)b * p.H_q + r) * p.n_q;
+
+  const int qi = q_lo + 32 * w + (lane & 31);          // this lane's query row
+  const int kg = lane >> 5;                            // k-group of the lane
+  const bool row_exists = qi < p.n_q;
+  const bool row_active = qi < Lq;
+
+  // rows of the block that are active
+  const int act_hi = min(q_lo + C::BM, Lq);            // exclusive
+  int ntiles = 0, nfull = 0;
+  if (act_hi > q_lo) {
+    const int kend = key_limit(act_hi - 1, Lk, p.causal, p.offset);
+    const int kfull = key_limit(q_lo, Lk, p.causal, p.offset);
+    ntiles = (kend + C::BN - 1) / C::BN;
+    nfull = kfull / C::BN;
+  }
+  // this wave's rows
+  const int w_lo = q_lo + 32 * w;
+  const int w_hi = min(w_lo + 32, Lq);
+  int wtiles = 0;
+  if (w_hi > w_lo) wtiles = (key_limit(w_hi - 1, Lk, p.causal, p.offset) + C::BN - 1) / C::BN;
+  const int kmax_lane = key_limit(qi, Lk, p.causal, p.offset);
+
+  f32x16 oacc[DV / 32];
+#pragma unroll
+  for (int i = 0; i < DV / 32; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oacc[i][e] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  if (ntiles > 0) {
+    // Q of this lane's row as the B operand of S^T = K Q^T (row k order)
+    op_t qreg[DH / 16];
+#pragma unroll
+    for (int ks = 0; ks < DH / 16; ++ks)
+      qreg[ks] = row_exists ? ld8<T>(Qb + (int64_t)qi * p.q_sr + 16 * ks + 8 * kg) : zero_op<T>();
+
+    // global -> register staging of one K/V tile
+    u32x4 kst[C::LOAD_K], vst[C::LOAD_V];
+    auto load_tile = [&](int t) {
+#pragma unroll
+      for (int i = 0; i < C::LOAD_K; ++i) {
+        const int c = tid + 64 * C::NW * i;
+        const int row = c / C::CH_K, col = c % C::CH_K;
+        const int key = t * C::BN + row;
+        kst[i] = key < p.n_k ? *reinterpret_cast<const u32x4*>(
+                                   (const char*)(Kb + (int64_t)key * p.k_sr) + 16 * col)
+                             : u32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int i = 0; i < C::LOAD_V; ++i) {
+        const int c = tid + 64 * C::NW * i;
+        const int row = c / C::CH_V, col = c % C::CH_V;
+        const int key = t * C::BN + row;
+        vst[i] = key < p.n_k ? *reinterpret_cast<const u32x4*>(
+                                   (const char*)(Vb + (int64_t)key * p.v_sr) + 16 * col)
+                             : u32x4{0, 0, 0, 0};
+      }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+      for (int i = 0; i < C::LOAD_K; ++i) {
+        const int c = tid + 64 * C::NW * i;
+        const int row = c / C::CH_K, col = c % C::CH_K;
+        *reinterpret_cast<u32x4*>((char*)(&k_lds[buf][row * C::KS]) + 16 * col) = kst[i];
+      }
+#pragma unroll
+      for (int i = 0; i < C::LOAD_V; ++i) {
+        const int c = tid + 64 * C::NW * i;
+        const int row = c / C::CH_V, col = c % C::CH_V;
+        *reinterpret_cast<u32x4*>((char*)(&v_lds[buf][row * C::VS]) + 16 * col) = vst[i];
+      }
+    };
+
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+
+    for (int t = 0; t < ntiles; ++t) {
+      const int buf = t & 1;
+      if (t + 1 < ntiles) load_tile(t + 1);
+      if (t < wtiles) {
+        const T* Ks = k_lds[buf];
+        const T* Vs = v_lds[buf];
+        // S^T tile: keys (rows) x this wave's 32 queries (columns)
+        f32x16 s[C::BN / 32];
+#pragma unroll
+        for (int mt = 0; mt < C::BN / 32; ++mt) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) s[mt][e] = 0.f;
+#pragma unroll
+          for (int ks = 0; ks < DH / 16; ++ks) {
+            op_t a = ld8<T>(Ks + (32 * mt + (lane & 31)) * C::KS + 16 * ks + 8 * kg);
+            mma(s[mt], a, qreg[ks]);
+          }
+        }
+        // scale into the log2 domain, mask, row max
+        const bool masked = t >= nfull;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < C::BN / 32; ++mt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            float v = s[mt][e] * p.scale_log2;
+            if (masked) {
+              const int key = t * C::BN + 32 * mt + 8 * (e >> 2) + 4 * kg + (e & 3);
+              v = key < kmax_lane ? v : -INFINITY;
+            }
+            s[mt][e] = v;
+            mx = fmaxf(mx, v);
+          }
+        mx = fmaxf(mx, partner32(mx));
+        const float m_new = fmaxf(m_run, mx);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        m_run = m_new;
+        float psum = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < C::BN / 32; ++mt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const float pe = __builtin_amdgcn_exp2f(s[mt][e] - m_use);
+            s[mt][e] = pe;
+            psum += pe;
+          }
+        l_run = l_run * alpha + psum;
+#pragma unroll
+        for (int i = 0; i < DV / 32; ++i)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) oacc[i][e] *= alpha;
+        // O^T += V^T P^T, contracting over the tile's keys in C order
+#pragma unroll
+        for (int mt = 0; mt < C::BN / 32; ++mt)
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            float pv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pv[e] = s[mt][8 * st + e];
+            const op_t bop = to_op<T>(pv);
+#pragma unroll
+            for (int dt = 0; dt < DV / 32; ++dt) {
+              const op_t aop = ld_tr<T>(Vs, C::VS, 32 * mt + 16 * st, 32 * dt);
+              mma(oacc[dt], aop, bop);
+            }
+          }
+      }
+      if (t + 1 < ntiles) store_tile(buf ^ 1);
+      __syncthreads();
+    }
+  }
+
+  // epilogue: O = acc / l, lse = ln2 * (m + log2 l); inactive rows get zeros
+  const float l_tot = l_run + partner32(l_run);
+  const float inv = (row_active && l_tot > 0.f) ? 1.f / l_tot : 0.f;
+  if (row_exists) {
+#pragma unroll
+    for (int dt = 0; dt < DV / 32; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = 32 * dt + 8 * j + 4 * kg;
+        st4<T>(Ob + (int64_t)qi * p.o_sr + d, oacc[dt][4 * j] * inv, oacc[dt][4 * j + 1] * inv,
+               oacc[dt][4 * j + 2] * inv, oacc[dt][4 * j + 3] * inv);
+      }
+    if (kg == 0)
+      lse_b[qi] = row_active ? (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994530942f : 0.f;
+  }
+}
+
+template <typename T, int DH, int DV>
+static int launch_fwd_t(const KernelParams& p, void* stream) {
+  using C = FwdCfg<T, DH, DV>;
+  const int nqblk = (p.n_q + C::BM - 1) / C::BM;
+  (void)nqblk;
+  const int64_t units = p.xcd_map ? ((p.groups + 7) / 8) * 8 : p.groups;
+  const int64_t grid = units * p.per_group;
+  if (grid <= 0) return (int)hipSuccess;
+  hipLaunchKernelGGL((fwd_kernel<T, DH, DV>), dim3((unsigned)grid), dim3(64 * C::NW), 0,
+                     (hipStream_t)stream, p);
+  return (int)hipGetLastError();
+}
+
+int fwd_block_rows(int /*dtype*/) { return 128; }
+
+int launch_fwd(const KernelParams& p, int dtype, int d_h, int d_v, void* stream) {
+  if (dtype == ATTN_BF16) {
+    if (d_h == 128 && d_v == 128) return launch_fwd_t<__bf16, 128, 128>(p, stream);
+    if (d_h == 128 && d_v == 64) return launch_fwd_t<__bf16, 128, 64>(p, stream);
+    if (d_h == 64 && d_v == 64) return launch_fwd_t<__bf16, 64, 64>(p, stream);
+    if (d_h == 64 && d_v == 128) return launch_fwd_t<__bf16, 64, 128>(p, stream);
+  } else {
+    if (d_h == 128 && d_v == 128) return launch_fwd_t<float, 128, 128>(p, stream);
+    if (d_h == 128 && d_v == 64) return launch_fwd_t<float, 128, 64>(p, stream);
+    if (d_h == 64 && d_v == 64) return launch_fwd_t<float, 64, 64>(p, stream);
+    if (d_h == 64 && d_v == 128) return launch_fwd_t<float, 64, 128>(p, stream);
+  }
+  return (int)hipErrorInvalidValue;
+}
+
+}  // namespace attn

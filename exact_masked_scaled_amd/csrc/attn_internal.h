@@ -1,0 +1,63 @@
+// Internal (non-ABI) declarations shared by the host dispatcher and the HIP
+// kernels of libattn_mi355x.so.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "attn.h"
+
+namespace attn {
+
+// Sequences per launch when per-sequence lengths are given: the lengths travel
+// by value in the kernel arguments (2 x 1 KiB), so longer batches are split
+// into several launches on the same stream.
+constexpr int kMaxBatchChunk = 256;
+
+// Everything a kernel needs, passed by value (__grid_constant__).
+struct KernelParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;      // forward output (backward input)
+  const void* dout;   // G_O
+  void* o_out;        // forward: O
+  float* lse;         // [B][H_q][n_q]
+  float* delta;       // workspace: D = rowsum(G_O o O), [B][H_q][n_q]
+  float* dq_acc;      // workspace: float32 G_Q accumulator, [B][H_q][n_q][d_h]
+  void* dq;
+  void* dk;
+  void* dv;
+  int64_t q_sb, q_sh, q_sr;
+  int64_t k_sb, k_sh, k_sr;
+  int64_t v_sb, v_sh, v_sr;
+  int64_t o_sb, o_sh, o_sr;
+  int32_t B, H_q, H_kv, n_q, n_k;
+  int32_t group;        // H_q / H_kv
+  int32_t causal;       // 0/1
+  int32_t offset;       // causal offset, clamped to [0, n_k]
+  float scale;          // 1/sqrt(d_h)
+  float scale_log2;     // log2(e)/sqrt(d_h)
+  int32_t has_lens;     // 0: every row active, every key valid
+  int32_t groups;       // (b, kv-head) units of work
+  int32_t per_group;    // work items per unit
+  int32_t xcd_map;      // 1: unit u runs on XCD u % 8 (groups % 8 == 0)
+  int32_t lens_q[kMaxBatchChunk];
+  int32_t lens_k[kMaxBatchChunk];
+};
+
+// Host-only validation; pure C++ (no HIP), shared by attn_validate/fwd/bwd.
+attn_status validate_problem(const attn_problem* prob, const attn_mask* mask);
+
+// Launchers (defined in the .hip translation units).  Return hipSuccess or
+// the launch error, as an int to keep this header free of HIP types.
+int launch_fwd(const KernelParams& p, int dtype, int d_h, int d_v, void* stream);
+int launch_bwd_pre(const KernelParams& p, int dtype, int d_h, int d_v, void* stream);
+int launch_bwd_main(const KernelParams& p, int dtype, int d_h, int d_v, void* stream);
+int launch_bwd_dq(const KernelParams& p, int dtype, int d_h, void* stream);
+
+// Tile sizes the dispatcher needs to size grids.
+int fwd_block_rows(int dtype);
+int bwd_block_keys(int dtype);
+
+}  // namespace attn

@@ -1,0 +1,131 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) exact masked scaled dot-product
+ * attention library (libattn_mi355x.so).
+ *
+ * Operation ("Appendix A.10 - Attention matrices and backpropagation",
+ * glenzli.com, secs. A.10.1-A.10.6, eqs. A.10.1-A.10.9):
+ *   for every sequence b, query head r (KV head g = r / (H_q / H_kv)),
+ *   active query row i < L_q[b] and its visible set
+ *       V_i = { j : j < L_k[b] and (causal == 0 or j <= i + causal_offset) },
+ *   S_ij = q_i . k_j / sqrt(d_h)                          (eq. A.10.1)
+ *   A_ij = exp(S_ij - m_i) / sum_{r in V_i} exp(S_ir - m_i) on V_i, else 0
+ *                                                        (eq. A.10.2)
+ *   O = A V                                               (eq. A.10.3)
+ *   lse_i = m_i + ln sum_{j in V_i} exp(S_ij - m_i)
+ * and given G_O = dL/dO:
+ *   G_V = A^T G_O, G_A = G_O V^T                          (eqs. A.10.5-6)
+ *   G_S = A o (G_A - c_i), c_i = sum_j A_ij (G_A)_ij       (eq. A.10.7)
+ *   G_Q = G_S K / sqrt(d_h), G_K = G_S^T Q / sqrt(d_h)     (eqs. A.10.8-9)
+ * with G_K, G_V summed over the query heads that share a KV head
+ * (sec. A.10.5).  The chunked-query form (n_q != n_k, a block of new queries
+ * against the full history) is the one of "Chapter 31: attention
+ * backpropagation" (eonloom handbook), sec. 1; that chapter's sec. 3 also
+ * rejects fully masked rows, as this library does.
+ *
+ * Rows i >= L_q[b] are inactive padding rows: their O, lse and G_Q rows are
+ * written as 0 and they contribute nothing to G_K / G_V.  Keys j >= L_k[b]
+ * get G_K = G_V = 0 exactly.
+ *
+ * Layout: every tensor is [B][H][n][d] with unit stride in d; the three outer
+ * strides (batch, head, row) are given in ELEMENTS.  G_O and G_Q use the
+ * strides of O and Q, G_K and G_V those of K and V.  lse (forward output,
+ * backward input) is a contiguous float32 [B][H_q][n_q] array.
+ *
+ * Ownership and execution: the caller owns every buffer and the stream.  All
+ * data pointers are DEVICE pointers except the seqlens arrays, which are HOST
+ * arrays read during the call (copied by value into the kernel arguments).
+ * Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the null
+ * stream); nothing synchronises the host.  The library allocates no device
+ * memory and keeps no global mutable state: calls are re-entrant.
+ *
+ * Errors: every argument check runs on the host before anything is enqueued;
+ * on any error the outputs are untouched.  Calls on different streams that
+ * share output buffers race (as any two kernels would).
+ */
+#ifndef ATTN_MI355X_H
+#define ATTN_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad stride, length out of
+                               range, H_q not a multiple of H_kv, negative size */
+  ATTN_ERR_EMPTY_ROW = 2,   /* an active query row has an empty visible set:
+                               L_k[b] == 0 with L_q[b] > 0, or causal with a
+                               negative offset (row 0 sees nothing)            */
+  ATTN_ERR_UNSUPPORTED = 3, /* head width not in {64, 128}, unknown dtype      */
+  ATTN_ERR_WORKSPACE = 4,   /* backward workspace missing or too small         */
+  ATTN_ERR_HIP = 5          /* a HIP launch failed                             */
+} attn_status;
+
+typedef enum {
+  ATTN_F32 = 0,  /* float32 I/O, float32 MFMA, float32 accumulation           */
+  ATTN_BF16 = 1  /* bfloat16 I/O, bf16 MFMA with float32 accumulation; P and
+                    G_S are rounded to bf16 (nearest-even) before the second
+                    products                                                  */
+} attn_dtype;
+
+/* The visible sets V_i (see above). */
+typedef struct {
+  int32_t causal;            /* 0: no causal rule; 1: j <= i + causal_offset   */
+  int32_t reserved;          /* must be 0                                      */
+  int64_t causal_offset;     /* 0 = square top-left causal; n_k - n_q places a
+                                block of n_q new queries at the end of the keys */
+  const int32_t* seqlens_q;  /* HOST [B] active rows per sequence, or NULL (= n_q) */
+  const int32_t* seqlens_k;  /* HOST [B] valid keys per sequence, or NULL (= n_k)  */
+} attn_mask;
+
+typedef struct {
+  int32_t B, H_q, H_kv;      /* H_q % H_kv == 0; g(r) = r / (H_q / H_kv)       */
+  int32_t n_q, n_k;          /* rows of Q/O and of K/V                         */
+  int32_t d_h, d_v;          /* widths of Q/K and of V/O: each 64 or 128       */
+  int32_t dtype;             /* attn_dtype                                      */
+  int64_t q_stride[3];       /* element strides of Q (and G_Q): batch, head, row */
+  int64_t k_stride[3];       /* K (and G_K)                                    */
+  int64_t v_stride[3];       /* V (and G_V)                                    */
+  int64_t o_stride[3];       /* O (and G_O)                                    */
+} attn_problem;
+
+/* Host-only argument check (no device work, no pointers needed).  Returns the
+ * status attn_fwd / attn_bwd would return for these sizes and masks, apart
+ * from pointer and workspace checks. */
+attn_status attn_validate(const attn_problem* prob, const attn_mask* mask);
+
+/* Bytes of device workspace attn_bwd needs for `prob` (256-byte aligned
+ * base).  The workspace holds per-row float32 D_i = rowsum(G_O o O) and a
+ * float32 accumulator for G_Q; its contents on entry are ignored. */
+size_t attn_bwd_workspace_size(const attn_problem* prob);
+
+/* Forward.  Q [B,H_q,n_q,d_h], K [B,H_kv,n_k,d_h], V [B,H_kv,n_k,d_v] in;
+ * O [B,H_q,n_q,d_v] and lse [B,H_q,n_q] (float32, contiguous) out.  Device
+ * pointers, 16-byte aligned; row strides multiples of 8 elements. */
+attn_status attn_fwd(const attn_problem* prob, const attn_mask* mask,
+                     const void* Q, const void* K, const void* V,
+                     void* O, float* lse, void* stream);
+
+/* Backward.  Takes the forward's inputs, its outputs O and lse, and G_O
+ * (strides of O); writes G_Q (strides of Q), G_K (strides of K) and G_V
+ * (strides of V).  `workspace` is device memory of at least
+ * attn_bwd_workspace_size(prob) bytes, 256-byte aligned. */
+attn_status attn_bwd(const attn_problem* prob, const attn_mask* mask,
+                     const void* Q, const void* K, const void* V,
+                     const void* O, const float* lse, const void* dO,
+                     void* dQ, void* dK, void* dV,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* attn_status_string(attn_status status);
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int32_t attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ATTN_MI355X_H */

@@ -1,0 +1,133 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the C ABI,
+run the float64 oracle on the same seeded (rounded) inputs, compare.
+
+Tolerance metric, per tensor over the compared elements:
+    max|gpu - ref| / max|ref|  <= 1e-5 (float32 I/O) or 2e-2 (bf16 I/O).
+"""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import oracle
+from exact_masked_scaled_amd import attn as A
+from exact_masked_scaled_amd import workloads as W
+
+TOL = {W.F32: 1e-5, W.BF16: 2e-2}
+TENSORS = ("O", "lse", "GQ", "GK", "GV")
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_device(a: np.ndarray):
+    import torch
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def to_f64(t) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def poison(t):
+    import torch
+    t.fill_(float("nan"))
+    return t
+
+
+def run_gpu(inp: W.Inputs, backward=True, poison_outputs=True):
+    """Forward (+ backward) on the GPU; returns device tensors."""
+    import torch
+    wl = inp.wl
+    q, k, v = to_device(inp.Q), to_device(inp.K), to_device(inp.V)
+    kw = inp.mask_kwargs()
+    out = torch.empty(wl.B, wl.H_q, wl.n_q, wl.d_v, dtype=q.dtype, device=q.device)
+    lse = torch.empty(wl.B, wl.H_q, wl.n_q, dtype=torch.float32, device=q.device)
+    if poison_outputs:
+        poison(out), poison(lse)
+    o, lse = A.fwd(q, k, v, out=out, lse=lse, **kw)
+    res = {"O": o, "lse": lse}
+    if backward:
+        do = to_device(inp.GO)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        prob = A._problem_from(q, k, v, A._strides(o))
+        ws = torch.empty(max(A.workspace_size(prob), 1), dtype=torch.uint8, device=q.device)
+        if poison_outputs:
+            poison(dq), poison(dk), poison(dv)
+            ws.fill_(0xFF)  # NaN bit patterns in the float32 workspace
+        dq, dk, dv = A.bwd(q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws, **kw)
+        res.update({"GQ": dq, "GK": dk, "GV": dv})
+    torch.cuda.synchronize()
+    return res
+
+
+def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    denom = float(np.max(np.abs(ref))) if ref.size else 0.0
+    diff = float(np.max(np.abs(got - ref))) if ref.size else 0.0
+    if not np.all(np.isfinite(got)):
+        return float("inf")
+    if denom == 0.0:
+        return diff
+    return diff / denom
+
+
+def compare_full(inp: W.Inputs, gpu: dict, backward=True) -> dict:
+    """Whole-tensor comparison against the oracle (small problems)."""
+    f64 = W.payload_to_f64
+    kw = inp.mask_kwargs()
+    if backward:
+        ref = oracle.attention_backward(f64(inp.Q), f64(inp.K), f64(inp.V), f64(inp.GO), **kw)
+    else:
+        ref = oracle.attention_forward(f64(inp.Q), f64(inp.K), f64(inp.V), **kw)
+    errs = {}
+    for name in TENSORS if backward else ("O", "lse"):
+        errs[name] = rel_err(to_f64(gpu[name]), ref[name])
+    return errs, ref
+
+
+def compare_groups(inp: W.Inputs, gpu: dict, groups) -> dict:
+    """Comparison on sampled (sequence, KV head) groups: every output of the
+    query heads of the group and G_K/G_V of its KV head."""
+    f64 = W.payload_to_f64
+    wl = inp.wl
+    kw = inp.mask_kwargs()
+    got = {n: [] for n in TENSORS}
+    ref = {n: [] for n in TENSORS}
+    Qf = _Lazy(inp.Q)
+    Kf = _Lazy(inp.K)
+    Vf = _Lazy(inp.V)
+    GOf = _Lazy(inp.GO)
+    for (b, g) in groups:
+        o = oracle.attention_group(Qf, Kf, Vf, GOf, b, g, **kw)
+        heads = o["heads"]
+        for name in ("O", "lse", "GQ"):
+            ref[name].append(o[name].ravel())
+            got[name].append(to_f64(gpu[name][b, heads[0]:heads[-1] + 1]).ravel())
+        for name in ("GK", "GV"):
+            ref[name].append(o[name].ravel())
+            got[name].append(to_f64(gpu[name][b, g]).ravel())
+    return {n: rel_err(np.concatenate(got[n]), np.concatenate(ref[n])) for n in TENSORS}
+
+
+class _Lazy:
+    """[b, h] indexing that widens one payload slice to float64 on demand."""
+
+    def __init__(self, a):
+        self.a = a
+        self.shape = a.shape
+
+    def __getitem__(self, idx):
+        return W.payload_to_f64(self.a[idx])
+
+
+def assert_within(errs: dict, dtype: str, label: str):
+    tol = TOL[dtype]
+    say(f"{label}: " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()) + f" (tol {tol:g})")
+    bad = {k: v for k, v in errs.items() if not (v <= tol)}
+    assert not bad, f"{label}: over tolerance {tol}: {bad}"

@@ -1,0 +1,113 @@
+"""Host-only checks of the C ABI: the library loads, exports every function the
+header declares, its structs match the header, and every argument error is
+reported before anything touches a device (so these run without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from exact_masked_scaled_amd import attn as A
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+def lib_or_skip():
+    if not os.path.exists(A.LIB_PATH):
+        pytest.fail(f"{A.LIB_PATH} not built (run __graft_entry__.build())")
+    return A.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    L = lib_or_skip()
+    names = declared_functions()
+    assert set(names) == set(A.EXPORTS), names
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.attn_version() >= 100
+
+
+def test_struct_layouts_match_header():
+    # attn_mask: int32, int32, int64, ptr, ptr ; attn_problem: 8 x int32 + 12 x int64
+    assert ctypes.sizeof(A.Mask) == 32
+    assert ctypes.sizeof(A.Problem) == 8 * 4 + 12 * 8
+    assert A.Problem.q_stride.offset == 32
+
+
+def prob(**kw):
+    base = dict(B=2, H_q=4, H_kv=2, n_q=100, n_k=130, d_h=128, d_v=64, dtype=A.BF16)
+    base.update(kw)
+    return A.make_problem(**base)
+
+
+def status(p, **mk):
+    lib_or_skip()
+    m, keep = A.make_mask(**mk)
+    return A.validate(p, m)
+
+
+def test_validation_codes():
+    assert status(prob()) == A.OK
+    assert status(prob(), causal=True, offset=0) == A.OK
+    assert status(prob(H_q=3, H_kv=2)) == A.INVALID_ARG
+    assert status(prob(d_h=96)) == A.UNSUPPORTED
+    assert status(prob(d_v=32)) == A.UNSUPPORTED
+    assert status(prob(dtype=7)) == A.UNSUPPORTED
+    assert status(prob(B=-1)) == A.INVALID_ARG
+    # empty visible sets of active rows
+    assert status(prob(), causal=True, offset=-1) == A.EMPTY_ROW
+    assert status(prob(), seqlens_k=[130, 0]) == A.EMPTY_ROW
+    assert status(prob(n_k=0)) == A.EMPTY_ROW
+    # ...but sequences without active rows are fine
+    assert status(prob(), seqlens_q=[100, 0], seqlens_k=[130, 0]) == A.OK
+    assert status(prob(n_q=0, n_k=0)) == A.OK
+    # lengths out of range
+    assert status(prob(), seqlens_q=[101, 3]) == A.INVALID_ARG
+    assert status(prob(), seqlens_k=[-1, 3]) == A.INVALID_ARG
+    # strides: multiples of 8, rows hold d elements
+    assert status(prob(q_stride=(4 * 100 * 128, 100 * 128, 132))) == A.INVALID_ARG
+    assert status(prob(k_stride=(2 * 130 * 64, 130 * 64, 64))) == A.INVALID_ARG
+    assert status(prob(q_stride=(4 * 100 * 136, 100 * 136, 136))) == A.OK
+
+
+def test_calls_reject_before_any_launch():
+    """attn_fwd / attn_bwd return the validation or pointer error without
+    enqueuing work: here no device exists, so reaching a launch would fail
+    differently (ATTN_ERR_HIP) or crash."""
+    L = lib_or_skip()
+    p = prob()
+    m, keep = A.make_mask(causal=True, offset=-3)
+    null = ctypes.c_void_p(0)
+    st = L.attn_fwd(ctypes.byref(p), ctypes.byref(m), null, null, null, null, null, null)
+    assert st == A.EMPTY_ROW
+    m2, keep2 = A.make_mask()
+    st = L.attn_fwd(ctypes.byref(p), ctypes.byref(m2), null, null, null, null, null, null)
+    assert st == A.INVALID_ARG  # null pointers
+    bad = ctypes.c_void_p(0x1004)  # misaligned (never dereferenced)
+    st = L.attn_fwd(ctypes.byref(p), ctypes.byref(m2), bad, bad, bad, bad, bad, null)
+    assert st == A.INVALID_ARG
+    fake = ctypes.c_void_p(0x10000)  # aligned but never dereferenced: workspace check comes first
+    st = L.attn_bwd(ctypes.byref(p), ctypes.byref(m2), fake, fake, fake, fake, fake, fake, fake, fake,
+                    fake, null, ctypes.c_size_t(0), null)
+    assert st == A.WORKSPACE
+    st = L.attn_bwd(ctypes.byref(p), ctypes.byref(m2), fake, fake, fake, fake, fake, fake, fake, fake,
+                    fake, fake, ctypes.c_size_t(16), null)
+    assert st == A.WORKSPACE
+    assert A.status_string(A.EMPTY_ROW).startswith("an active query row")
+
+
+def test_workspace_size():
+    lib_or_skip()
+    p = prob(B=3, H_q=4, n_q=100, d_h=128)
+    rows = 3 * 4 * 100
+    delta = (rows * 4 + 255) // 256 * 256
+    assert A.workspace_size(p) == delta + rows * 128 * 4
+    assert A.workspace_size(prob(B=0)) == 0
