@@ -1,0 +1,253 @@
+#!/usr/bin/env python3
+"""Throughput of exact masked scaled dot-product attention, forward + backward.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3] [--uniform-len N]
+
+One step = the whole hot path over one batch of synthetic input: the forward
+(O and lse) and the backward's three stages (D and accumulator clear; G_K, G_V
+and the G_Q accumulation; G_Q conversion), all through the C ABI on one HIP
+stream, inputs resident in HBM.  Default workload: bf16 causal GQA with key and
+row padding, B=8, H_q=32, H_kv=8, n=4096, d=128 (lengths drawn in [2048, 4096]).
+
+Prints ONE JSON line.  `value` is algorithmic TFLOP/s: only visible
+(query, key) pairs are credited, 2(d_h + d_v) FLOPs per pair forward and
+2(3 d_h + 2 d_v) backward.  `roofline` describes the dominant kernel, timed
+with HIP events on the stream it is launched on; `cpu_baseline` times the
+float64 oracle on a bounded sample of the same workload on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA, published
+PEAK_HBM_GBS = 8000.0
+METRIC = "attention fwd+bwd TFLOP/s and % of MFMA peak (bf16 causal GQA, n=4096)"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_main_causal_gqa_b8_n4096_traffic.txt")
+KERNEL_SOURCES = ("attn_bwd.hip", "attn_device.h", "attn_internal.h")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "exact_masked_scaled_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(units_per_launch_bytes):
+    """HBM bytes per launch of the backward main kernel from the committed
+    rocprofv3 counter summary, or None when the kernel source has changed
+    since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(inp, seconds: float):
+    """The float64 oracle as it stands, on whole (sequence, query head) pairs of
+    the same workload until about `seconds` of host time is spent."""
+    import numpy as np
+
+    import oracle
+    from exact_masked_scaled_amd import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        threads = len(os.sched_getaffinity(0))
+    wl = inp.wl
+    lq = inp.seqlens_q or [wl.n_q] * wl.B
+    lk = inp.seqlens_k or [wl.n_k] * wl.B
+    done_pairs, heads, t_used = 0, [], 0.0
+    order = [(b, r) for b in range(wl.B) for r in range(wl.H_q)]
+    t_start = time.perf_counter()
+    for b, r in order:
+        g = oracle.kv_group(r, wl.H_q, wl.H_kv)
+        M = oracle.visible_mask(wl.n_q, wl.n_k, lq[b], lk[b], wl.causal, wl.offset)
+        q = W.payload_to_f64(inp.Q[b, r])
+        k = W.payload_to_f64(inp.K[b, g])
+        v = W.payload_to_f64(inp.V[b, g])
+        go = W.payload_to_f64(inp.GO[b, r])
+        t0 = time.perf_counter()
+        f = oracle.head_forward(q, k, v, M)
+        oracle.head_backward(q, k, v, f["A"], M, go)
+        t_used += time.perf_counter() - t0
+        done_pairs += int(M.sum())
+        heads.append((b, r))
+        if time.perf_counter() - t_start >= seconds:
+            break
+    flop = 2 * done_pairs * (wl.d_h + wl.d_v) + 2 * done_pairs * (3 * wl.d_h + 2 * wl.d_v)
+    return {
+        "value": flop / t_used / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"float64 numpy oracle, forward+backward of {len(heads)} whole (sequence, query head) "
+                   f"pairs of the same workload (first: {heads[0]}, last: {heads[-1]}), "
+                   f"{t_used:.1f} s; algorithmic FLOPs of the visible pairs / oracle time"),
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--uniform-len", type=int, default=None,
+                    help="replace the drawn sequence lengths by this length (e.g. 4096: unpadded)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "this build has no multi-GPU path", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from exact_masked_scaled_amd import attn
+    from exact_masked_scaled_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    attn.lib()  # fail loudly without the library
+    wl = W.WORKLOADS[args.workload]
+    inp = W.make_inputs(wl, uniform_len=args.uniform_len)
+    kw = inp.mask_kwargs()
+    work = W.work(wl, inp.seqlens_q, inp.seqlens_k)
+
+    import numpy as np
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    q, k, v, do = dev(inp.Q), dev(inp.K), dev(inp.V), dev(inp.GO)
+    o = torch.empty(wl.B, wl.H_q, wl.n_q, wl.d_v, dtype=q.dtype, device=q.device)
+    lse = torch.empty(wl.B, wl.H_q, wl.n_q, dtype=torch.float32, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    prob = attn.make_problem(wl.B, wl.H_q, wl.H_kv, wl.n_q, wl.n_k, wl.d_h, wl.d_v,
+                             attn.BF16 if wl.dtype == W.BF16 else attn.F32)
+    ws = torch.empty(attn.workspace_size(prob), dtype=torch.uint8, device=q.device)
+    staged = attn.StagedBackward(q, k, v, o, lse, do, dq, dk, dv, ws, **kw)
+    stream = torch.cuda.current_stream()
+
+    names = ("fwd", "bwd_prepare", "bwd_main", "bwd_finish")
+
+    def step(events=None):
+        if events is not None:
+            events[0].record(stream)
+        attn.fwd(q, k, v, out=o, lse=lse, stream=stream, **kw)
+        if events is not None:
+            events[1].record(stream)
+        staged.prepare(stream)
+        if events is not None:
+            events[2].record(stream)
+        staged.main(stream)
+        if events is not None:
+            events[3].record(stream)
+        staged.finish(stream)
+        if events is not None:
+            events[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    kern_ms = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j, n in enumerate(names)}
+
+    flop = work["fwd_flop"] + work["bwd_flop"]
+    value = flop / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[wl.dtype]
+    dominant = max(kern_ms, key=kern_ms.get)
+    per_launch = {"fwd": work["fwd_flop"], "bwd_main": work["bwd_flop"]}
+    kernels = {}
+    for n in names:
+        ent = {"ms": round(kern_ms[n], 4)}
+        if n in per_launch:
+            tf = per_launch[n] / (kern_ms[n] * 1e-3) / 1e12
+            ent.update({"TFLOP/s": round(tf, 2), "frac_of_peak": round(tf / peak, 4)})
+        elif n == "bwd_prepare":
+            byt = 2 * wl.B * wl.H_q * wl.n_q * wl.d_v * (2 if wl.dtype == W.BF16 else 4) \
+                + wl.B * wl.H_q * wl.n_q * 4 * (1 + wl.d_h)
+            ent.update({"GB/s": round(byt / (kern_ms[n] * 1e-3) / 1e9, 1)})
+        elif n == "bwd_finish":
+            byt = wl.B * wl.H_q * wl.n_q * wl.d_h * (4 + (2 if wl.dtype == W.BF16 else 4))
+            ent.update({"GB/s": round(byt / (kern_ms[n] * 1e-3) / 1e9, 1)})
+        kernels[n] = ent
+    if dominant in per_launch:
+        ach = per_launch[dominant] / (kern_ms[dominant] * 1e-3) / 1e12
+        roof = {"kernel": dominant, "bound": "mfma", "achieved": round(ach, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(ach / peak, 4),
+                "traffic": load_traffic(None) if dominant == "bwd_main" else None}
+    else:
+        roof = {"kernel": dominant, "bound": "hbm", "achieved": None, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": None, "traffic": None}
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "pct_of_peak": round(100 * value / peak, 2),
+        "config": {
+            "workload": wl.name, "B": wl.B, "H_q": wl.H_q, "H_kv": wl.H_kv, "n_q": wl.n_q,
+            "n_k": wl.n_k, "d_h": wl.d_h, "d_v": wl.d_v, "causal": wl.causal, "offset": wl.offset,
+            "seqlens_k": inp.seqlens_k, "seqlens_q": inp.seqlens_q, "seed": inp.seed,
+            "visible_pairs": work["pairs"], "fwd_gflop": round(work["fwd_flop"] / 1e9, 3),
+            "bwd_gflop": round(work["bwd_flop"] / 1e9, 3),
+            "literal_formula_fwd_gflop": round(work["literal_fwd_flop"] / 1e9, 3),
+        },
+        "kernels": kernels,
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

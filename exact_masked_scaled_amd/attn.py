@@ -32,6 +32,7 @@ BF16 = 1
 
 # every symbol the header declares
 EXPORTS = ("attn_validate", "attn_bwd_workspace_size", "attn_fwd", "attn_bwd",
+           "attn_bwd_prepare", "attn_bwd_main", "attn_bwd_finish",
            "attn_status_string", "attn_version")
 
 
@@ -83,6 +84,12 @@ def lib():
     L.attn_fwd.restype = ctypes.c_int
     L.attn_bwd.argtypes = [P, M, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.attn_bwd.restype = ctypes.c_int
+    L.attn_bwd_prepare.argtypes = [P, M, vp, vp, vp, ctypes.c_size_t, vp]
+    L.attn_bwd_prepare.restype = ctypes.c_int
+    L.attn_bwd_main.argtypes = [P, M, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.attn_bwd_main.restype = ctypes.c_int
+    L.attn_bwd_finish.argtypes = [P, M, vp, vp, ctypes.c_size_t, vp]
+    L.attn_bwd_finish.restype = ctypes.c_int
     L.attn_status_string.argtypes = [ctypes.c_int]
     L.attn_status_string.restype = ctypes.c_char_p
     L.attn_version.argtypes = []
@@ -246,3 +253,44 @@ def bwd(q, k, v, o, lse, do, *, causal=False, offset=0, seqlens_q=None, seqlens_
     if st != OK:
         raise AttnError(st, "attn_bwd")
     return dq, dk, dv
+
+
+class StagedBackward:
+    """The backward's three ABI stages bound to fixed tensors, for callers that
+    time or schedule them separately (calling prepare(), main(), finish() in
+    order equals one bwd() call)."""
+
+    def __init__(self, q, k, v, o, lse, do, dq, dk, dv, workspace, *, causal=False, offset=0,
+                 seqlens_q=None, seqlens_k=None):
+        for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do), ("dq", dq),
+                        ("dk", dk), ("dv", dv)):
+            _check4(name, t, q.dtype)
+        if do.stride() != o.stride() or dq.stride() != q.stride() or dk.stride() != k.stride() \
+                or dv.stride() != v.stride():
+            raise ValueError("gradient strides must match their tensors")
+        self.prob = _problem_from(q, k, v, _strides(o))
+        self.mask, self._keep = make_mask(causal, offset, seqlens_q, seqlens_k)
+        self.t = (q, k, v, o, lse, do, dq, dk, dv, workspace)
+        self.ws = _ptr(workspace)
+        self.ws_bytes = ctypes.c_size_t(workspace.numel())
+
+    def _check(self, st, what):
+        if st != OK:
+            raise AttnError(st, what)
+
+    def prepare(self, stream=None):
+        q, k, v, o, lse, do, dq, dk, dv, ws = self.t
+        self._check(lib().attn_bwd_prepare(ctypes.byref(self.prob), ctypes.byref(self.mask), _ptr(o),
+                                           _ptr(do), self.ws, self.ws_bytes, _stream(stream)),
+                    "attn_bwd_prepare")
+
+    def main(self, stream=None):
+        q, k, v, o, lse, do, dq, dk, dv, ws = self.t
+        self._check(lib().attn_bwd_main(ctypes.byref(self.prob), ctypes.byref(self.mask), _ptr(q),
+                                        _ptr(k), _ptr(v), _ptr(lse), _ptr(do), _ptr(dk), _ptr(dv),
+                                        self.ws, self.ws_bytes, _stream(stream)), "attn_bwd_main")
+
+    def finish(self, stream=None):
+        q, k, v, o, lse, do, dq, dk, dv, ws = self.t
+        self._check(lib().attn_bwd_finish(ctypes.byref(self.prob), ctypes.byref(self.mask), _ptr(dq),
+                                          self.ws, self.ws_bytes, _stream(stream)), "attn_bwd_finish")

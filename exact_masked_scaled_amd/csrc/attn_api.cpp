@@ -105,23 +105,39 @@ attn_status attn_fwd(const attn_problem* prob, const attn_mask* mask, const void
   return ATTN_OK;
 }
 
-attn_status attn_bwd(const attn_problem* prob, const attn_mask* mask, const void* Q, const void* K,
-                     const void* V, const void* O, const float* lse, const void* dO, void* dQ, void* dK,
-                     void* dV, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+enum : int { kPrepare = 1, kMain = 2, kFinish = 4 };
+
+struct BwdPtrs {
+  const void *Q, *K, *V, *O, *dO;
+  const float* lse;
+  void *dQ, *dK, *dV;
+};
+
+// Shared body of attn_bwd and its stages: validate, check the pointers the
+// requested stages read or write, then enqueue the stages per sequence chunk.
+attn_status bwd_stages(const attn_problem* prob, const attn_mask* mask, const BwdPtrs& t,
+                       void* workspace, size_t workspace_bytes, void* stream, int stages) {
   attn_status st = validate_problem(prob, mask);
   if (st != ATTN_OK) return st;
   const attn_problem& p = *prob;
   const attn_mask& m = *mask;
   if (p.B == 0 || (p.n_q == 0 && p.n_k == 0)) return ATTN_OK;
   const bool has_q = p.n_q > 0, has_k = p.n_k > 0;
-  if (has_q && (!Q || !O || !lse || !dO || !dQ || !aligned16(Q) || !aligned16(O) || !aligned16(lse) ||
-                !aligned16(dO) || !aligned16(dQ)))
+  auto need = [](const void* ptr) { return ptr != nullptr && aligned16(ptr); };
+  if (has_q) {
+    if ((stages & kPrepare) && !(need(t.O) && need(t.dO))) return ATTN_ERR_INVALID_ARG;
+    if ((stages & kMain) && !(need(t.Q) && need(t.lse) && need(t.dO))) return ATTN_ERR_INVALID_ARG;
+    if ((stages & kFinish) && !need(t.dQ)) return ATTN_ERR_INVALID_ARG;
+  }
+  if (has_k && (stages & kMain) && !(need(t.K) && need(t.V) && need(t.dK) && need(t.dV)))
     return ATTN_ERR_INVALID_ARG;
-  if (has_k && (!K || !V || !dK || !dV || !aligned16(K) || !aligned16(V) || !aligned16(dK) ||
-                !aligned16(dV)))
-    return ATTN_ERR_INVALID_ARG;
-  const size_t need = attn_bwd_workspace_size(prob);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need || ((uintptr_t)workspace % kWsAlign) != 0))
+  const size_t need_ws = attn_bwd_workspace_size(prob);
+  if (need_ws > 0 &&
+      (workspace == nullptr || workspace_bytes < need_ws || ((uintptr_t)workspace % kWsAlign) != 0))
     return ATTN_ERR_WORKSPACE;
   const size_t es = esize(p.dtype);
   const size_t rows = (size_t)p.B * p.H_q * p.n_q;
@@ -136,22 +152,52 @@ attn_status attn_bwd(const attn_problem* prob, const attn_mask* mask, const void
     fill_chunk(kp, p, m, b0, nb);
     kp.per_group = nkblk;
     const int64_t row0 = (int64_t)b0 * p.H_q * p.n_q;
-    kp.q = off(Q, b0 * p.q_stride[0], es);
-    kp.k = off(K, b0 * p.k_stride[0], es);
-    kp.v = off(V, b0 * p.v_stride[0], es);
-    kp.o = off(O, b0 * p.o_stride[0], es);
-    kp.dout = off(dO, b0 * p.o_stride[0], es);
-    kp.lse = const_cast<float*>(lse) + (lse ? row0 : 0);
+    kp.q = off(t.Q, b0 * p.q_stride[0], es);
+    kp.k = off(t.K, b0 * p.k_stride[0], es);
+    kp.v = off(t.V, b0 * p.v_stride[0], es);
+    kp.o = off(t.O, b0 * p.o_stride[0], es);
+    kp.dout = off(t.dO, b0 * p.o_stride[0], es);
+    kp.lse = t.lse ? const_cast<float*>(t.lse) + row0 : nullptr;
     kp.delta = delta ? delta + row0 : nullptr;
-    kp.dq_acc = dq_acc ? dq_acc + row0 * p.d_h : nullptr;
-    kp.dq = off(dQ, b0 * p.q_stride[0], es);
-    kp.dk = off(dK, b0 * p.k_stride[0], es);
-    kp.dv = off(dV, b0 * p.v_stride[0], es);
-    if (launch_bwd_pre(kp, p.dtype, p.d_h, p.d_v, stream) != 0) return ATTN_ERR_HIP;
-    if (launch_bwd_main(kp, p.dtype, p.d_h, p.d_v, stream) != 0) return ATTN_ERR_HIP;
-    if (launch_bwd_dq(kp, p.dtype, p.d_h, stream) != 0) return ATTN_ERR_HIP;
+    kp.dq_acc = dq_acc && workspace ? dq_acc + row0 * p.d_h : nullptr;
+    kp.dq = off(t.dQ, b0 * p.q_stride[0], es);
+    kp.dk = off(t.dK, b0 * p.k_stride[0], es);
+    kp.dv = off(t.dV, b0 * p.v_stride[0], es);
+    if ((stages & kPrepare) && launch_bwd_pre(kp, p.dtype, p.d_h, p.d_v, stream) != 0) return ATTN_ERR_HIP;
+    if ((stages & kMain) && launch_bwd_main(kp, p.dtype, p.d_h, p.d_v, stream) != 0) return ATTN_ERR_HIP;
+    if ((stages & kFinish) && launch_bwd_dq(kp, p.dtype, p.d_h, stream) != 0) return ATTN_ERR_HIP;
   }
   return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_bwd(const attn_problem* prob, const attn_mask* mask, const void* Q, const void* K,
+                     const void* V, const void* O, const float* lse, const void* dO, void* dQ, void* dK,
+                     void* dV, void* workspace, size_t workspace_bytes, void* stream) {
+  const BwdPtrs t{Q, K, V, O, dO, lse, dQ, dK, dV};
+  return bwd_stages(prob, mask, t, workspace, workspace_bytes, stream, kPrepare | kMain | kFinish);
+}
+
+attn_status attn_bwd_prepare(const attn_problem* prob, const attn_mask* mask, const void* O,
+                             const void* dO, void* workspace, size_t workspace_bytes, void* stream) {
+  const BwdPtrs t{nullptr, nullptr, nullptr, O, dO, nullptr, nullptr, nullptr, nullptr};
+  return bwd_stages(prob, mask, t, workspace, workspace_bytes, stream, kPrepare);
+}
+
+attn_status attn_bwd_main(const attn_problem* prob, const attn_mask* mask, const void* Q, const void* K,
+                          const void* V, const float* lse, const void* dO, void* dK, void* dV,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  const BwdPtrs t{Q, K, V, nullptr, dO, lse, nullptr, dK, dV};
+  return bwd_stages(prob, mask, t, workspace, workspace_bytes, stream, kMain);
+}
+
+attn_status attn_bwd_finish(const attn_problem* prob, const attn_mask* mask, void* dQ, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  const BwdPtrs t{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, dQ, nullptr, nullptr};
+  return bwd_stages(prob, mask, t, workspace, workspace_bytes, stream, kFinish);
 }
 
 const char* attn_status_string(attn_status s) {

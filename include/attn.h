@@ -119,6 +119,26 @@ attn_status attn_bwd(const attn_problem* prob, const attn_mask* mask,
                      void* dQ, void* dK, void* dV,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* The backward in its three stages, for callers that schedule or time them
+ * separately; attn_bwd is exactly prepare, main and finish enqueued in that
+ * order on one stream with one workspace.  Each stage validates like
+ * attn_bwd.
+ *   prepare: D_i = rowsum(G_O o O) into the workspace (the row scalar c_i of
+ *            eq. A.10.7) and clears the workspace's float32 G_Q accumulator;
+ *   main:    writes G_K and G_V and accumulates G_Q into the workspace
+ *            (eqs. A.10.5-A.10.9), reading D from the workspace;
+ *   finish:  converts the G_Q accumulator to the I/O dtype into dQ.
+ * Pointers a stage does not use may be NULL. */
+attn_status attn_bwd_prepare(const attn_problem* prob, const attn_mask* mask,
+                             const void* O, const void* dO,
+                             void* workspace, size_t workspace_bytes, void* stream);
+attn_status attn_bwd_main(const attn_problem* prob, const attn_mask* mask,
+                          const void* Q, const void* K, const void* V,
+                          const float* lse, const void* dO, void* dK, void* dV,
+                          void* workspace, size_t workspace_bytes, void* stream);
+attn_status attn_bwd_finish(const attn_problem* prob, const attn_mask* mask, void* dQ,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* attn_status_string(attn_status status);
 

@@ -196,3 +196,21 @@ def test_repeat_calls_are_stable():
     for n in ("O", "lse", "GK", "GV"):
         assert bool((a[n] == b[n]).all()), n
     assert P.rel_err(P.to_f64(a["GQ"]), P.to_f64(b["GQ"])) < 1e-2
+
+
+def test_staged_backward_equals_bwd():
+    """attn_bwd_prepare + attn_bwd_main + attn_bwd_finish give what attn_bwd gives."""
+    import torch
+    inp = W.make_custom_inputs(W.custom_workload(W.BF16, 2, 4, 2, 200, 260, 128, 128, True, 60),
+                               seed=5, seqlens_q=[200, 111], seqlens_k=[260, 170])
+    ref = P.run_gpu(inp)
+    q, k, v, do = (P.to_device(x) for x in (inp.Q, inp.K, inp.V, inp.GO))
+    o, lse = ref["O"], ref["lse"]
+    dq, dk, dv = (P.poison(torch.empty_like(x)) for x in (q, k, v))
+    prob = A._problem_from(q, k, v, A._strides(o))
+    ws = torch.full((A.workspace_size(prob),), 0xFF, dtype=torch.uint8, device=q.device)
+    st = A.StagedBackward(q, k, v, o, lse, do, dq, dk, dv, ws, **inp.mask_kwargs())
+    st.prepare(); st.main(); st.finish()
+    torch.cuda.synchronize()
+    assert bool((dk == ref["GK"]).all()) and bool((dv == ref["GV"]).all())
+    assert P.rel_err(P.to_f64(dq), P.to_f64(ref["GQ"])) < 1e-2
