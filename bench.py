@@ -32,8 +32,9 @@ if ROOT not in sys.path:
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA, published
 PEAK_HBM_GBS = 8000.0
 METRIC = "attention fwd+bwd TFLOP/s and % of MFMA peak (bf16 causal GQA, n=4096)"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_main_causal_gqa_b8_n4096_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_dkdv_causal_gqa_b8_n4096_traffic.txt")
 KERNEL_SOURCES = ("attn_bwd.hip", "attn_device.h", "attn_internal.h")
+DOMINANT = "bwd_dkdv"
 
 
 def kernel_source_hash() -> str:
@@ -119,6 +120,9 @@ def main(argv=None):
                     help="replace the drawn sequence lengths by this length (e.g. 4096: unpadded)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="after timing, run a plain elementwise copy of this many MiB (3 launches) "
+                         "so HBM byte counters can be scaled against a kernel of known traffic")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -158,7 +162,7 @@ def main(argv=None):
     staged = attn.StagedBackward(q, k, v, o, lse, do, dq, dk, dv, ws, **kw)
     stream = torch.cuda.current_stream()
 
-    names = ("fwd", "bwd_prepare", "bwd_main", "bwd_finish")
+    names = ("fwd", "bwd_dq", "bwd_dkdv")
 
     def step(events=None):
         if events is not None:
@@ -166,20 +170,17 @@ def main(argv=None):
         attn.fwd(q, k, v, out=o, lse=lse, stream=stream, **kw)
         if events is not None:
             events[1].record(stream)
-        staged.prepare(stream)
+        staged.dq(stream)
         if events is not None:
             events[2].record(stream)
-        staged.main(stream)
+        staged.dkdv(stream)
         if events is not None:
             events[3].record(stream)
-        staged.finish(stream)
-        if events is not None:
-            events[4].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -192,30 +193,24 @@ def main(argv=None):
     flop = work["fwd_flop"] + work["bwd_flop"]
     value = flop / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[wl.dtype]
-    dominant = max(kern_ms, key=kern_ms.get)
-    per_launch = {"fwd": work["fwd_flop"], "bwd_main": work["bwd_flop"]}
+    P, dh, dv_ = work["pairs"], wl.d_h, wl.d_v
+    # algorithmic FLOPs credited to each kernel, without double counting the
+    # recomputed products: dq gets the G_Q product only, dkdv the recomputed
+    # scores, dP, G_V and G_K
+    alg = {"fwd": 2 * P * (dh + dv_), "bwd_dq": 2 * P * dh, "bwd_dkdv": 2 * P * (2 * dh + 2 * dv_)}
+    executed = {"fwd": 2 * P * (dh + dv_), "bwd_dq": 2 * P * (2 * dh + dv_), "bwd_dkdv": 2 * P * (2 * dh + 2 * dv_)}
     kernels = {}
     for n in names:
-        ent = {"ms": round(kern_ms[n], 4)}
-        if n in per_launch:
-            tf = per_launch[n] / (kern_ms[n] * 1e-3) / 1e12
-            ent.update({"TFLOP/s": round(tf, 2), "frac_of_peak": round(tf / peak, 4)})
-        elif n == "bwd_prepare":
-            byt = 2 * wl.B * wl.H_q * wl.n_q * wl.d_v * (2 if wl.dtype == W.BF16 else 4) \
-                + wl.B * wl.H_q * wl.n_q * 4 * (1 + wl.d_h)
-            ent.update({"GB/s": round(byt / (kern_ms[n] * 1e-3) / 1e9, 1)})
-        elif n == "bwd_finish":
-            byt = wl.B * wl.H_q * wl.n_q * wl.d_h * (4 + (2 if wl.dtype == W.BF16 else 4))
-            ent.update({"GB/s": round(byt / (kern_ms[n] * 1e-3) / 1e9, 1)})
-        kernels[n] = ent
-    if dominant in per_launch:
-        ach = per_launch[dominant] / (kern_ms[dominant] * 1e-3) / 1e12
-        roof = {"kernel": dominant, "bound": "mfma", "achieved": round(ach, 2), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(ach / peak, 4),
-                "traffic": load_traffic(None) if dominant == "bwd_main" else None}
-    else:
-        roof = {"kernel": dominant, "bound": "hbm", "achieved": None, "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": None, "traffic": None}
+        sec = kern_ms[n] * 1e-3
+        kernels[n] = {"ms": round(kern_ms[n], 4),
+                      "algorithmic_TFLOP/s": round(alg[n] / sec / 1e12, 2),
+                      "executed_MFMA_TFLOP/s": round(executed[n] / sec / 1e12, 2),
+                      "executed_frac_of_peak": round(executed[n] / sec / 1e12 / peak, 4)}
+    dominant = max(kern_ms, key=kern_ms.get)
+    ach = alg[dominant] / (kern_ms[dominant] * 1e-3) / 1e12
+    roof = {"kernel": dominant, "bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(ach / peak, 4),
+            "traffic": load_traffic(None) if dominant == DOMINANT else None}
 
     result = {
         "metric": METRIC,
@@ -243,6 +238,14 @@ def main(argv=None):
         "roofline": roof,
         "cpu_baseline": None,
     }
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=q.device)
+        c = torch.empty_like(a)
+        for _ in range(3):
+            torch.mul(a, 1.0, out=c)  # reads and writes exactly n * 4 bytes
+        torch.cuda.synchronize()
+        result["copy_calibration"] = {"bytes_read": n * 4, "bytes_written": n * 4, "launches": 3}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)

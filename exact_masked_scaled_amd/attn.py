@@ -32,7 +32,7 @@ BF16 = 1
 
 # every symbol the header declares
 EXPORTS = ("attn_validate", "attn_bwd_workspace_size", "attn_fwd", "attn_bwd",
-           "attn_bwd_prepare", "attn_bwd_main", "attn_bwd_finish",
+           "attn_bwd_dq", "attn_bwd_dkdv",
            "attn_status_string", "attn_version")
 
 
@@ -84,12 +84,10 @@ def lib():
     L.attn_fwd.restype = ctypes.c_int
     L.attn_bwd.argtypes = [P, M, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.attn_bwd.restype = ctypes.c_int
-    L.attn_bwd_prepare.argtypes = [P, M, vp, vp, vp, ctypes.c_size_t, vp]
-    L.attn_bwd_prepare.restype = ctypes.c_int
-    L.attn_bwd_main.argtypes = [P, M, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
-    L.attn_bwd_main.restype = ctypes.c_int
-    L.attn_bwd_finish.argtypes = [P, M, vp, vp, ctypes.c_size_t, vp]
-    L.attn_bwd_finish.restype = ctypes.c_int
+    L.attn_bwd_dq.argtypes = [P, M, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.attn_bwd_dq.restype = ctypes.c_int
+    L.attn_bwd_dkdv.argtypes = [P, M, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.attn_bwd_dkdv.restype = ctypes.c_int
     L.attn_status_string.argtypes = [ctypes.c_int]
     L.attn_status_string.restype = ctypes.c_char_p
     L.attn_version.argtypes = []
@@ -256,9 +254,8 @@ def bwd(q, k, v, o, lse, do, *, causal=False, offset=0, seqlens_q=None, seqlens_
 
 
 class StagedBackward:
-    """The backward's three ABI stages bound to fixed tensors, for callers that
-    time or schedule them separately (calling prepare(), main(), finish() in
-    order equals one bwd() call)."""
+    """The backward's two ABI passes bound to fixed tensors, for callers that
+    time or schedule them separately (dq() then dkdv() equals one bwd())."""
 
     def __init__(self, q, k, v, o, lse, do, dq, dk, dv, workspace, *, causal=False, offset=0,
                  seqlens_q=None, seqlens_k=None):
@@ -278,19 +275,14 @@ class StagedBackward:
         if st != OK:
             raise AttnError(st, what)
 
-    def prepare(self, stream=None):
+    def dq(self, stream=None):
         q, k, v, o, lse, do, dq, dk, dv, ws = self.t
-        self._check(lib().attn_bwd_prepare(ctypes.byref(self.prob), ctypes.byref(self.mask), _ptr(o),
-                                           _ptr(do), self.ws, self.ws_bytes, _stream(stream)),
-                    "attn_bwd_prepare")
+        self._check(lib().attn_bwd_dq(ctypes.byref(self.prob), ctypes.byref(self.mask), _ptr(q), _ptr(k),
+                                      _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), self.ws,
+                                      self.ws_bytes, _stream(stream)), "attn_bwd_dq")
 
-    def main(self, stream=None):
+    def dkdv(self, stream=None):
         q, k, v, o, lse, do, dq, dk, dv, ws = self.t
-        self._check(lib().attn_bwd_main(ctypes.byref(self.prob), ctypes.byref(self.mask), _ptr(q),
+        self._check(lib().attn_bwd_dkdv(ctypes.byref(self.prob), ctypes.byref(self.mask), _ptr(q),
                                         _ptr(k), _ptr(v), _ptr(lse), _ptr(do), _ptr(dk), _ptr(dv),
-                                        self.ws, self.ws_bytes, _stream(stream)), "attn_bwd_main")
-
-    def finish(self, stream=None):
-        q, k, v, o, lse, do, dq, dk, dv, ws = self.t
-        self._check(lib().attn_bwd_finish(ctypes.byref(self.prob), ctypes.byref(self.mask), _ptr(dq),
-                                          self.ws, self.ws_bytes, _stream(stream)), "attn_bwd_finish")
+                                        self.ws, self.ws_bytes, _stream(stream)), "attn_bwd_dkdv")

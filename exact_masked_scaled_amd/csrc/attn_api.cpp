@@ -74,7 +74,7 @@ attn_status attn_validate(const attn_problem* prob, const attn_mask* mask) {
 size_t attn_bwd_workspace_size(const attn_problem* prob) {
   if (prob == nullptr || prob->B < 0 || prob->H_q < 0 || prob->n_q < 0 || prob->d_h < 0) return 0;
   const size_t rows = (size_t)prob->B * (size_t)prob->H_q * (size_t)prob->n_q;
-  return align_up(rows * sizeof(float), kWsAlign) + rows * (size_t)prob->d_h * sizeof(float);
+  return align_up(rows * sizeof(float), kWsAlign);
 }
 
 attn_status attn_fwd(const attn_problem* prob, const attn_mask* mask, const void* Q, const void* K,
@@ -109,7 +109,7 @@ attn_status attn_fwd(const attn_problem* prob, const attn_mask* mask, const void
 
 namespace {
 
-enum : int { kPrepare = 1, kMain = 2, kFinish = 4 };
+enum : int { kDq = 1, kDkdv = 2 };
 
 struct BwdPtrs {
   const void *Q, *K, *V, *O, *dO;
@@ -117,40 +117,39 @@ struct BwdPtrs {
   void *dQ, *dK, *dV;
 };
 
-// Shared body of attn_bwd and its stages: validate, check the pointers the
-// requested stages read or write, then enqueue the stages per sequence chunk.
-attn_status bwd_stages(const attn_problem* prob, const attn_mask* mask, const BwdPtrs& t,
-                       void* workspace, size_t workspace_bytes, void* stream, int stages) {
+// Shared body of attn_bwd and its two passes: validate, check the pointers
+// the requested passes read or write, then enqueue them per sequence chunk.
+attn_status bwd_passes(const attn_problem* prob, const attn_mask* mask, const BwdPtrs& t,
+                       void* workspace, size_t workspace_bytes, void* stream, int passes) {
   attn_status st = validate_problem(prob, mask);
   if (st != ATTN_OK) return st;
   const attn_problem& p = *prob;
   const attn_mask& m = *mask;
   if (p.B == 0 || (p.n_q == 0 && p.n_k == 0)) return ATTN_OK;
   const bool has_q = p.n_q > 0, has_k = p.n_k > 0;
-  auto need = [](const void* ptr) { return ptr != nullptr && aligned16(ptr); };
+  auto ok = [](const void* ptr) { return ptr != nullptr && aligned16(ptr); };
   if (has_q) {
-    if ((stages & kPrepare) && !(need(t.O) && need(t.dO))) return ATTN_ERR_INVALID_ARG;
-    if ((stages & kMain) && !(need(t.Q) && need(t.lse) && need(t.dO))) return ATTN_ERR_INVALID_ARG;
-    if ((stages & kFinish) && !need(t.dQ)) return ATTN_ERR_INVALID_ARG;
+    if ((passes & kDq) && !(ok(t.Q) && ok(t.O) && ok(t.lse) && ok(t.dO) && ok(t.dQ)))
+      return ATTN_ERR_INVALID_ARG;
+    if ((passes & kDkdv) && !(ok(t.Q) && ok(t.lse) && ok(t.dO))) return ATTN_ERR_INVALID_ARG;
   }
-  if (has_k && (stages & kMain) && !(need(t.K) && need(t.V) && need(t.dK) && need(t.dV)))
+  if (has_k && (passes & kDkdv) && !(ok(t.K) && ok(t.V) && ok(t.dK) && ok(t.dV)))
     return ATTN_ERR_INVALID_ARG;
+  if (has_k && has_q && (passes & kDq) && !(ok(t.K) && ok(t.V))) return ATTN_ERR_INVALID_ARG;
   const size_t need_ws = attn_bwd_workspace_size(prob);
   if (need_ws > 0 &&
       (workspace == nullptr || workspace_bytes < need_ws || ((uintptr_t)workspace % kWsAlign) != 0))
     return ATTN_ERR_WORKSPACE;
   const size_t es = esize(p.dtype);
-  const size_t rows = (size_t)p.B * p.H_q * p.n_q;
   float* delta = (float*)workspace;
-  float* dq_acc = (float*)((char*)workspace + align_up(rows * sizeof(float), kWsAlign));
   KernelParams kp;
   fill_common(kp, p, m);
-  const int nkblk = (p.n_k + bwd_block_keys(p.dtype) - 1) / bwd_block_keys(p.dtype);
+  const int nqblk = (p.n_q + bwd_dq_block_rows(p.dtype) - 1) / bwd_dq_block_rows(p.dtype);
+  const int nkblk = (p.n_k + bwd_dkdv_block_keys(p.dtype) - 1) / bwd_dkdv_block_keys(p.dtype);
   const int cs = chunk_size(kp, p.B);
   for (int b0 = 0; b0 < p.B; b0 += cs) {
     const int nb = std::min(cs, p.B - b0);
     fill_chunk(kp, p, m, b0, nb);
-    kp.per_group = nkblk;
     const int64_t row0 = (int64_t)b0 * p.H_q * p.n_q;
     kp.q = off(t.Q, b0 * p.q_stride[0], es);
     kp.k = off(t.K, b0 * p.k_stride[0], es);
@@ -159,13 +158,17 @@ attn_status bwd_stages(const attn_problem* prob, const attn_mask* mask, const Bw
     kp.dout = off(t.dO, b0 * p.o_stride[0], es);
     kp.lse = t.lse ? const_cast<float*>(t.lse) + row0 : nullptr;
     kp.delta = delta ? delta + row0 : nullptr;
-    kp.dq_acc = dq_acc && workspace ? dq_acc + row0 * p.d_h : nullptr;
     kp.dq = off(t.dQ, b0 * p.q_stride[0], es);
     kp.dk = off(t.dK, b0 * p.k_stride[0], es);
     kp.dv = off(t.dV, b0 * p.v_stride[0], es);
-    if ((stages & kPrepare) && launch_bwd_pre(kp, p.dtype, p.d_h, p.d_v, stream) != 0) return ATTN_ERR_HIP;
-    if ((stages & kMain) && launch_bwd_main(kp, p.dtype, p.d_h, p.d_v, stream) != 0) return ATTN_ERR_HIP;
-    if ((stages & kFinish) && launch_bwd_dq(kp, p.dtype, p.d_h, stream) != 0) return ATTN_ERR_HIP;
+    if ((passes & kDq) && has_q) {
+      kp.per_group = kp.group * nqblk;
+      if (launch_bwd_dq(kp, p.dtype, p.d_h, p.d_v, stream) != 0) return ATTN_ERR_HIP;
+    }
+    if ((passes & kDkdv) && has_k) {
+      kp.per_group = nkblk;
+      if (launch_bwd_dkdv(kp, p.dtype, p.d_h, p.d_v, stream) != 0) return ATTN_ERR_HIP;
+    }
   }
   return ATTN_OK;
 }
@@ -178,26 +181,21 @@ attn_status attn_bwd(const attn_problem* prob, const attn_mask* mask, const void
                      const void* V, const void* O, const float* lse, const void* dO, void* dQ, void* dK,
                      void* dV, void* workspace, size_t workspace_bytes, void* stream) {
   const BwdPtrs t{Q, K, V, O, dO, lse, dQ, dK, dV};
-  return bwd_stages(prob, mask, t, workspace, workspace_bytes, stream, kPrepare | kMain | kFinish);
+  return bwd_passes(prob, mask, t, workspace, workspace_bytes, stream, kDq | kDkdv);
 }
 
-attn_status attn_bwd_prepare(const attn_problem* prob, const attn_mask* mask, const void* O,
-                             const void* dO, void* workspace, size_t workspace_bytes, void* stream) {
-  const BwdPtrs t{nullptr, nullptr, nullptr, O, dO, nullptr, nullptr, nullptr, nullptr};
-  return bwd_stages(prob, mask, t, workspace, workspace_bytes, stream, kPrepare);
+attn_status attn_bwd_dq(const attn_problem* prob, const attn_mask* mask, const void* Q, const void* K,
+                        const void* V, const void* O, const float* lse, const void* dO, void* dQ,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  const BwdPtrs t{Q, K, V, O, dO, lse, dQ, nullptr, nullptr};
+  return bwd_passes(prob, mask, t, workspace, workspace_bytes, stream, kDq);
 }
 
-attn_status attn_bwd_main(const attn_problem* prob, const attn_mask* mask, const void* Q, const void* K,
+attn_status attn_bwd_dkdv(const attn_problem* prob, const attn_mask* mask, const void* Q, const void* K,
                           const void* V, const float* lse, const void* dO, void* dK, void* dV,
                           void* workspace, size_t workspace_bytes, void* stream) {
   const BwdPtrs t{Q, K, V, nullptr, dO, lse, nullptr, dK, dV};
-  return bwd_stages(prob, mask, t, workspace, workspace_bytes, stream, kMain);
-}
-
-attn_status attn_bwd_finish(const attn_problem* prob, const attn_mask* mask, void* dQ, void* workspace,
-                            size_t workspace_bytes, void* stream) {
-  const BwdPtrs t{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, dQ, nullptr, nullptr};
-  return bwd_stages(prob, mask, t, workspace, workspace_bytes, stream, kFinish);
+  return bwd_passes(prob, mask, t, workspace, workspace_bytes, stream, kDkdv);
 }
 
 const char* attn_status_string(attn_status s) {

@@ -138,6 +138,38 @@ template <> __device__ __forceinline__ void st4<float>(float* p, float a, float 
   *reinterpret_cast<f32x4*>(p) = v;
 }
 
+// ---------------------------------------------------------------- row staging
+// Moves ROWS rows of a row-major [n][D] tensor (unit stride in d, row stride
+// in elements) into an LDS tile with row stride LDS_STRIDE, in 16-byte chunks
+// through registers, so the global loads of the next tile can be in flight
+// while the current one is consumed.  Rows at or beyond `limit` read as zero.
+template <typename T, int ROWS, int D, int NT>
+struct RowStager {
+  static constexpr int CH = D * (int)sizeof(T) / 16;  // 16-byte chunks per row
+  static constexpr int N = ROWS * CH / NT;             // chunks per thread
+  static_assert(ROWS * CH % NT == 0, "tile must split evenly over the threads");
+  u32x4 r[N];
+
+  __device__ __forceinline__ void load(const T* base, int64_t row_stride, int row0, int limit, int tid) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int c = tid + NT * i;
+      const int row = c / CH, col = c % CH;
+      const int g = row0 + row;
+      r[i] = g < limit ? *reinterpret_cast<const u32x4*>((const char*)(base + (int64_t)g * row_stride) + 16 * col)
+                       : u32x4{0, 0, 0, 0};
+    }
+  }
+  __device__ __forceinline__ void store(T* lds, int lds_stride, int tid) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int c = tid + NT * i;
+      const int row = c / CH, col = c % CH;
+      *reinterpret_cast<u32x4*>((char*)(lds + row * lds_stride) + 16 * col) = r[i];
+    }
+  }
+};
+
 // ---------------------------------------------------------------- work mapping
 // Work is grouped in units (a sequence and a KV head) of `per_group` items.
 // With xcd_map, unit u runs on XCD u % 8: workgroups are dealt to the 8 XCDs

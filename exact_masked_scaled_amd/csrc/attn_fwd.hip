@@ -39,7 +39,7 @@ __device__ __forceinline__ int key_limit(int i, int Lk, int causal, int off) {
 }
 
 template <typename T, int DH, int DV>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(const KernelParams p) {
+__global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(const KernelParams p) {
   using C = FwdCfg<T, DH, DV>;
   using op_t = typename Op<T>::type;
   __shared__ __attribute__((aligned(16))) T k_lds[2][C::BN * C::KS];

@@ -24,7 +24,6 @@ struct KernelParams {
   void* o_out;        // forward: O
   float* lse;         // [B][H_q][n_q]
   float* delta;       // workspace: D = rowsum(G_O o O), [B][H_q][n_q]
-  float* dq_acc;      // workspace: float32 G_Q accumulator, [B][H_q][n_q][d_h]
   void* dq;
   void* dk;
   void* dv;
@@ -52,12 +51,12 @@ attn_status validate_problem(const attn_problem* prob, const attn_mask* mask);
 // Launchers (defined in the .hip translation units).  Return hipSuccess or
 // the launch error, as an int to keep this header free of HIP types.
 int launch_fwd(const KernelParams& p, int dtype, int d_h, int d_v, void* stream);
-int launch_bwd_pre(const KernelParams& p, int dtype, int d_h, int d_v, void* stream);
-int launch_bwd_main(const KernelParams& p, int dtype, int d_h, int d_v, void* stream);
-int launch_bwd_dq(const KernelParams& p, int dtype, int d_h, void* stream);
+int launch_bwd_dq(const KernelParams& p, int dtype, int d_h, int d_v, void* stream);
+int launch_bwd_dkdv(const KernelParams& p, int dtype, int d_h, int d_v, void* stream);
 
 // Tile sizes the dispatcher needs to size grids.
 int fwd_block_rows(int dtype);
-int bwd_block_keys(int dtype);
+int bwd_dq_block_rows(int dtype);
+int bwd_dkdv_block_keys(int dtype);
 
 }  // namespace attn

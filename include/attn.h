@@ -98,8 +98,8 @@ typedef struct {
 attn_status attn_validate(const attn_problem* prob, const attn_mask* mask);
 
 /* Bytes of device workspace attn_bwd needs for `prob` (256-byte aligned
- * base).  The workspace holds per-row float32 D_i = rowsum(G_O o O) and a
- * float32 accumulator for G_Q; its contents on entry are ignored. */
+ * base): per-row float32 D_i = rowsum(G_O o O), B * H_q * n_q floats.  Its
+ * contents on entry are ignored. */
 size_t attn_bwd_workspace_size(const attn_problem* prob);
 
 /* Forward.  Q [B,H_q,n_q,d_h], K [B,H_kv,n_k,d_h], V [B,H_kv,n_k,d_v] in;
@@ -119,25 +119,23 @@ attn_status attn_bwd(const attn_problem* prob, const attn_mask* mask,
                      void* dQ, void* dK, void* dV,
                      void* workspace, size_t workspace_bytes, void* stream);
 
-/* The backward in its three stages, for callers that schedule or time them
- * separately; attn_bwd is exactly prepare, main and finish enqueued in that
- * order on one stream with one workspace.  Each stage validates like
- * attn_bwd.
- *   prepare: D_i = rowsum(G_O o O) into the workspace (the row scalar c_i of
- *            eq. A.10.7) and clears the workspace's float32 G_Q accumulator;
- *   main:    writes G_K and G_V and accumulates G_Q into the workspace
- *            (eqs. A.10.5-A.10.9), reading D from the workspace;
- *   finish:  converts the G_Q accumulator to the I/O dtype into dQ.
- * Pointers a stage does not use may be NULL. */
-attn_status attn_bwd_prepare(const attn_problem* prob, const attn_mask* mask,
-                             const void* O, const void* dO,
-                             void* workspace, size_t workspace_bytes, void* stream);
-attn_status attn_bwd_main(const attn_problem* prob, const attn_mask* mask,
+/* The backward in its two passes, for callers that schedule or time them
+ * separately; attn_bwd is exactly attn_bwd_dq followed by attn_bwd_dkdv on
+ * one stream with one workspace.  Each validates like attn_bwd.
+ *   dq:   forms D_i = rowsum(G_O o O) (the row scalar c_i of eq. A.10.7) into
+ *         the workspace and writes G_Q (eqs. A.10.6-A.10.8);
+ *   dkdv: reads D from the workspace and writes G_K and G_V (eqs. A.10.5-7,
+ *         A.10.9), summed over the query heads of each KV head.
+ * Each G_Q, G_K and G_V element is written exactly once (no atomics), so
+ * results are bitwise reproducible. */
+attn_status attn_bwd_dq(const attn_problem* prob, const attn_mask* mask,
+                        const void* Q, const void* K, const void* V,
+                        const void* O, const float* lse, const void* dO, void* dQ,
+                        void* workspace, size_t workspace_bytes, void* stream);
+attn_status attn_bwd_dkdv(const attn_problem* prob, const attn_mask* mask,
                           const void* Q, const void* K, const void* V,
                           const float* lse, const void* dO, void* dK, void* dV,
                           void* workspace, size_t workspace_bytes, void* stream);
-attn_status attn_bwd_finish(const attn_problem* prob, const attn_mask* mask, void* dQ,
-                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* attn_status_string(attn_status status);

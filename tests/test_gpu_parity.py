@@ -188,18 +188,17 @@ def test_empty_row_is_an_error_on_gpu_call():
 
 
 def test_repeat_calls_are_stable():
-    """Forward and G_K/G_V are deterministic; G_Q differs at most by the order
-    of its float32 atomic additions."""
+    """Every output is bitwise reproducible (each element is written once, in a
+    fixed order of additions)."""
     inp = W.make_custom_inputs(W.custom_workload(W.BF16, 1, 4, 1, 256, 256, 128, 128, True), seed=3)
     a = P.run_gpu(inp)
     b = P.run_gpu(inp)
-    for n in ("O", "lse", "GK", "GV"):
+    for n in ("O", "lse", "GQ", "GK", "GV"):
         assert bool((a[n] == b[n]).all()), n
-    assert P.rel_err(P.to_f64(a["GQ"]), P.to_f64(b["GQ"])) < 1e-2
 
 
 def test_staged_backward_equals_bwd():
-    """attn_bwd_prepare + attn_bwd_main + attn_bwd_finish give what attn_bwd gives."""
+    """attn_bwd_dq followed by attn_bwd_dkdv gives what attn_bwd gives."""
     import torch
     inp = W.make_custom_inputs(W.custom_workload(W.BF16, 2, 4, 2, 200, 260, 128, 128, True, 60),
                                seed=5, seqlens_q=[200, 111], seqlens_k=[260, 170])
@@ -210,7 +209,7 @@ def test_staged_backward_equals_bwd():
     prob = A._problem_from(q, k, v, A._strides(o))
     ws = torch.full((A.workspace_size(prob),), 0xFF, dtype=torch.uint8, device=q.device)
     st = A.StagedBackward(q, k, v, o, lse, do, dq, dk, dv, ws, **inp.mask_kwargs())
-    st.prepare(); st.main(); st.finish()
+    st.dq(); st.dkdv()
     torch.cuda.synchronize()
     assert bool((dk == ref["GK"]).all()) and bool((dv == ref["GV"]).all())
-    assert P.rel_err(P.to_f64(dq), P.to_f64(ref["GQ"])) < 1e-2
+    assert bool((dq == ref["GQ"]).all())
