@@ -45,10 +45,8 @@ struct DqCfg {
   static constexpr int NW = 4;
   static constexpr int BM = 32 * NW;
   static constexpr int BN = 64;
-  static constexpr int PAD = 32 / (int)sizeof(T);
-  static constexpr int KS = DH + PAD;
-  static constexpr int VS = DV + PAD;
-  static constexpr int OCC = sizeof(T) == 2 ? 2 : 1;
+  static constexpr int KS = Tile<T, DH>::STRIDE;
+  static constexpr int VS = Tile<T, DV>::STRIDE;
 };
 
 template <typename T, int DH, int DV>
@@ -121,19 +119,18 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(con
     for (int ks = 0; ks < DH / 16; ++ks)
       qreg[ks] = row_exists ? ld8<T>(Qb + (int64_t)qi * p.q_sr + 16 * ks + 8 * kg) : zero_op<T>();
 
-    RowStager<T, C::BN, DH, 64 * C::NW> kst;
-    RowStager<T, C::BN, DV, 64 * C::NW> vst;
-    kst.load(Kb, p.k_sr, 0, p.n_k, tid);
-    vst.load(Vb, p.v_sr, 0, p.n_k, tid);
-    kst.store(k_lds[0], C::KS, tid);
-    vst.store(v_lds[0], C::VS, tid);
+    using KL = TileLoad<T, C::BN, DH, 64 * C::NW>;
+    using VL = TileLoad<T, C::BN, DV, 64 * C::NW>;
+    KL::issue(Kb, p.k_sr, 0, p.n_k, k_lds[0], tid);
+    VL::issue(Vb, p.v_sr, 0, p.n_k, v_lds[0], tid);
+    wait_tile_loads();
     __syncthreads();
 
     for (int t = 0; t < ntiles; ++t) {
       const int buf = t & 1;
       if (t + 1 < ntiles) {
-        kst.load(Kb, p.k_sr, (t + 1) * C::BN, p.n_k, tid);
-        vst.load(Vb, p.v_sr, (t + 1) * C::BN, p.n_k, tid);
+        KL::issue(Kb, p.k_sr, (t + 1) * C::BN, p.n_k, k_lds[buf ^ 1], tid);
+        VL::issue(Vb, p.v_sr, (t + 1) * C::BN, p.n_k, v_lds[buf ^ 1], tid);
       }
       if (t < wtiles) {
         const T* Ks = k_lds[buf];
@@ -145,10 +142,10 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(con
           for (int e = 0; e < 16; ++e) { s[mt][e] = 0.f; dp[mt][e] = 0.f; }
 #pragma unroll
           for (int ks = 0; ks < DH / 16; ++ks)
-            mma(s[mt], ld8<T>(Ks + (32 * mt + (lane & 31)) * C::KS + 16 * ks + 8 * kg), qreg[ks]);
+            mma(s[mt], ld8_tile<T, DH>(Ks, 32 * mt + (lane & 31), 16 * ks + 8 * kg), qreg[ks]);
 #pragma unroll
           for (int ks = 0; ks < DV / 16; ++ks)
-            mma(dp[mt], ld8<T>(Vs + (32 * mt + (lane & 31)) * C::VS + 16 * ks + 8 * kg), doreg[ks]);
+            mma(dp[mt], ld8_tile<T, DV>(Vs, 32 * mt + (lane & 31), 16 * ks + 8 * kg), doreg[ks]);
         }
         const bool masked = t >= nfull;
 #pragma unroll
@@ -173,13 +170,10 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(con
             const op_t bop = to_op<T>(tmp);
 #pragma unroll
             for (int dt = 0; dt < DH / 32; ++dt)
-              mma(acc[dt], ld_tr<T>(Ks, C::KS, 32 * mt + 16 * st, 32 * dt), bop);
+              mma(acc[dt], ld_tr<T, DH>(Ks, 32 * mt + 16 * st, 32 * dt), bop);
           }
       }
-      if (t + 1 < ntiles) {
-        kst.store(k_lds[buf ^ 1], C::KS, tid);
-        vst.store(v_lds[buf ^ 1], C::VS, tid);
-      }
+      wait_tile_loads();
       __syncthreads();
     }
   }
@@ -204,9 +198,8 @@ struct DkvCfg {
   static constexpr int KT = 1;                        // 32-key tiles per wave
   static constexpr int BN = 32 * KT * NW;             // keys per workgroup
   static constexpr int BM = 32;                       // query rows per step
-  static constexpr int PAD = 32 / (int)sizeof(T);
-  static constexpr int QS = DH + PAD;
-  static constexpr int OS = DV + PAD;
+  static constexpr int QS = Tile<T, DH>::STRIDE;
+  static constexpr int OS = Tile<T, DV>::STRIDE;
 };
 
 template <typename T, int DH, int DV>
@@ -270,15 +263,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const KernelParams p) 
     // the wave's key range decides whether a step needs the element mask
     const int wk_hi = kw0 + 32 * KT;  // exclusive
 
-    RowStager<T, C::BM, DH, 64 * C::NW> qst;
-    RowStager<T, C::BM, DV, 64 * C::NW> ost;
+    using QL = TileLoad<T, C::BM, DH, 64 * C::NW>;
+    using OL = TileLoad<T, C::BM, DV, 64 * C::NW>;
     float lse_st = 0.f, dlt_st = 0.f;
-    auto stage_load = [&](int s) {
+    // Q and G_O rows of step s go straight to LDS; their lse (in log2 units)
+    // and D go through registers and are written to LDS by stage_rows
+    auto stage_issue = [&](int s, int buf) {
       const int rr = s / nq, qb = qb_first + s % nq;
       const int r = g * p.group + rr;
       const int q0 = qb * C::BM;
-      qst.load((const T*)p.q + b * p.q_sb + r * p.q_sh, p.q_sr, q0, p.n_q, tid);
-      ost.load((const T*)p.dout + b * p.o_sb + r * p.o_sh, p.o_sr, q0, p.n_q, tid);
+      QL::issue((const T*)p.q + b * p.q_sb + r * p.q_sh, p.q_sr, q0, p.n_q, q_lds[buf], tid);
+      OL::issue((const T*)p.dout + b * p.o_sb + r * p.o_sh, p.o_sr, q0, p.n_q, do_lds[buf], tid);
       if (tid < C::BM) {
         const int q = q0 + tid;
         const int64_t rb = ((int64_t)b * p.H_q + r) * p.n_q;
@@ -286,95 +281,119 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const KernelParams p) 
         dlt_st = q < p.n_q ? p.delta[rb + q] : 0.f;
       }
     };
-    auto stage_store = [&](int buf) {
-      qst.store(q_lds[buf], C::QS, tid);
-      ost.store(do_lds[buf], C::OS, tid);
+    auto stage_rows = [&](int buf) {
       if (tid < C::BM) {
         lse_lds[buf][tid] = lse_st;
         dlt_lds[buf][tid] = dlt_st;
       }
     };
 
-    stage_load(0);
-    stage_store(0);
+    stage_issue(0, 0);
+    stage_rows(0);
+    wait_tile_loads();
     __syncthreads();
 
     for (int s = 0; s < nsteps; ++s) {
       const int buf = s & 1;
       const int q0 = (qb_first + s % nq) * C::BM;
-      if (s + 1 < nsteps) stage_load(s + 1);
+      if (s + 1 < nsteps) stage_issue(s + 1, buf ^ 1);
       const T* Qs = q_lds[buf];
       const T* Os = do_lds[buf];
 
-      // S = Q K^T and dP = G_O V^T for the wave's keys (lane = key)
-      f32x16 sv[KT], dp[KT];
+      // With bf16 operands every LDS operand of the step is read up front, so
+      // the products below run back to back instead of each waiting on its
+      // own read (there are registers for it at one wave per SIMD; the float32
+      // operands are twice as large and are read where they are used):
+      // A operands of S = Q K^T and dP = G_O V^T (row order, lane = query)...
+      constexpr bool PRELOAD = sizeof(T) == 2;
+      op_t qa[DH / 16], oa[DV / 16];
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt)
+      for (int ks = 0; ks < DH / 16; ++ks) qa[ks] = ld8_tile<T, DH>(Qs, lane & 31, 16 * ks + 8 * kg);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) { sv[kt][e] = 0.f; dp[kt][e] = 0.f; }
+      for (int ks = 0; ks < DV / 16; ++ks) oa[ks] = ld8_tile<T, DV>(Os, lane & 31, 16 * ks + 8 * kg);
+      // ...and B operands of G_V += P^T G_O and G_K += G_S^T Q (C order, lane = d)
+      op_t ob[2][DV / 32], qb[2][DH / 32];
+      auto read_b = [&](int st) {
 #pragma unroll
-      for (int ks = 0; ks < DH / 16; ++ks) {
-        const op_t a = ld8<T>(Qs + (lane & 31) * C::QS + 16 * ks + 8 * kg);
+        for (int nt = 0; nt < DV / 32; ++nt) ob[st][nt] = ld_tr<T, DV>(Os, 16 * st, 32 * nt);
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt) mma(sv[kt], a, kreg[kt][ks]);
+        for (int nt = 0; nt < DH / 32; ++nt) qb[st][nt] = ld_tr<T, DH>(Qs, 16 * st, 32 * nt);
+      };
+      if constexpr (PRELOAD) {
+        read_b(0);
+        read_b(1);
       }
-#pragma unroll
-      for (int ks = 0; ks < DV / 16; ++ks) {
-        const op_t a = ld8<T>(Os + (lane & 31) * C::OS + 16 * ks + 8 * kg);
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt) mma(dp[kt], a, vreg[kt][ks]);
-      }
-      // P and G_S; rows of this lane's registers: q0 + 8*(e/4) + 4*kg + e%4
-      const bool full = (q0 + C::BM <= Lq) && (wk_hi <= Lk) && (!p.causal || wk_hi - 1 <= q0 + p.offset);
       f32x4 l4[4], d4[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         l4[j] = *reinterpret_cast<const f32x4*>(&lse_lds[buf][8 * j + 4 * kg]);
         d4[j] = *reinterpret_cast<const f32x4*>(&dlt_lds[buf][8 * j + 4 * kg]);
       }
+
+      // S and dP for the wave's keys (lane = key, registers = queries)
+      f32x16 sv[KT], dp[KT];
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        const int key = kw0 + 32 * kt + (lane & 31);
+      for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          float pv = __builtin_amdgcn_exp2f(sv[kt][e] * p.scale_log2 - l4[e >> 2][e & 3]);
-          if (!full) {
-            const int q = q0 + 8 * (e >> 2) + 4 * kg + (e & 3);
-            const bool vis = (key < Lk) && (q < Lq) && (!p.causal || key <= q + p.offset);
-            pv = vis ? pv : 0.f;
+        for (int e = 0; e < 16; ++e) { sv[kt][e] = 0.f; dp[kt][e] = 0.f; }
+#pragma unroll
+      for (int ks = 0; ks < DH / 16; ++ks)
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) mma(sv[kt], qa[ks], kreg[kt][ks]);
+#pragma unroll
+      for (int ks = 0; ks < DV / 16; ++ks)
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) mma(dp[kt], oa[ks], vreg[kt][ks]);
+
+      // P = exp(S/sqrt(d) - lse) on the visible set and G_S = P o (dP - D);
+      // register e holds query q0 + 8*(e/4) + 4*kg + e%4
+      const bool full = (q0 + C::BM <= Lq) && (wk_hi <= Lk) && (!p.causal || wk_hi - 1 <= q0 + p.offset);
+      if (full) {
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const float pv = __builtin_amdgcn_exp2f(sv[kt][e] * p.scale_log2 - l4[e >> 2][e & 3]);
+            sv[kt][e] = pv;
+            dp[kt][e] = pv * (dp[kt][e] - d4[e >> 2][e & 3]);
           }
-          sv[kt][e] = pv;
-          dp[kt][e] = pv * (dp[kt][e] - d4[e >> 2][e & 3]);
+      } else {
+        const int off_eff = p.causal ? p.offset : p.n_k;  // j <= i + n_k always holds
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+          const int key = kw0 + 32 * kt + (lane & 31);
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int q = q0 + 8 * (e >> 2) + 4 * kg + (e & 3);
+            const bool vis = (key < Lk) & (q < Lq) & (key <= q + off_eff);
+            float pv = __builtin_amdgcn_exp2f(sv[kt][e] * p.scale_log2 - l4[e >> 2][e & 3]);
+            pv = vis ? pv : 0.f;
+            sv[kt][e] = pv;
+            dp[kt][e] = pv * (dp[kt][e] - d4[e >> 2][e & 3]);
+          }
         }
       }
-      // G_V += P^T G_O, G_K += G_S^T Q (A = this lane's key row; B by transposed read)
+      // G_V += P^T G_O, G_K += G_S^T Q (A = this lane's key row, C order over queries)
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        op_t pa[KT], da[KT];
+        if constexpr (!PRELOAD) read_b(st);
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) {
           float tmp[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) tmp[e] = sv[kt][8 * st + e];
-          pa[kt] = to_op<T>(tmp);
+          const op_t pa = to_op<T>(tmp);
 #pragma unroll
           for (int e = 0; e < 8; ++e) tmp[e] = dp[kt][8 * st + e];
-          da[kt] = to_op<T>(tmp);
-        }
+          const op_t da = to_op<T>(tmp);
 #pragma unroll
-        for (int nt = 0; nt < DV / 32; ++nt) {
-          const op_t bo = ld_tr<T>(Os, C::OS, 16 * st, 32 * nt);
+          for (int nt = 0; nt < DV / 32; ++nt) mma(dv[kt][nt], pa, ob[st][nt]);
 #pragma unroll
-          for (int kt = 0; kt < KT; ++kt) mma(dv[kt][nt], pa[kt], bo);
-        }
-#pragma unroll
-        for (int nt = 0; nt < DH / 32; ++nt) {
-          const op_t bq = ld_tr<T>(Qs, C::QS, 16 * st, 32 * nt);
-#pragma unroll
-          for (int kt = 0; kt < KT; ++kt) mma(dk[kt][nt], da[kt], bq);
+          for (int nt = 0; nt < DH / 32; ++nt) mma(dk[kt][nt], da, qb[st][nt]);
         }
       }
-      if (s + 1 < nsteps) stage_store(buf ^ 1);
+      if (s + 1 < nsteps) stage_rows(buf ^ 1);
+      wait_tile_loads();
       __syncthreads();
     }
   }

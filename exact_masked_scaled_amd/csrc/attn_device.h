@@ -69,6 +69,34 @@ template <typename T> __device__ __forceinline__ typename Op<T>::type zero_op() 
   return r;
 }
 
+// ---------------------------------------------------------------- LDS tiles
+// Layout of a row-major [rows][D] tile in LDS, without padding: the 16-byte
+// chunk c of row r is stored at chunk position c ^ f(r) of that row.  Two read
+// patterns must be free of bank conflicts (64 banks x 4 bytes):
+//   row reads:  16 lanes read the same 16-byte chunk of 16 consecutive rows
+//               (operands in row order, ld8_tile);
+//   transposed: 32 lanes read 8 bytes each from rows 4i..4i+3, 4 consecutive
+//               chunks (ld_tr).
+// With 256-byte rows (bf16, d = 128) both patterns touch 16 distinct chunk
+// positions modulo 256 bytes for f(r) = 4*(r % 4) + (r / 4) % 4; with 128-byte
+// rows (bf16, d = 64; two rows per 256 bytes) for
+// f(r) = 4*((r / 2) % 2) + (r / 4) % 4.  float32 tiles (the float32 path)
+// reuse the first function on their 16-byte chunks.
+template <typename T, int D>
+struct Tile {
+  static constexpr int STRIDE = D;                        // elements per row
+  static constexpr int EPC = 16 / (int)sizeof(T);         // elements per chunk
+  static constexpr int CH = D / EPC;                      // chunks per row
+  static __device__ __forceinline__ int f(int r) {
+    if constexpr (sizeof(T) == 2 && D == 64) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+    else return ((r & 3) << 2) | ((r >> 2) & 3);
+  }
+  static_assert(CH >= 8, "swizzle needs at least 8 chunks per row");
+  static __device__ __forceinline__ int off(int r, int e) {
+    return r * D + ((((e / EPC) ^ f(r))) * EPC) + (e % EPC);
+  }
+};
+
 // ---------------------------------------------------------------- 8-element row reads
 // 8 consecutive elements starting at p (16-byte aligned): one or two b128 reads.
 template <typename T> __device__ __forceinline__ typename Op<T>::type ld8(const T* p);
@@ -83,36 +111,50 @@ template <> __device__ __forceinline__ f32x8 ld8<float>(const float* p) {
   r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
   return r;
 }
+// Elements e..e+7 (e a multiple of 8) of row r of an LDS tile.
+template <typename T, int D>
+__device__ __forceinline__ typename Op<T>::type ld8_tile(const T* tile, int r, int e) {
+  if constexpr (sizeof(T) == 2) {
+    return ld8<T>(tile + Tile<T, D>::off(r, e));  // one chunk
+  } else {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(tile + Tile<T, D>::off(r, e));
+    const f32x4 b = *reinterpret_cast<const f32x4*>(tile + Tile<T, D>::off(r, e + 4));
+    f32x8 v;
+    v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+    v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
+    return v;
+  }
+}
 
 // ---------------------------------------------------------------- transposed reads
-// Operand chunk in C order from a row-major LDS matrix X[k][n] (n contiguous,
-// row stride `ld` elements): lane l receives X[kb + 8*(e/4) + 4*(l/32) + e%4]
-// [nb + l % 32] for e = 0..7.  Usable as an A operand (m = n index) or a B
-// operand (n index), contracting over k.
+// Operand chunk in C order from an LDS tile X[k][n] (n the contiguous index):
+// lane l receives X[kb + 8*(e/4) + 4*(l/32) + e%4][nb + l % 32] for e = 0..7.
+// Usable as an A operand (m = n index) or a B operand (n index), contracting
+// over k.  kb must be a multiple of 16 and nb a multiple of 32.
 //
 // bf16: two ds_read_b64_tr_b16.  Within each 16-lane group the instruction
 // hands lane t element e' of the 64-bit word read by source lane 4*e' + t/4,
 // column t % 4; so source lane s points at row (s / 4), columns 4*(s % 4).
-template <typename T> __device__ __forceinline__ typename Op<T>::type ld_tr(const T* X, int ld, int kb, int nb);
-template <> __device__ __forceinline__ bf16x8 ld_tr<__bf16>(const __bf16* X, int ld, int kb, int nb) {
+template <typename T, int D>
+__device__ __forceinline__ typename Op<T>::type ld_tr(const T* X, int kb, int nb) {
   const int l = lane_id();
-  const int s = l & 15, grp = l >> 4;
-  const __bf16* p0 = X + (kb + 4 * (grp >> 1) + (s >> 2)) * ld + nb + 16 * (grp & 1) + 4 * (s & 3);
-  const __bf16* p1 = p0 + 8 * ld;
-  i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4*)(p0));
-  i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4*)(p1));
-  union { i16x4 v[2]; bf16x8 b; } u;
-  u.v[0] = lo;
-  u.v[1] = hi;
-  return u.b;
-}
-template <> __device__ __forceinline__ f32x8 ld_tr<float>(const float* X, int ld, int kb, int nb) {
-  const int l = lane_id();
-  const float* p = X + (kb + 4 * (l >> 5)) * ld + nb + (l & 31);
-  f32x8 r;
+  if constexpr (sizeof(T) == 2) {
+    const int s = l & 15, grp = l >> 4;
+    const int r0 = kb + 4 * (grp >> 1) + (s >> 2);
+    const int e0 = nb + 16 * (grp & 1) + 4 * (s & 3);
+    i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4*)(X + Tile<T, D>::off(r0, e0)));
+    i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4*)(X + Tile<T, D>::off(r0 + 8, e0)));
+    union { i16x4 v[2]; bf16x8 b; } u;
+    u.v[0] = lo;
+    u.v[1] = hi;
+    return u.b;
+  } else {
+    const int r0 = kb + 4 * (l >> 5), n = nb + (l & 31);
+    f32x8 r;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = p[(8 * (e >> 2) + (e & 3)) * ld];
-  return r;
+    for (int e = 0; e < 8; ++e) r[e] = X[Tile<T, D>::off(r0 + 8 * (e >> 2) + (e & 3), n)];
+    return r;
+  }
 }
 
 // ---------------------------------------------------------------- cross-lane
@@ -138,37 +180,41 @@ template <> __device__ __forceinline__ void st4<float>(float* p, float a, float 
   *reinterpret_cast<f32x4*>(p) = v;
 }
 
-// ---------------------------------------------------------------- row staging
-// Moves ROWS rows of a row-major [n][D] tensor (unit stride in d, row stride
-// in elements) into an LDS tile with row stride LDS_STRIDE, in 16-byte chunks
-// through registers, so the global loads of the next tile can be in flight
-// while the current one is consumed.  Rows at or beyond `limit` read as zero.
+// ---------------------------------------------------------------- tile staging
+// Copies ROWS rows of a row-major [n][D] global tensor (unit stride in d, row
+// stride in elements) into an LDS tile laid out as Tile<T, D>, with direct
+// global-to-LDS loads (global_load_lds_dwordx4): no registers hold the data
+// and the copy completes asynchronously (vmcnt), so the next tile can be in
+// flight while the current one is consumed.  One instruction moves 64
+// consecutive 16-byte chunks of the tile (lane i -> chunk i), so each lane
+// fetches the global chunk that the swizzle places there.  Rows at or beyond
+// `limit` are filled with copies of row limit - 1 (limit >= 1): every kernel
+// masks those rows out before they can reach an output.
 template <typename T, int ROWS, int D, int NT>
-struct RowStager {
-  static constexpr int CH = D * (int)sizeof(T) / 16;  // 16-byte chunks per row
-  static constexpr int N = ROWS * CH / NT;             // chunks per thread
-  static_assert(ROWS * CH % NT == 0, "tile must split evenly over the threads");
-  u32x4 r[N];
+struct TileLoad {
+  using L = Tile<T, D>;
+  static constexpr int CHUNKS = ROWS * L::CH;
+  static constexpr int N = CHUNKS / NT;  // instructions per thread
+  static_assert(CHUNKS % NT == 0, "tile must split evenly over the threads");
 
-  __device__ __forceinline__ void load(const T* base, int64_t row_stride, int row0, int limit, int tid) {
+  static __device__ __forceinline__ void issue(const T* base, int64_t row_stride, int row0, int limit, T* lds,
+                                               int tid) {
+    const int wave_base = (tid >> 6) * 64, lane = tid & 63;
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const int c = tid + NT * i;
-      const int row = c / CH, col = c % CH;
-      const int g = row0 + row;
-      r[i] = g < limit ? *reinterpret_cast<const u32x4*>((const char*)(base + (int64_t)g * row_stride) + 16 * col)
-                       : u32x4{0, 0, 0, 0};
-    }
-  }
-  __device__ __forceinline__ void store(T* lds, int lds_stride, int tid) const {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int c = tid + NT * i;
-      const int row = c / CH, col = c % CH;
-      *reinterpret_cast<u32x4*>((char*)(lds + row * lds_stride) + 16 * col) = r[i];
+      const int first = wave_base + NT * i;  // first chunk written by this wave instruction
+      const int pc = first + lane;           // physical chunk this lane fills
+      const int row = pc / L::CH;
+      const int chunk = (pc % L::CH) ^ L::f(row);
+      const int g = min(row0 + row, limit - 1);
+      const T* src = base + (int64_t)g * row_stride + chunk * L::EPC;
+      __builtin_amdgcn_global_load_lds((const void*)src, (ATTN_LDS void*)(lds + first * L::EPC), 16, 0, 0);
     }
   }
 };
+
+// Wait until every global-to-LDS copy issued by this wave has landed.
+__device__ __forceinline__ void wait_tile_loads() { __builtin_amdgcn_s_waitcnt(0); }
 
 // ---------------------------------------------------------------- work mapping
 // Work is grouped in units (a sequence and a KV head) of `per_group` items.

@@ -24,13 +24,8 @@ struct FwdCfg {
   static constexpr int NW = 4;            // waves per workgroup
   static constexpr int BM = 32 * NW;      // query rows per workgroup
   static constexpr int BN = 64;           // keys per tile
-  static constexpr int PAD = 32 / (int)sizeof(T);  // 32 bytes of row padding in LDS
-  static constexpr int KS = DH + PAD;     // LDS row stride of K tiles (elements)
-  static constexpr int VS = DV + PAD;     // LDS row stride of V tiles
-  static constexpr int CH_K = DH * (int)sizeof(T) / 16;   // 16-byte chunks per K row
-  static constexpr int CH_V = DV * (int)sizeof(T) / 16;
-  static constexpr int LOAD_K = BN * CH_K / (64 * NW);    // chunks per thread per tile
-  static constexpr int LOAD_V = BN * CH_V / (64 * NW);
+  static constexpr int KS = Tile<T, DH>::STRIDE;  // LDS row stride of K tiles (elements)
+  static constexpr int VS = Tile<T, DV>::STRIDE;  // LDS row stride of V tiles
 };
 
 // Row i sees keys j < kmax(i).
@@ -99,50 +94,20 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(const 
     for (int ks = 0; ks < DH / 16; ++ks)
       qreg[ks] = row_exists ? ld8<T>(Qb + (int64_t)qi * p.q_sr + 16 * ks + 8 * kg) : zero_op<T>();
 
-    // global -> register staging of one K/V tile
-    u32x4 kst[C::LOAD_K], vst[C::LOAD_V];
-    auto load_tile = [&](int t) {
-#pragma unroll
-      for (int i = 0; i < C::LOAD_K; ++i) {
-        const int c = tid + 64 * C::NW * i;
-        const int row = c / C::CH_K, col = c % C::CH_K;
-        const int key = t * C::BN + row;
-        kst[i] = key < p.n_k ? *reinterpret_cast<const u32x4*>(
-                                   (const char*)(Kb + (int64_t)key * p.k_sr) + 16 * col)
-                             : u32x4{0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int i = 0; i < C::LOAD_V; ++i) {
-        const int c = tid + 64 * C::NW * i;
-        const int row = c / C::CH_V, col = c % C::CH_V;
-        const int key = t * C::BN + row;
-        vst[i] = key < p.n_k ? *reinterpret_cast<const u32x4*>(
-                                   (const char*)(Vb + (int64_t)key * p.v_sr) + 16 * col)
-                             : u32x4{0, 0, 0, 0};
-      }
-    };
-    auto store_tile = [&](int buf) {
-#pragma unroll
-      for (int i = 0; i < C::LOAD_K; ++i) {
-        const int c = tid + 64 * C::NW * i;
-        const int row = c / C::CH_K, col = c % C::CH_K;
-        *reinterpret_cast<u32x4*>((char*)(&k_lds[buf][row * C::KS]) + 16 * col) = kst[i];
-      }
-#pragma unroll
-      for (int i = 0; i < C::LOAD_V; ++i) {
-        const int c = tid + 64 * C::NW * i;
-        const int row = c / C::CH_V, col = c % C::CH_V;
-        *reinterpret_cast<u32x4*>((char*)(&v_lds[buf][row * C::VS]) + 16 * col) = vst[i];
-      }
-    };
-
-    load_tile(0);
-    store_tile(0);
+    // K/V tiles stream through two LDS buffers with direct global-to-LDS loads
+    using KL = TileLoad<T, C::BN, DH, 64 * C::NW>;
+    using VL = TileLoad<T, C::BN, DV, 64 * C::NW>;
+    KL::issue(Kb, p.k_sr, 0, p.n_k, k_lds[0], tid);
+    VL::issue(Vb, p.v_sr, 0, p.n_k, v_lds[0], tid);
+    wait_tile_loads();
     __syncthreads();
 
     for (int t = 0; t < ntiles; ++t) {
       const int buf = t & 1;
-      if (t + 1 < ntiles) load_tile(t + 1);
+      if (t + 1 < ntiles) {
+        KL::issue(Kb, p.k_sr, (t + 1) * C::BN, p.n_k, k_lds[buf ^ 1], tid);
+        VL::issue(Vb, p.v_sr, (t + 1) * C::BN, p.n_k, v_lds[buf ^ 1], tid);
+      }
       if (t < wtiles) {
         const T* Ks = k_lds[buf];
         const T* Vs = v_lds[buf];
@@ -154,7 +119,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(const 
           for (int e = 0; e < 16; ++e) s[mt][e] = 0.f;
 #pragma unroll
           for (int ks = 0; ks < DH / 16; ++ks) {
-            op_t a = ld8<T>(Ks + (32 * mt + (lane & 31)) * C::KS + 16 * ks + 8 * kg);
+            op_t a = ld8_tile<T, DH>(Ks, 32 * mt + (lane & 31), 16 * ks + 8 * kg);
             mma(s[mt], a, qreg[ks]);
           }
         }
@@ -203,12 +168,12 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(const 
             const op_t bop = to_op<T>(pv);
 #pragma unroll
             for (int dt = 0; dt < DV / 32; ++dt) {
-              const op_t aop = ld_tr<T>(Vs, C::VS, 32 * mt + 16 * st, 32 * dt);
+              const op_t aop = ld_tr<T, DV>(Vs, 32 * mt + 16 * st, 32 * dt);
               mma(oacc[dt], aop, bop);
             }
           }
       }
-      if (t + 1 < ntiles) store_tile(buf ^ 1);
+      wait_tile_loads();
       __syncthreads();
     }
   }
