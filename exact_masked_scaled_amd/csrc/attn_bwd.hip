@@ -53,8 +53,12 @@ template <typename T, int DH, int DV>
 __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(const KernelParams p) {
   using C = DqCfg<T, DH, DV>;
   using op_t = typename Op<T>::type;
-  __shared__ __attribute__((aligned(16))) T k_lds[2][C::BN * C::KS];
-  __shared__ __attribute__((aligned(16))) T v_lds[2][C::BN * C::VS];
+  // one array per buffer, so the compiler sees that the copy into one buffer
+  // never aliases reads of the other and leaves the copy in flight
+  __shared__ __attribute__((aligned(16))) T k_lds0[C::BN * C::KS];
+  __shared__ __attribute__((aligned(16))) T k_lds1[C::BN * C::KS];
+  __shared__ __attribute__((aligned(16))) T v_lds0[C::BN * C::VS];
+  __shared__ __attribute__((aligned(16))) T v_lds1[C::BN * C::VS];
 
   const int nqblk = (p.n_q + C::BM - 1) / C::BM;
   int unit, item;
@@ -119,60 +123,79 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(con
     for (int ks = 0; ks < DH / 16; ++ks)
       qreg[ks] = row_exists ? ld8<T>(Qb + (int64_t)qi * p.q_sr + 16 * ks + 8 * kg) : zero_op<T>();
 
-    using KL = TileLoad<T, C::BN, DH, 64 * C::NW>;
-    using VL = TileLoad<T, C::BN, DV, 64 * C::NW>;
-    KL::issue(Kb, p.k_sr, 0, p.n_k, k_lds[0], tid);
-    VL::issue(Vb, p.v_sr, 0, p.n_k, v_lds[0], tid);
-    wait_tile_loads();
-    __syncthreads();
+    // per-lane LDS offsets (K and V tiles share them when d_h == d_v)
+    RowOffsets<T, DH> kro;
+    RowOffsets<T, DV> vro_own;
+    TrOffsets<T, DH> kto;
+    kro.init(lane);
+    kto.init(lane);
+    if constexpr (DH != DV) vro_own.init(lane);
+    const RowOffsets<T, DV>& vro = [&]() -> const RowOffsets<T, DV>& {
+      if constexpr (DH == DV) return kro; else return vro_own;
+    }();
 
-    for (int t = 0; t < ntiles; ++t) {
-      const int buf = t & 1;
-      if (t + 1 < ntiles) {
-        KL::issue(Kb, p.k_sr, (t + 1) * C::BN, p.n_k, k_lds[buf ^ 1], tid);
-        VL::issue(Vb, p.v_sr, (t + 1) * C::BN, p.n_k, v_lds[buf ^ 1], tid);
-      }
-      if (t < wtiles) {
-        const T* Ks = k_lds[buf];
-        const T* Vs = v_lds[buf];
-        f32x16 s[C::BN / 32], dp[C::BN / 32];
+    // one key tile, 32 keys at a time: S^T, dP^T, G_S^T, then
+    // G_Q^T += K^T G_S^T (only one 32-key slice of S^T / dP^T is live at once)
+    auto tile = [&](const int t, const T* Ks, const T* Vs) {
+      const bool masked = t >= nfull;  // tile straddles the causal diagonal or the key length
 #pragma unroll
-        for (int mt = 0; mt < C::BN / 32; ++mt) {
+      for (int mt = 0; mt < C::BN / 32; ++mt) {
+        f32x16 s, dp;
 #pragma unroll
-          for (int e = 0; e < 16; ++e) { s[mt][e] = 0.f; dp[mt][e] = 0.f; }
+        for (int e = 0; e < 16; ++e) { s[e] = 0.f; dp[e] = 0.f; }
 #pragma unroll
-          for (int ks = 0; ks < DH / 16; ++ks)
-            mma(s[mt], ld8_tile<T, DH>(Ks, 32 * mt + (lane & 31), 16 * ks + 8 * kg), qreg[ks]);
+        for (int ks = 0; ks < DH / 16; ++ks) mma(s, kro.read(Ks, 32 * mt, ks), qreg[ks]);
 #pragma unroll
-          for (int ks = 0; ks < DV / 16; ++ks)
-            mma(dp[mt], ld8_tile<T, DV>(Vs, 32 * mt + (lane & 31), 16 * ks + 8 * kg), doreg[ks]);
-        }
-        const bool masked = t >= nfull;
-#pragma unroll
-        for (int mt = 0; mt < C::BN / 32; ++mt)
+        for (int ks = 0; ks < DV / 16; ++ks) mma(dp, vro.read(Vs, 32 * mt, ks), doreg[ks]);
+        if (masked) {
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            float pv = __builtin_amdgcn_exp2f(s[mt][e] * p.scale_log2 - lse2);
-            if (masked) {
-              const int key = t * C::BN + 32 * mt + 8 * (e >> 2) + 4 * kg + (e & 3);
-              pv = key < kmax_lane ? pv : 0.f;
-            }
-            dp[mt][e] = pv * (dp[mt][e] - Di);
+            const int key = t * C::BN + 32 * mt + 8 * (e >> 2) + 4 * kg + (e & 3);
+            float pv = __builtin_amdgcn_exp2f(fmaf(s[e], p.scale_log2, -lse2));
+            pv = key < kmax_lane ? pv : 0.f;
+            dp[e] = pv * (dp[e] - Di);
           }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const float pv = __builtin_amdgcn_exp2f(fmaf(s[e], p.scale_log2, -lse2));
+            dp[e] = pv * (dp[e] - Di);
+          }
+        }
         // G_Q^T += K^T G_S^T: A = K^T (lane = d) by transposed read, B = G_S^T
 #pragma unroll
-        for (int mt = 0; mt < C::BN / 32; ++mt)
+        for (int st = 0; st < 2; ++st) {
+          float tmp[8];
 #pragma unroll
-          for (int st = 0; st < 2; ++st) {
-            float tmp[8];
+          for (int e = 0; e < 8; ++e) tmp[e] = dp[8 * st + e];
+          const op_t bop = to_op<T>(tmp);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) tmp[e] = dp[mt][8 * st + e];
-            const op_t bop = to_op<T>(tmp);
-#pragma unroll
-            for (int dt = 0; dt < DH / 32; ++dt)
-              mma(acc[dt], ld_tr<T, DH>(Ks, 32 * mt + 16 * st, 32 * dt), bop);
-          }
+          for (int dt = 0; dt < DH / 32; ++dt) mma(acc[dt], kto.read(Ks, 32 * mt + 16 * st, dt), bop);
+        }
       }
+    };
+
+    using KL = TileLoad<T, C::BN, DH, 64 * C::NW>;
+    using VL = TileLoad<T, C::BN, DV, 64 * C::NW>;
+    KL::issue(Kb, p.k_sr, 0, p.n_k, k_lds0, tid);
+    VL::issue(Vb, p.v_sr, 0, p.n_k, v_lds0, tid);
+    wait_tile_loads();
+    __syncthreads();
+    // two tiles per trip so each LDS buffer address is a compile-time constant
+    for (int t = 0; t < ntiles; t += 2) {
+      if (t + 1 < ntiles) {
+        KL::issue(Kb, p.k_sr, (t + 1) * C::BN, p.n_k, k_lds1, tid);
+        VL::issue(Vb, p.v_sr, (t + 1) * C::BN, p.n_k, v_lds1, tid);
+      }
+      if (t < wtiles) tile(t, k_lds0, v_lds0);
+      wait_tile_loads();
+      __syncthreads();
+      if (t + 1 >= ntiles) break;
+      if (t + 2 < ntiles) {
+        KL::issue(Kb, p.k_sr, (t + 2) * C::BN, p.n_k, k_lds0, tid);
+        VL::issue(Vb, p.v_sr, (t + 2) * C::BN, p.n_k, v_lds0, tid);
+      }
+      if (t + 1 < wtiles) tile(t + 1, k_lds1, v_lds1);
       wait_tile_loads();
       __syncthreads();
     }
@@ -207,10 +230,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const KernelParams p) 
   using C = DkvCfg<T, DH, DV>;
   using op_t = typename Op<T>::type;
   constexpr int KT = C::KT;
-  __shared__ __attribute__((aligned(16))) T q_lds[2][C::BM * C::QS];
-  __shared__ __attribute__((aligned(16))) T do_lds[2][C::BM * C::OS];
-  __shared__ __attribute__((aligned(16))) float lse_lds[2][C::BM];
-  __shared__ __attribute__((aligned(16))) float dlt_lds[2][C::BM];
+  // one array per buffer (see bwd_dq_kernel)
+  __shared__ __attribute__((aligned(16))) T q_lds0[C::BM * C::QS];
+  __shared__ __attribute__((aligned(16))) T q_lds1[C::BM * C::QS];
+  __shared__ __attribute__((aligned(16))) T do_lds0[C::BM * C::OS];
+  __shared__ __attribute__((aligned(16))) T do_lds1[C::BM * C::OS];
+  __shared__ __attribute__((aligned(16))) float rows_lds0[2 * C::BM];  // lse (log2 units), then D
+  __shared__ __attribute__((aligned(16))) float rows_lds1[2 * C::BM];
 
   int unit, kb;
   if (!map_work(blockIdx.x, p.groups, p.per_group, p.xcd_map, unit, kb)) return;
@@ -268,12 +294,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const KernelParams p) 
     float lse_st = 0.f, dlt_st = 0.f;
     // Q and G_O rows of step s go straight to LDS; their lse (in log2 units)
     // and D go through registers and are written to LDS by stage_rows
-    auto stage_issue = [&](int s, int buf) {
+    auto stage_issue = [&](int s, T* q_dst, T* o_dst) {
       const int rr = s / nq, qb = qb_first + s % nq;
       const int r = g * p.group + rr;
       const int q0 = qb * C::BM;
-      QL::issue((const T*)p.q + b * p.q_sb + r * p.q_sh, p.q_sr, q0, p.n_q, q_lds[buf], tid);
-      OL::issue((const T*)p.dout + b * p.o_sb + r * p.o_sh, p.o_sr, q0, p.n_q, do_lds[buf], tid);
+      QL::issue((const T*)p.q + b * p.q_sb + r * p.q_sh, p.q_sr, q0, p.n_q, q_dst, tid);
+      OL::issue((const T*)p.dout + b * p.o_sb + r * p.o_sh, p.o_sr, q0, p.n_q, o_dst, tid);
       if (tid < C::BM) {
         const int q = q0 + tid;
         const int64_t rb = ((int64_t)b * p.H_q + r) * p.n_q;
@@ -281,24 +307,39 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const KernelParams p) 
         dlt_st = q < p.n_q ? p.delta[rb + q] : 0.f;
       }
     };
-    auto stage_rows = [&](int buf) {
+    auto stage_rows = [&](float* rows) {
       if (tid < C::BM) {
-        lse_lds[buf][tid] = lse_st;
-        dlt_lds[buf][tid] = dlt_st;
+        rows[tid] = lse_st;
+        rows[C::BM + tid] = dlt_st;
       }
     };
 
-    stage_issue(0, 0);
-    stage_rows(0);
+    stage_issue(0, q_lds0, do_lds0);
+    stage_rows(rows_lds0);
     wait_tile_loads();
     __syncthreads();
 
-    for (int s = 0; s < nsteps; ++s) {
-      const int buf = s & 1;
+    // per-lane LDS offsets (Q and G_O tiles share them when d_h == d_v)
+    RowOffsets<T, DH> qro;
+    RowOffsets<T, DV> oro_own;
+    TrOffsets<T, DH> qto;
+    TrOffsets<T, DV> oto_own;
+    qro.init(lane);
+    qto.init(lane);
+    if constexpr (DH != DV) {
+      oro_own.init(lane);
+      oto_own.init(lane);
+    }
+    const RowOffsets<T, DV>& oro = [&]() -> const RowOffsets<T, DV>& {
+      if constexpr (DH == DV) return qro; else return oro_own;
+    }();
+    const TrOffsets<T, DV>& oto = [&]() -> const TrOffsets<T, DV>& {
+      if constexpr (DH == DV) return qto; else return oto_own;
+    }();
+
+    // one step: 32 query rows of one query head against the wave's keys
+    auto step = [&](const int s, const T* Qs, const T* Os, const float* lse_s, const float* dlt_s) {
       const int q0 = (qb_first + s % nq) * C::BM;
-      if (s + 1 < nsteps) stage_issue(s + 1, buf ^ 1);
-      const T* Qs = q_lds[buf];
-      const T* Os = do_lds[buf];
 
       // With bf16 operands every LDS operand of the step is read up front, so
       // the products below run back to back instead of each waiting on its
@@ -308,16 +349,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const KernelParams p) 
       constexpr bool PRELOAD = sizeof(T) == 2;
       op_t qa[DH / 16], oa[DV / 16];
 #pragma unroll
-      for (int ks = 0; ks < DH / 16; ++ks) qa[ks] = ld8_tile<T, DH>(Qs, lane & 31, 16 * ks + 8 * kg);
+      for (int ks = 0; ks < DH / 16; ++ks) qa[ks] = qro.read(Qs, 0, ks);
 #pragma unroll
-      for (int ks = 0; ks < DV / 16; ++ks) oa[ks] = ld8_tile<T, DV>(Os, lane & 31, 16 * ks + 8 * kg);
+      for (int ks = 0; ks < DV / 16; ++ks) oa[ks] = oro.read(Os, 0, ks);
       // ...and B operands of G_V += P^T G_O and G_K += G_S^T Q (C order, lane = d)
       op_t ob[2][DV / 32], qb[2][DH / 32];
       auto read_b = [&](int st) {
 #pragma unroll
-        for (int nt = 0; nt < DV / 32; ++nt) ob[st][nt] = ld_tr<T, DV>(Os, 16 * st, 32 * nt);
+        for (int nt = 0; nt < DV / 32; ++nt) ob[st][nt] = oto.read(Os, 16 * st, nt);
 #pragma unroll
-        for (int nt = 0; nt < DH / 32; ++nt) qb[st][nt] = ld_tr<T, DH>(Qs, 16 * st, 32 * nt);
+        for (int nt = 0; nt < DH / 32; ++nt) qb[st][nt] = qto.read(Qs, 16 * st, nt);
       };
       if constexpr (PRELOAD) {
         read_b(0);
@@ -326,8 +367,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const KernelParams p) 
       f32x4 l4[4], d4[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        l4[j] = *reinterpret_cast<const f32x4*>(&lse_lds[buf][8 * j + 4 * kg]);
-        d4[j] = *reinterpret_cast<const f32x4*>(&dlt_lds[buf][8 * j + 4 * kg]);
+        l4[j] = *reinterpret_cast<const f32x4*>(&lse_s[8 * j + 4 * kg]);
+        d4[j] = *reinterpret_cast<const f32x4*>(&dlt_s[8 * j + 4 * kg]);
       }
 
       // S and dP for the wave's keys (lane = key, registers = queries)
@@ -392,7 +433,33 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const KernelParams p) 
           for (int nt = 0; nt < DH / 32; ++nt) mma(dk[kt][nt], da, qb[st][nt]);
         }
       }
-      if (s + 1 < nsteps) stage_rows(buf ^ 1);
+    };
+
+    if constexpr (sizeof(T) == 4) {  // float32: one step per trip (register budget)
+      for (int s = 0; s < nsteps; ++s) {
+        const bool odd = s & 1;
+        T* qn = odd ? q_lds0 : q_lds1;
+        T* on = odd ? do_lds0 : do_lds1;
+        float* rn = odd ? rows_lds0 : rows_lds1;
+        float* rc = odd ? rows_lds1 : rows_lds0;
+        if (s + 1 < nsteps) stage_issue(s + 1, qn, on);
+        step(s, odd ? q_lds1 : q_lds0, odd ? do_lds1 : do_lds0, rc, rc + C::BM);
+        if (s + 1 < nsteps) stage_rows(rn);
+        wait_tile_loads();
+        __syncthreads();
+      }
+    } else
+    // two steps per trip so each LDS buffer is a distinct, compile-time object
+    for (int s = 0; s < nsteps; s += 2) {
+      if (s + 1 < nsteps) stage_issue(s + 1, q_lds1, do_lds1);
+      step(s, q_lds0, do_lds0, rows_lds0, rows_lds0 + C::BM);
+      if (s + 1 < nsteps) stage_rows(rows_lds1);
+      wait_tile_loads();
+      __syncthreads();
+      if (s + 1 >= nsteps) break;
+      if (s + 2 < nsteps) stage_issue(s + 2, q_lds0, do_lds0);
+      step(s + 1, q_lds1, do_lds1, rows_lds1, rows_lds1 + C::BM);
+      if (s + 2 < nsteps) stage_rows(rows_lds0);
       wait_tile_loads();
       __syncthreads();
     }

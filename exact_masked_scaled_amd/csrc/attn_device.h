@@ -157,6 +157,59 @@ __device__ __forceinline__ typename Op<T>::type ld_tr(const T* X, int kb, int nb
   }
 }
 
+// ---------------------------------------------------------------- precomputed LDS offsets
+// The swizzle of a tile depends on the row only through row % 16, and every
+// read pattern below starts at a multiple of 16 rows, so a lane's byte
+// offsets are fixed for the whole kernel; the row block enters as a
+// compile-time or uniform displacement.  (float32 tiles use the generic path.)
+//
+// Row order, A/B operand rows = lane % 32 (+ rb), k chunk 16*ks + 8*(lane/32).
+template <typename T, int D>
+struct RowOffsets {
+  int off[D / 16];
+  __device__ __forceinline__ void init(int lane) {
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+      off[ks] = Tile<T, D>::off(lane & 31, 16 * ks + 8 * (lane >> 5)) * (int)sizeof(T);
+  }
+  // rows rb .. rb+31 (rb a multiple of 32)
+  __device__ __forceinline__ typename Op<T>::type read(const T* tile, int rb, int ks) const {
+    if constexpr (sizeof(T) == 2) {
+      return *reinterpret_cast<const typename Op<T>::type*>(reinterpret_cast<const char*>(tile) +
+                                                              rb * D * (int)sizeof(T) + off[ks]);
+    } else {
+      return ld8_tile<T, D>(tile, rb + (lane_id() & 31), 16 * ks + 8 * (lane_id() >> 5));
+    }
+  }
+};
+// Transposed reads (ld_tr) with kb a multiple of 16 and nb = 32 * nt.
+template <typename T, int D>
+struct TrOffsets {
+  int off[2][D / 32];
+  __device__ __forceinline__ void init(int lane) {
+    const int s = lane & 15, grp = lane >> 4;
+    const int r0 = 4 * (grp >> 1) + (s >> 2);
+    const int e0 = 16 * (grp & 1) + 4 * (s & 3);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int nt = 0; nt < D / 32; ++nt) off[h][nt] = Tile<T, D>::off(r0 + 8 * h, 32 * nt + e0) * (int)sizeof(T);
+  }
+  __device__ __forceinline__ typename Op<T>::type read(const T* tile, int kb, int nt) const {
+    if constexpr (sizeof(T) == 2) {
+      const char* base = reinterpret_cast<const char*>(tile) + kb * D * (int)sizeof(T);
+      i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4*)(base + off[0][nt]));
+      i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4*)(base + off[1][nt]));
+      union { i16x4 v[2]; bf16x8 b; } u;
+      u.v[0] = lo;
+      u.v[1] = hi;
+      return u.b;
+    } else {
+      return ld_tr<T, D>(tile, kb, 32 * nt);
+    }
+  }
+};
+
 // ---------------------------------------------------------------- cross-lane
 // Value of lane l ^ 32 (v_permlane32_swap: swaps the upper half of the first
 // operand with the lower half of the second).

@@ -9,11 +9,14 @@
 // row statistics need one cross-lane exchange (with lane ^ 32).  The
 // probabilities then feed O^T += V^T P^T directly as the B operand (their
 // C-layout order is the operand's k order); V^T comes from LDS through the
-// transpose read.  The softmax is the max-subtracted one of eq. A.10.2,
-// evaluated online: a running max m and sum l per row, rescaling the
-// accumulator when m grows.  Whole key tiles beyond a row block's visible
-// range are skipped; tiles that straddle the causal diagonal or the key
-// length get an element mask.
+// transpose read.  The softmax is the shifted one of eq. A.10.2, evaluated
+// online: per row a shift m and a running sum l of exp(S - m); the shift
+// follows the running maximum (lazily, see below) and the accumulator is
+// rescaled whenever it moves.  Because O and l always share one shift, the
+// quotient O / l is exactly the softmax-weighted sum in real arithmetic
+// (the shift only keeps the exponentials in range).  Whole key tiles beyond a
+// row block's visible range are skipped; tiles that straddle the causal
+// diagonal or the key length get an element mask.
 #include "attn_device.h"
 #include "attn_internal.h"
 
@@ -37,8 +40,12 @@ template <typename T, int DH, int DV>
 __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(const KernelParams p) {
   using C = FwdCfg<T, DH, DV>;
   using op_t = typename Op<T>::type;
-  __shared__ __attribute__((aligned(16))) T k_lds[2][C::BN * C::KS];
-  __shared__ __attribute__((aligned(16))) T v_lds[2][C::BN * C::VS];
+  // separate arrays per buffer: the compiler can then see that the copy into
+  // one buffer never aliases reads of the other and keeps the copy in flight
+  __shared__ __attribute__((aligned(16))) T k_lds0[C::BN * C::KS];
+  __shared__ __attribute__((aligned(16))) T k_lds1[C::BN * C::KS];
+  __shared__ __attribute__((aligned(16))) T v_lds0[C::BN * C::VS];
+  __shared__ __attribute__((aligned(16))) T v_lds1[C::BN * C::VS];
 
   const int nqblk = (p.n_q + C::BM - 1) / C::BM;
   int unit, item;
@@ -94,69 +101,70 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(const 
     for (int ks = 0; ks < DH / 16; ++ks)
       qreg[ks] = row_exists ? ld8<T>(Qb + (int64_t)qi * p.q_sr + 16 * ks + 8 * kg) : zero_op<T>();
 
+    RowOffsets<T, DH> kro;
+    TrOffsets<T, DV> vto;
+    kro.init(lane);
+    vto.init(lane);
+    const float tau_raw = 8.f / p.scale_log2;
     // K/V tiles stream through two LDS buffers with direct global-to-LDS loads
     using KL = TileLoad<T, C::BN, DH, 64 * C::NW>;
     using VL = TileLoad<T, C::BN, DV, 64 * C::NW>;
-    KL::issue(Kb, p.k_sr, 0, p.n_k, k_lds[0], tid);
-    VL::issue(Vb, p.v_sr, 0, p.n_k, v_lds[0], tid);
+    KL::issue(Kb, p.k_sr, 0, p.n_k, k_lds0, tid);
+    VL::issue(Vb, p.v_sr, 0, p.n_k, v_lds0, tid);
     wait_tile_loads();
     __syncthreads();
 
-    for (int t = 0; t < ntiles; ++t) {
-      const int buf = t & 1;
-      if (t + 1 < ntiles) {
-        KL::issue(Kb, p.k_sr, (t + 1) * C::BN, p.n_k, k_lds[buf ^ 1], tid);
-        VL::issue(Vb, p.v_sr, (t + 1) * C::BN, p.n_k, v_lds[buf ^ 1], tid);
-      }
-      if (t < wtiles) {
-        const T* Ks = k_lds[buf];
-        const T* Vs = v_lds[buf];
-        // S^T tile: keys (rows) x this wave's 32 queries (columns)
+    auto tile = [&](const int t, const T* Ks, const T* Vs) {
+        // S^T tile: keys (rows) x this wave's 32 queries (columns), raw scores
         f32x16 s[C::BN / 32];
 #pragma unroll
         for (int mt = 0; mt < C::BN / 32; ++mt) {
 #pragma unroll
           for (int e = 0; e < 16; ++e) s[mt][e] = 0.f;
 #pragma unroll
-          for (int ks = 0; ks < DH / 16; ++ks) {
-            op_t a = ld8_tile<T, DH>(Ks, 32 * mt + (lane & 31), 16 * ks + 8 * kg);
-            mma(s[mt], a, qreg[ks]);
-          }
+          for (int ks = 0; ks < DH / 16; ++ks) mma(s[mt], kro.read(Ks, 32 * mt, ks), qreg[ks]);
         }
-        // scale into the log2 domain, mask, row max
-        const bool masked = t >= nfull;
+        if (t >= nfull) {  // tile straddles the causal diagonal or the key length
+#pragma unroll
+          for (int mt = 0; mt < C::BN / 32; ++mt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int key = t * C::BN + 32 * mt + 8 * (e >> 2) + 4 * kg + (e & 3);
+              s[mt][e] = key < kmax_lane ? s[mt][e] : -INFINITY;
+            }
+        }
         float mx = -INFINITY;
 #pragma unroll
         for (int mt = 0; mt < C::BN / 32; ++mt)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            float v = s[mt][e] * p.scale_log2;
-            if (masked) {
-              const int key = t * C::BN + 32 * mt + 8 * (e >> 2) + 4 * kg + (e & 3);
-              v = key < kmax_lane ? v : -INFINITY;
-            }
-            s[mt][e] = v;
-            mx = fmaxf(mx, v);
-          }
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[mt][e]);
         mx = fmaxf(mx, partner32(mx));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        m_run = m_new;
+        // The shift m (raw-score units) follows the running max lazily: it only
+        // moves when the max exceeds it by more than 8 in log2 units, so the
+        // probabilities stay below 2^8 and the accumulator is rescaled rarely.
+        // O and l always share the same shift, so the quotient is unchanged.
+        const bool grow = mx > m_run + tau_raw;
+        if (__any(grow)) {
+          const float m_new = grow ? mx : m_run;
+          const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * p.scale_log2);
+          m_run = m_new;
+          l_run *= alpha;
+#pragma unroll
+          for (int i = 0; i < DV / 32; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) oacc[i][e] *= alpha;
+        }
+        const float mc = m_run == -INFINITY ? 0.f : m_run * p.scale_log2;
         float psum = 0.f;
 #pragma unroll
         for (int mt = 0; mt < C::BN / 32; ++mt)
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            const float pe = __builtin_amdgcn_exp2f(s[mt][e] - m_use);
+            const float pe = __builtin_amdgcn_exp2f(fmaf(s[mt][e], p.scale_log2, -mc));
             s[mt][e] = pe;
             psum += pe;
           }
-        l_run = l_run * alpha + psum;
-#pragma unroll
-        for (int i = 0; i < DV / 32; ++i)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) oacc[i][e] *= alpha;
+        l_run += psum;
         // O^T += V^T P^T, contracting over the tile's keys in C order
 #pragma unroll
         for (int mt = 0; mt < C::BN / 32; ++mt)
@@ -167,12 +175,25 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(const 
             for (int e = 0; e < 8; ++e) pv[e] = s[mt][8 * st + e];
             const op_t bop = to_op<T>(pv);
 #pragma unroll
-            for (int dt = 0; dt < DV / 32; ++dt) {
-              const op_t aop = ld_tr<T, DV>(Vs, 32 * mt + 16 * st, 32 * dt);
-              mma(oacc[dt], aop, bop);
-            }
+            for (int dt = 0; dt < DV / 32; ++dt) mma(oacc[dt], vto.read(Vs, 32 * mt + 16 * st, dt), bop);
           }
+    };
+
+    // two tiles per trip so each LDS buffer address is a compile-time constant
+    for (int t = 0; t < ntiles; t += 2) {
+      if (t + 1 < ntiles) {
+        KL::issue(Kb, p.k_sr, (t + 1) * C::BN, p.n_k, k_lds1, tid);
+        VL::issue(Vb, p.v_sr, (t + 1) * C::BN, p.n_k, v_lds1, tid);
       }
+      if (t < wtiles) tile(t, k_lds0, v_lds0);
+      wait_tile_loads();
+      __syncthreads();
+      if (t + 1 >= ntiles) break;
+      if (t + 2 < ntiles) {
+        KL::issue(Kb, p.k_sr, (t + 2) * C::BN, p.n_k, k_lds0, tid);
+        VL::issue(Vb, p.v_sr, (t + 2) * C::BN, p.n_k, v_lds0, tid);
+      }
+      if (t + 1 < wtiles) tile(t + 1, k_lds1, v_lds1);
       wait_tile_loads();
       __syncthreads();
     }
@@ -191,7 +212,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(const 
                oacc[dt][4 * j + 2] * inv, oacc[dt][4 * j + 3] * inv);
       }
     if (kg == 0)
-      lse_b[qi] = row_active ? (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994530942f : 0.f;
+      lse_b[qi] = row_active ? (m_run * p.scale_log2 + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994530942f
+                             : 0.f;
   }
 }
 
