@@ -221,6 +221,7 @@ struct DkvCfg {
   static constexpr int KT = 1;                        // 32-key tiles per wave
   static constexpr int BN = 32 * KT * NW;             // keys per workgroup
   static constexpr int BM = 32;                       // query rows per step
+  static constexpr int NS = 4;                        // pipeline stages (steps in flight)
   static constexpr int QS = Tile<T, DH>::STRIDE;
   static constexpr int OS = Tile<T, DV>::STRIDE;
 };
@@ -230,13 +231,26 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const KernelParams p) 
   using C = DkvCfg<T, DH, DV>;
   using op_t = typename Op<T>::type;
   constexpr int KT = C::KT;
-  // one array per buffer (see bwd_dq_kernel)
-  __shared__ __attribute__((aligned(16))) T q_lds0[C::BM * C::QS];
-  __shared__ __attribute__((aligned(16))) T q_lds1[C::BM * C::QS];
-  __shared__ __attribute__((aligned(16))) T do_lds0[C::BM * C::OS];
-  __shared__ __attribute__((aligned(16))) T do_lds1[C::BM * C::OS];
-  __shared__ __attribute__((aligned(16))) float rows_lds0[2 * C::BM];  // lse (log2 units), then D
-  __shared__ __attribute__((aligned(16))) float rows_lds1[2 * C::BM];
+  // A ring of NS stages for the Q / G_O tiles of consecutive steps (one array
+  // per stage, see bwd_dq_kernel), and per stage and wave its own copy of the
+  // 32 rows' lse (natural log) followed by their D.
+  constexpr int NS = C::NS;
+  __shared__ __attribute__((aligned(16))) T q_st0[C::BM * C::QS];
+  __shared__ __attribute__((aligned(16))) T q_st1[C::BM * C::QS];
+  __shared__ __attribute__((aligned(16))) T q_st2[C::BM * C::QS];
+  __shared__ __attribute__((aligned(16))) T q_st3[C::BM * C::QS];
+  __shared__ __attribute__((aligned(16))) T o_st0[C::BM * C::OS];
+  __shared__ __attribute__((aligned(16))) T o_st1[C::BM * C::OS];
+  __shared__ __attribute__((aligned(16))) T o_st2[C::BM * C::OS];
+  __shared__ __attribute__((aligned(16))) T o_st3[C::BM * C::OS];
+  __shared__ __attribute__((aligned(16))) float r_st0[C::NW * 2 * C::BM];
+  __shared__ __attribute__((aligned(16))) float r_st1[C::NW * 2 * C::BM];
+  __shared__ __attribute__((aligned(16))) float r_st2[C::NW * 2 * C::BM];
+  __shared__ __attribute__((aligned(16))) float r_st3[C::NW * 2 * C::BM];
+  // stage -> arrays (folds to one array when the stage is a constant)
+  auto q_st = [&](int st) -> T* { return st == 0 ? q_st0 : st == 1 ? q_st1 : st == 2 ? q_st2 : q_st3; };
+  auto o_st = [&](int st) -> T* { return st == 0 ? o_st0 : st == 1 ? o_st1 : st == 2 ? o_st2 : o_st3; };
+  auto r_st = [&](int st) -> float* { return st == 0 ? r_st0 : st == 1 ? r_st1 : st == 2 ? r_st2 : r_st3; };
 
   int unit, kb;
   if (!map_work(blockIdx.x, p.groups, p.per_group, p.xcd_map, unit, kb)) return;
@@ -291,33 +305,27 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const KernelParams p) 
 
     using QL = TileLoad<T, C::BM, DH, 64 * C::NW>;
     using OL = TileLoad<T, C::BM, DV, 64 * C::NW>;
-    float lse_st = 0.f, dlt_st = 0.f;
-    // Q and G_O rows of step s go straight to LDS; their lse (in log2 units)
-    // and D go through registers and are written to LDS by stage_rows
-    auto stage_issue = [&](int s, T* q_dst, T* o_dst) {
+    // vector-memory instructions one wave issues per step (all waves alike)
+    constexpr int CPS = QL::N + OL::N + 1;
+    // Copies of step s: Q and G_O rows into stage `st`; every wave also copies
+    // the 32 rows' lse and D (lanes 0-31 and 32-63) into its own slot, so all
+    // waves issue the same number of copies and each reads only its own slot.
+    // (everything the copies need is read from the kernel arguments once,
+    // here, so no argument load sits behind the copies in the memory queue)
+    const T* const q_base = (const T*)p.q + b * p.q_sb;
+    const T* const o_base = (const T*)p.dout + b * p.o_sb;
+    const float* const rows_base = (lane < 32 ? p.lse : p.delta) + (int64_t)b * p.H_q * p.n_q;
+    const int64_t q_sh = p.q_sh, o_sh = p.o_sh, q_sr = p.q_sr, o_sr = p.o_sr;
+    const int n_q = p.n_q, group = p.group;
+    auto issue = [&](int s, int st) {
       const int rr = s / nq, qb = qb_first + s % nq;
-      const int r = g * p.group + rr;
+      const int r = g * group + rr;
       const int q0 = qb * C::BM;
-      QL::issue((const T*)p.q + b * p.q_sb + r * p.q_sh, p.q_sr, q0, p.n_q, q_dst, tid);
-      OL::issue((const T*)p.dout + b * p.o_sb + r * p.o_sh, p.o_sr, q0, p.n_q, o_dst, tid);
-      if (tid < C::BM) {
-        const int q = q0 + tid;
-        const int64_t rb = ((int64_t)b * p.H_q + r) * p.n_q;
-        lse_st = q < p.n_q ? p.lse[rb + q] * 1.4426950408889634f : 0.f;
-        dlt_st = q < p.n_q ? p.delta[rb + q] : 0.f;
-      }
+      QL::issue(q_base + r * q_sh, q_sr, q0, n_q, q_st(st), tid);
+      OL::issue(o_base + r * o_sh, o_sr, q0, n_q, o_st(st), tid);
+      const int qq = min(q0 + (lane & 31), n_q - 1);
+      load_lane_floats(rows_base + (int64_t)r * n_q + qq, r_st(st) + w * 2 * C::BM);
     };
-    auto stage_rows = [&](float* rows) {
-      if (tid < C::BM) {
-        rows[tid] = lse_st;
-        rows[C::BM + tid] = dlt_st;
-      }
-    };
-
-    stage_issue(0, q_lds0, do_lds0);
-    stage_rows(rows_lds0);
-    wait_tile_loads();
-    __syncthreads();
 
     // per-lane LDS offsets (Q and G_O tiles share them when d_h == d_v)
     RowOffsets<T, DH> qro;
@@ -360,14 +368,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const KernelParams p) 
 #pragma unroll
         for (int nt = 0; nt < DH / 32; ++nt) qb[st][nt] = qto.read(Qs, 16 * st, nt);
       };
-      if constexpr (PRELOAD) {
-        read_b(0);
-        read_b(1);
-      }
+      if constexpr (PRELOAD) read_b(0);
       f32x4 l4[4], d4[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        l4[j] = *reinterpret_cast<const f32x4*>(&lse_s[8 * j + 4 * kg]);
+        l4[j] = *reinterpret_cast<const f32x4*>(&lse_s[8 * j + 4 * kg]) * 1.4426950408889634f;
         d4[j] = *reinterpret_cast<const f32x4*>(&dlt_s[8 * j + 4 * kg]);
       }
 
@@ -417,7 +422,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const KernelParams p) 
       // G_V += P^T G_O, G_K += G_S^T Q (A = this lane's key row, C order over queries)
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        if constexpr (!PRELOAD) read_b(st);
+        if (!PRELOAD || st == 1) read_b(st);
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) {
           float tmp[8];
@@ -435,33 +440,41 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const KernelParams p) 
       }
     };
 
-    if constexpr (sizeof(T) == 4) {  // float32: one step per trip (register budget)
+    // Step s waits for its own copies only (those of the next NS - 2 steps
+    // stay in flight), passes a workgroup barrier, issues the copies of step
+    // s + NS - 1 into the stage step s - 1 used (every wave is past it), and
+    // computes.
+    static_assert(NS == 4, "wait_for assumes at most two later steps in flight");
+    auto wait_for = [&](int s) {
+      const int ahead = min(nsteps - 1, s + NS - 2) - s;  // later steps already issued
+      if (ahead >= 2) stage_barrier<2 * CPS>();
+      else if (ahead == 1) stage_barrier<CPS>();
+      else stage_barrier<0>();
+    };
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s)
+      if (s < nsteps) issue(s, s);
+    if constexpr (sizeof(T) == 4) {  // float32: stage chosen at run time (register budget)
       for (int s = 0; s < nsteps; ++s) {
-        const bool odd = s & 1;
-        T* qn = odd ? q_lds0 : q_lds1;
-        T* on = odd ? do_lds0 : do_lds1;
-        float* rn = odd ? rows_lds0 : rows_lds1;
-        float* rc = odd ? rows_lds1 : rows_lds0;
-        if (s + 1 < nsteps) stage_issue(s + 1, qn, on);
-        step(s, odd ? q_lds1 : q_lds0, odd ? do_lds1 : do_lds0, rc, rc + C::BM);
-        if (s + 1 < nsteps) stage_rows(rn);
-        wait_tile_loads();
-        __syncthreads();
+        const int st = s % NS;
+        wait_for(s);
+        if (s + NS - 1 < nsteps) issue(s + NS - 1, (s + NS - 1) % NS);
+        const float* rw = r_st(st) + w * 2 * C::BM;
+        step(s, q_st(st), o_st(st), rw, rw + C::BM);
       }
-    } else
-    // two steps per trip so each LDS buffer is a distinct, compile-time object
-    for (int s = 0; s < nsteps; s += 2) {
-      if (s + 1 < nsteps) stage_issue(s + 1, q_lds1, do_lds1);
-      step(s, q_lds0, do_lds0, rows_lds0, rows_lds0 + C::BM);
-      if (s + 1 < nsteps) stage_rows(rows_lds1);
-      wait_tile_loads();
-      __syncthreads();
-      if (s + 1 >= nsteps) break;
-      if (s + 2 < nsteps) stage_issue(s + 2, q_lds0, do_lds0);
-      step(s + 1, q_lds1, do_lds1, rows_lds1, rows_lds1 + C::BM);
-      if (s + 2 < nsteps) stage_rows(rows_lds0);
-      wait_tile_loads();
-      __syncthreads();
+    } else {
+      // NS steps per trip so every stage is a distinct, compile-time LDS object
+      for (int s0 = 0; s0 < nsteps; s0 += NS) {
+#pragma unroll
+        for (int u = 0; u < NS; ++u) {
+          const int s = s0 + u;
+          if (s >= nsteps) break;
+          wait_for(s);
+          if (s + NS - 1 < nsteps) issue(s + NS - 1, (u + NS - 1) % NS);
+          const float* rw = r_st(u) + w * 2 * C::BM;
+          step(s, q_st(u), o_st(u), rw, rw + C::BM);
+        }
+      }
     }
   }
 

@@ -269,6 +269,26 @@ struct TileLoad {
 // Wait until every global-to-LDS copy issued by this wave has landed.
 __device__ __forceinline__ void wait_tile_loads() { __builtin_amdgcn_s_waitcnt(0); }
 
+// Workgroup barrier for multi-stage pipelines: waits until at most N of this
+// wave's vector-memory operations (issued in order) are still outstanding and
+// all of its LDS accesses are complete, then synchronises the workgroup.
+// Unlike __syncthreads(), whose fence drains every pending global-to-LDS copy,
+// this lets the copies of later stages stay in flight.  The memory clobbers
+// keep the compiler from moving memory accesses across it.
+template <int N>
+__device__ __forceinline__ void stage_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N < 10) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+  else asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// 64 lanes copy one float each into 256 consecutive LDS bytes (lane i ->
+// float i), e.g. two rows of 32 per-query scalars.
+__device__ __forceinline__ void load_lane_floats(const float* src, float* lds) {
+  __builtin_amdgcn_global_load_lds((const void*)src, (ATTN_LDS void*)lds, 4, 0, 0);
+}
+
 // ---------------------------------------------------------------- work mapping
 // Work is grouped in units (a sequence and a KV head) of `per_group` items.
 // With xcd_map, unit u runs on XCD u % 8: workgroups are dealt to the 8 XCDs
