@@ -499,6 +499,269 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const KernelParams p) 
   }
 }
 
+// ============================================================== dK/dV pass, wave pairs (bf16)
+// Same work unit as bwd_dkdv_kernel (128 keys of one sequence and KV head,
+// every query head of the group, 32-row query steps), with the work of one
+// 32-key tile split over a PAIR of waves so that each holds half the state
+// and two waves share every SIMD:
+//   wave A (waves 0-3): S = Q K^T, P = exp(S - lse) on the visible set,
+//                       G_V += P^T G_O; hands P to its partner through LDS;
+//   wave B (waves 4-7): one step behind, dP = G_O V^T, G_S = P o (dP - D),
+//                       G_K += G_S^T Q.
+// Q / G_O tiles (and per wave the step's lse and D) arrive through a 4-stage
+// ring of direct global-to-LDS copies issued two steps ahead; one workgroup
+// barrier per step.
+template <typename T, int DH, int DV>
+struct DkvPairCfg {
+  static constexpr int NW = 8;            // waves: 4 pairs
+  static constexpr int PAIRS = 4;
+  static constexpr int BN = 32 * PAIRS;   // keys per workgroup
+  static constexpr int BM = 32;           // query rows per step
+  static constexpr int NS = 4;            // ring stages
+  static constexpr int QCH = BM * Tile<T, DH>::CH;   // 16-byte chunks of a Q tile
+  static constexpr int OCH = BM * Tile<T, DV>::CH;   // ... of a G_O tile
+  static constexpr int JOBS = (QCH + OCH) / 64;      // wave-instructions of copies per step
+  static constexpr int JPW = (JOBS + NW - 1) / NW;   // per wave (padded with dummy copies)
+  static constexpr int CPS = JPW + 1;                // + the lse/D copy
+  static_assert(QCH % 64 == 0 && OCH % 64 == 0, "tiles must be whole wave copies");
+};
+
+template <typename T, int DH, int DV>
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(const KernelParams p) {
+  using C = DkvPairCfg<T, DH, DV>;
+  using op_t = typename Op<T>::type;
+  constexpr int NS = C::NS;
+  __shared__ __attribute__((aligned(16))) T q_st0[C::BM * DH];
+  __shared__ __attribute__((aligned(16))) T q_st1[C::BM * DH];
+  __shared__ __attribute__((aligned(16))) T q_st2[C::BM * DH];
+  __shared__ __attribute__((aligned(16))) T q_st3[C::BM * DH];
+  __shared__ __attribute__((aligned(16))) T o_st0[C::BM * DV];
+  __shared__ __attribute__((aligned(16))) T o_st1[C::BM * DV];
+  __shared__ __attribute__((aligned(16))) T o_st2[C::BM * DV];
+  __shared__ __attribute__((aligned(16))) T o_st3[C::BM * DV];
+  __shared__ __attribute__((aligned(16))) float r_st0[C::NW * 2 * C::BM];
+  __shared__ __attribute__((aligned(16))) float r_st1[C::NW * 2 * C::BM];
+  __shared__ __attribute__((aligned(16))) float r_st2[C::NW * 2 * C::BM];
+  __shared__ __attribute__((aligned(16))) float r_st3[C::NW * 2 * C::BM];
+  // P handed from wave A to wave B: per pair 4 x f32x4 per lane, element-major
+  __shared__ __attribute__((aligned(16))) float p_x0[C::PAIRS * 4 * 64 * 4];
+  __shared__ __attribute__((aligned(16))) float p_x1[C::PAIRS * 4 * 64 * 4];
+  __shared__ __attribute__((aligned(16))) T junk[64 * Tile<T, DH>::EPC];  // target of padding copies
+  auto q_st = [&](int st) -> T* { return st == 0 ? q_st0 : st == 1 ? q_st1 : st == 2 ? q_st2 : q_st3; };
+  auto o_st = [&](int st) -> T* { return st == 0 ? o_st0 : st == 1 ? o_st1 : st == 2 ? o_st2 : o_st3; };
+  auto r_st = [&](int st) -> float* { return st == 0 ? r_st0 : st == 1 ? r_st1 : st == 2 ? r_st2 : r_st3; };
+
+  int unit, kb;
+  if (!map_work(blockIdx.x, p.groups, p.per_group, p.xcd_map, unit, kb)) return;
+  const int b = unit / p.H_kv, g = unit - (unit / p.H_kv) * p.H_kv;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, kg = lane >> 5;
+  const int pair = w & 3;
+  const bool side_a = w < C::PAIRS;
+  const int Lq = p.has_lens ? p.lens_q[b] : p.n_q;
+  const int Lk = p.has_lens ? p.lens_k[b] : p.n_k;
+  const int k_lo = kb * C::BN;
+  const int kw0 = k_lo + 32 * pair;               // first key of the pair
+  const int key = kw0 + (lane & 31);              // this lane's key
+  const int wk_hi = kw0 + 32;
+
+  const T* Kb = (const T*)p.k + b * p.k_sb + g * p.k_sh;
+  const T* Vb = (const T*)p.v + b * p.v_sb + g * p.v_sh;
+  T* dKb = (T*)p.dk + b * p.k_sb + g * p.k_sh;
+  T* dVb = (T*)p.dv + b * p.v_sb + g * p.v_sh;
+
+  // side A accumulates G_V (d_v columns), side B G_K (d_h columns)
+  constexpr int NACC = (DH > DV ? DH : DV) / 32;
+  f32x16 acc[NACC];
+#pragma unroll
+  for (int i = 0; i < NACC; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
+
+  const int q_first = p.causal ? max(0, k_lo - p.offset) : 0;
+  const int qb_first = q_first / C::BM;
+  const int qb_end = (Lq + C::BM - 1) / C::BM;
+  const int nq = k_lo < Lk && qb_first < qb_end ? qb_end - qb_first : 0;
+  const int nsteps = nq * p.group;
+
+  if (nsteps > 0) {
+    // this lane's key row: K for side A (S = Q K^T), V for side B (dP = G_O V^T)
+    constexpr int NOP = (DH > DV ? DH : DV) / 16;
+    op_t kv[NOP];
+    {
+      const bool ok = key < p.n_k;
+      const T* src = side_a ? Kb + (int64_t)key * p.k_sr : Vb + (int64_t)key * p.v_sr;
+      const int nks = side_a ? DH / 16 : DV / 16;
+#pragma unroll
+      for (int ks = 0; ks < NOP; ++ks)
+        kv[ks] = (ok && ks < nks) ? ld8<T>(src + 16 * ks + 8 * kg) : zero_op<T>();
+    }
+
+    // copies: arguments read once (no argument load behind the copies)
+    const T* const q_base = (const T*)p.q + b * p.q_sb;
+    const T* const o_base = (const T*)p.dout + b * p.o_sb;
+    const float* const rows_base = (lane < 32 ? p.lse : p.delta) + (int64_t)b * p.H_q * p.n_q;
+    const int64_t q_sh = p.q_sh, o_sh = p.o_sh, q_sr = p.q_sr, o_sr = p.o_sr;
+    const int n_q = p.n_q, group = p.group;
+    auto issue = [&](int s, int st) {
+      const int rr = s / nq, qb = qb_first + s % nq;
+      const int r = g * group + rr;
+      const int q0 = qb * C::BM;
+      const T* qsrc = q_base + r * q_sh;
+      const T* osrc = o_base + r * o_sh;
+#pragma unroll
+      for (int i = 0; i < C::JPW; ++i) {
+        const int job = w + C::NW * i;
+        int pc, row, chunk;
+        const T* src;
+        T* dst;
+        if (job < C::QCH / 64) {
+          using L = Tile<T, DH>;
+          pc = job * 64 + lane;
+          row = pc / L::CH;
+          chunk = (pc % L::CH) ^ L::f(row);
+          src = qsrc + (int64_t)min(q0 + row, n_q - 1) * q_sr + chunk * L::EPC;
+          dst = q_st(st) + job * 64 * L::EPC;
+        } else if (job < C::JOBS) {
+          using L = Tile<T, DV>;
+          pc = (job - C::QCH / 64) * 64 + lane;
+          row = pc / L::CH;
+          chunk = (pc % L::CH) ^ L::f(row);
+          src = osrc + (int64_t)min(q0 + row, n_q - 1) * o_sr + chunk * L::EPC;
+          dst = o_st(st) + (job - C::QCH / 64) * 64 * L::EPC;
+        } else {  // padding copy keeps every wave's count equal
+          src = qsrc + (int64_t)min(q0, n_q - 1) * q_sr;
+          dst = junk;
+        }
+        __builtin_amdgcn_global_load_lds((const void*)src, (ATTN_LDS void*)dst, 16, 0, 0);
+      }
+      const int qq = min(q0 + (lane & 31), n_q - 1);
+      load_lane_floats(rows_base + (int64_t)r * n_q + qq, r_st(st) + w * 2 * C::BM);
+    };
+
+    RowOffsets<T, DH> qro;
+    RowOffsets<T, DV> oro;
+    TrOffsets<T, DH> qto;
+    TrOffsets<T, DV> oto;
+    if (side_a) { qro.init(lane); oto.init(lane); } else { oro.init(lane); qto.init(lane); }
+
+    const int off_eff = p.causal ? p.offset : p.n_k;  // j <= i + n_k always holds
+    // ---- side A, step s: S, P (to LDS), G_V += P^T G_O
+    auto side_a_step = [&](int s, const T* Qs, const T* Os, const float* rows, float* px) {
+      const int q0 = (qb_first + s % nq) * C::BM;
+      f32x16 sv;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sv[e] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < DH / 16; ++ks) mma(sv, qro.read(Qs, 0, ks), kv[ks]);
+      f32x4 l4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        l4[j] = *reinterpret_cast<const f32x4*>(&rows[8 * j + 4 * kg]) * 1.4426950408889634f;
+      const bool full = (q0 + C::BM <= Lq) && (wk_hi <= Lk) && (!p.causal || wk_hi - 1 <= q0 + p.offset);
+      if (full) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sv[e] = __builtin_amdgcn_exp2f(fmaf(sv[e], p.scale_log2, -l4[e >> 2][e & 3]));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int q = q0 + 8 * (e >> 2) + 4 * kg + (e & 3);
+          const bool vis = (key < Lk) & (q < Lq) & (key <= q + off_eff);
+          const float pv = __builtin_amdgcn_exp2f(fmaf(sv[e], p.scale_log2, -l4[e >> 2][e & 3]));
+          sv[e] = vis ? pv : 0.f;
+        }
+      }
+      // hand P to side B (element-major: float4 j of lane l at (j * 64 + l) * 4)
+      float* pp = px + pair * 4 * 64 * 4;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f32x4 v;
+        v[0] = sv[4 * j]; v[1] = sv[4 * j + 1]; v[2] = sv[4 * j + 2]; v[3] = sv[4 * j + 3];
+        *reinterpret_cast<f32x4*>(pp + (j * 64 + lane) * 4) = v;
+      }
+      // G_V += P^T G_O
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        float tmp[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tmp[e] = sv[8 * st + e];
+        const op_t pa = to_op<T>(tmp);
+#pragma unroll
+        for (int nt = 0; nt < DV / 32; ++nt) mma(acc[nt], pa, oto.read(Os, 16 * st, nt));
+      }
+    };
+    // ---- side B, step s: dP, G_S = P o (dP - D), G_K += G_S^T Q
+    auto side_b_step = [&](const T* Qs, const T* Os, const float* rows, const float* px) {
+      f32x16 dp;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) dp[e] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < DV / 16; ++ks) mma(dp, oro.read(Os, 0, ks), kv[ks]);
+      const float* pp = px + pair * 4 * 64 * 4;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 pv = *reinterpret_cast<const f32x4*>(pp + (j * 64 + lane) * 4);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&rows[C::BM + 8 * j + 4 * kg]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dp[4 * j + i] = pv[i] * (dp[4 * j + i] - d4[i]);
+      }
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        float tmp[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tmp[e] = dp[8 * st + e];
+        const op_t da = to_op<T>(tmp);
+#pragma unroll
+        for (int nt = 0; nt < DH / 32; ++nt) mma(acc[nt], da, qto.read(Qs, 16 * st, nt));
+      }
+    };
+
+    // Iteration s: side A does step s, side B step s - 1 (P of step s - 1 was
+    // written before the barrier).  Step s's copies must have landed; those
+    // of step s + 1 may stay in flight.  After the barrier the copies of step
+    // s + 2 go into the stage step s - 2 used (both sides are past it).
+    auto wait_for = [&](int s) {
+      if (s + 1 < nsteps) stage_barrier<C::CPS>();
+      else stage_barrier<0>();
+    };
+    issue(0, 0);
+    if (1 < nsteps) issue(1, 1);
+    for (int s0 = 0; s0 <= nsteps; s0 += NS) {
+#pragma unroll
+      for (int u = 0; u < NS; ++u) {
+        const int s = s0 + u;
+        if (s > nsteps) break;
+        wait_for(s);
+        if (s + 2 < nsteps) issue(s + 2, (u + 2) % NS);
+        if (side_a) {
+          if (s < nsteps) side_a_step(s, q_st(u), o_st(u), r_st(u) + w * 2 * C::BM, (u & 1) ? p_x1 : p_x0);
+        } else if (s >= 1) {
+          const int up = (u + NS - 1) % NS;
+          side_b_step(q_st(up), o_st(up), r_st(up) + w * 2 * C::BM, (u & 1) ? p_x0 : p_x1);
+        }
+      }
+    }
+  }
+
+  // store: side A holds G_V, side B G_K (scaled); lane = d, registers = keys
+  if (side_a) {
+#pragma unroll
+    for (int nt = 0; nt < DV / 32; ++nt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int kk = kw0 + 8 * (e >> 2) + 4 * kg + (e & 3);
+        if (kk < p.n_k) dVb[(int64_t)kk * p.v_sr + 32 * nt + (lane & 31)] = (T)acc[nt][e];
+      }
+  } else {
+#pragma unroll
+    for (int nt = 0; nt < DH / 32; ++nt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int kk = kw0 + 8 * (e >> 2) + 4 * kg + (e & 3);
+        if (kk < p.n_k) dKb[(int64_t)kk * p.k_sr + 32 * nt + (lane & 31)] = (T)(acc[nt][e] * p.scale);
+      }
+  }
+}
+
 // ============================================================== launchers
 template <typename T, int DH, int DV>
 static int launch_dq_t(const KernelParams& p, void* stream) {
@@ -514,7 +777,12 @@ static int launch_dkdv_t(const KernelParams& p, void* stream) {
   const int64_t units = p.xcd_map ? ((p.groups + 7) / 8) * 8 : p.groups;
   const int64_t grid = units * p.per_group;
   if (grid <= 0) return (int)hipSuccess;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<T, DH, DV>), dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, p);
+  if constexpr (sizeof(T) == 2) {
+    hipLaunchKernelGGL((bwd_dkdv_pair_kernel<T, DH, DV>), dim3((unsigned)grid), dim3(512), 0, (hipStream_t)stream,
+                       p);
+  } else {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, DH, DV>), dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, p);
+  }
   return (int)hipGetLastError();
 }
 
