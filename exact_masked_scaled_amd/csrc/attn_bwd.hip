@@ -501,62 +501,82 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const KernelParams p) 
 
 // ============================================================== dK/dV pass, wave pairs (bf16)
 // Same work unit as bwd_dkdv_kernel (128 keys of one sequence and KV head,
-// every query head of the group, 32-row query steps), with the work of one
-// 32-key tile split over a PAIR of waves so that each holds half the state
-// and two waves share every SIMD:
-//   wave A (waves 0-3): S = Q K^T, P = exp(S - lse) on the visible set,
-//                       G_V += P^T G_O; hands P to its partner through LDS;
-//   wave B (waves 4-7): one step behind, dP = G_O V^T, G_S = P o (dP - D),
-//                       G_K += G_S^T Q.
-// Q / G_O tiles (and per wave the step's lse and D) arrive through a 4-stage
-// ring of direct global-to-LDS copies issued two steps ahead; one workgroup
-// barrier per step.
+// every query head of the group, 32-row query steps).  The work of one 32-key
+// tile is split over a PAIR of waves that share a SIMD:
+//   wave X (waves 0-3): holds the tile's K and V rows.  In iteration s it
+//       issues the products S = Q K^T and dP = G_O V^T of step s and, in the
+//       same instruction stream, the element-wise work of step s - 1:
+//       P = exp(S - lse) on the visible set and G_S = P o (dP - D), handed to
+//       its partner through LDS already in bf16 MFMA operand form.  The
+//       exponentials thus run while the matrix cores work on the next step.
+//   wave Y (waves 4-7): two steps behind, accumulates G_V += P^T G_O and
+//       G_K += G_S^T Q (sixteen products on eight independent accumulators).
+// Q / G_O tiles (and per pair the step's lse and D) arrive through an NS-stage
+// ring of direct global-to-LDS copies issued NS - 3 steps ahead (the other
+// three stages hold the tiles of steps s, s - 1 and s - 2); one workgroup
+// barrier per step.  Only Y waves issue copies, right after the barrier: a
+// wave stalls while its copies queue for the address unit, and this way X
+// keeps the matrix core busy meanwhile.
 template <typename T, int DH, int DV>
 struct DkvPairCfg {
   static constexpr int NW = 8;            // waves: 4 pairs
   static constexpr int PAIRS = 4;
   static constexpr int BN = 32 * PAIRS;   // keys per workgroup
   static constexpr int BM = 32;           // query rows per step
-  static constexpr int NS = 4;            // ring stages
+  static constexpr int NS = 4;            // ring stages (even: exchange parity follows the stage)
+  static constexpr int PD = NS - 3;       // copy distance in steps
   static constexpr int QCH = BM * Tile<T, DH>::CH;   // 16-byte chunks of a Q tile
   static constexpr int OCH = BM * Tile<T, DV>::CH;   // ... of a G_O tile
   static constexpr int JOBS = (QCH + OCH) / 64;      // wave-instructions of copies per step
-  static constexpr int JPW = (JOBS + NW - 1) / NW;   // per wave (padded with dummy copies)
-  static constexpr int CPS = JPW + 1;                // + the lse/D copy
-  static_assert(QCH % 64 == 0 && OCH % 64 == 0, "tiles must be whole wave copies");
+  static constexpr int JPW = JOBS / PAIRS;           // per Y wave (Y waves issue every copy)
+  static constexpr int CPS = JPW + 1;                // + the pair's lse/D copy
+  static constexpr int NR = DH / 32 + DV / 32;       // Y's accumulator blocks
+  static constexpr int KVB = (DH + DV) / 64;         // X's blocks holding K and V
+  static constexpr int NB = NR > KVB + 4 ? NR : KVB + 4;
+  static_assert(QCH % 64 == 0 && OCH % 64 == 0 && JOBS % PAIRS == 0, "tiles must be whole wave copies");
+  static_assert(NS % 2 == 0 && NS >= 4 && NS <= 6, "ring stages");
 };
+
+template <int N> struct IC { static constexpr int value = N; };
 
 template <typename T, int DH, int DV>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(const KernelParams p) {
+  static_assert(sizeof(T) == 2, "wave-pair dK/dV pass is the bf16 path");
   using C = DkvPairCfg<T, DH, DV>;
   using op_t = typename Op<T>::type;
-  constexpr int NS = C::NS;
-  __shared__ __attribute__((aligned(16))) T q_st0[C::BM * DH];
-  __shared__ __attribute__((aligned(16))) T q_st1[C::BM * DH];
-  __shared__ __attribute__((aligned(16))) T q_st2[C::BM * DH];
-  __shared__ __attribute__((aligned(16))) T q_st3[C::BM * DH];
-  __shared__ __attribute__((aligned(16))) T o_st0[C::BM * DV];
-  __shared__ __attribute__((aligned(16))) T o_st1[C::BM * DV];
-  __shared__ __attribute__((aligned(16))) T o_st2[C::BM * DV];
-  __shared__ __attribute__((aligned(16))) T o_st3[C::BM * DV];
-  __shared__ __attribute__((aligned(16))) float r_st0[C::NW * 2 * C::BM];
-  __shared__ __attribute__((aligned(16))) float r_st1[C::NW * 2 * C::BM];
-  __shared__ __attribute__((aligned(16))) float r_st2[C::NW * 2 * C::BM];
-  __shared__ __attribute__((aligned(16))) float r_st3[C::NW * 2 * C::BM];
-  // P handed from wave A to wave B: per pair 4 x f32x4 per lane, element-major
-  __shared__ __attribute__((aligned(16))) float p_x0[C::PAIRS * 4 * 64 * 4];
-  __shared__ __attribute__((aligned(16))) float p_x1[C::PAIRS * 4 * 64 * 4];
-  __shared__ __attribute__((aligned(16))) T junk[64 * Tile<T, DH>::EPC];  // target of padding copies
-  auto q_st = [&](int st) -> T* { return st == 0 ? q_st0 : st == 1 ? q_st1 : st == 2 ? q_st2 : q_st3; };
-  auto o_st = [&](int st) -> T* { return st == 0 ? o_st0 : st == 1 ? o_st1 : st == 2 ? o_st2 : o_st3; };
-  auto r_st = [&](int st) -> float* { return st == 0 ? r_st0 : st == 1 ? r_st1 : st == 2 ? r_st2 : r_st3; };
+  constexpr int NS = C::NS, PD = C::PD, KVB = C::KVB;
+  // One __shared__ array per ring stage (its Q tile, G_O tile and lse/D rows),
+  // selected at compile time: the compiler then tells a stage being read from
+  // the one being copied into and does not wait for copies still in flight
+  // (it keeps only a few distinct copy targets apart, so a few large arrays).
+  constexpr int QB = C::BM * DH * (int)sizeof(T), OB = C::BM * DV * (int)sizeof(T);
+  constexpr int SB = QB + OB + C::PAIRS * 2 * C::BM * (int)sizeof(float);
+  __shared__ __attribute__((aligned(16))) char st0[SB];
+  __shared__ __attribute__((aligned(16))) char st1[SB];
+  __shared__ __attribute__((aligned(16))) char st2[SB];
+  __shared__ __attribute__((aligned(16))) char st3[SB];
+  __shared__ __attribute__((aligned(16))) char st4[SB];
+  __shared__ __attribute__((aligned(16))) char st5[SB];
+  // P and G_S handed from X to Y: per pair 4 operands per lane (P k-steps 0, 1,
+  // then G_S k-steps 0, 1), operand j of lane l at index j * 64 + l
+  __shared__ op_t x_x0[C::PAIRS * 4 * 64];
+  __shared__ op_t x_x1[C::PAIRS * 4 * 64];
+  auto stage = [&](auto K) -> char* {
+    constexpr int k = decltype(K)::value % NS;
+    if constexpr (k == 0) return st0; else if constexpr (k == 1) return st1;
+    else if constexpr (k == 2) return st2; else if constexpr (k == 3) return st3;
+    else if constexpr (k == 4) return st4; else return st5;
+  };
+  auto q_st = [&](auto K) -> T* { return reinterpret_cast<T*>(stage(K)); };
+  auto o_st = [&](auto K) -> T* { return reinterpret_cast<T*>(stage(K) + QB); };
+  auto r_st = [&](auto K) -> float* { return reinterpret_cast<float*>(stage(K) + QB + OB); };
 
   int unit, kb;
   if (!map_work(blockIdx.x, p.groups, p.per_group, p.xcd_map, unit, kb)) return;
   const int b = unit / p.H_kv, g = unit - (unit / p.H_kv) * p.H_kv;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, kg = lane >> 5;
   const int pair = w & 3;
-  const bool side_a = w < C::PAIRS;
+  const bool side_x = w < C::PAIRS;
   const int Lq = p.has_lens ? p.lens_q[b] : p.n_q;
   const int Lk = p.has_lens ? p.lens_k[b] : p.n_k;
   const int k_lo = kb * C::BN;
@@ -569,13 +589,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(const KernelParam
   T* dKb = (T*)p.dk + b * p.k_sb + g * p.k_sh;
   T* dVb = (T*)p.dv + b * p.v_sb + g * p.v_sh;
 
-  // side A accumulates G_V (d_v columns), side B G_K (d_h columns)
-  constexpr int NACC = (DH > DV ? DH : DV) / 32;
-  f32x16 acc[NACC];
+  // Y: R[0, DV/32) accumulate G_V, R[DV/32, NR) G_K.
+  // X: R[0, KVB) hold this lane's K row (operands 0 .. DH/16-1) and V row
+  //    (operands DH/16 ..); R[KVB + 2j], R[KVB + 2j + 1] the S and dP tiles of
+  //    the steps with parity j.
+  f32x16 R[C::NB];
 #pragma unroll
-  for (int i = 0; i < NACC; ++i)
+  for (int i = 0; i < C::NB; ++i)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
+    for (int e = 0; e < 16; ++e) R[i][e] = 0.f;
 
   const int q_first = p.causal ? max(0, k_lo - p.offset) : 0;
   const int qb_first = q_first / C::BM;
@@ -584,81 +606,111 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(const KernelParam
   const int nsteps = nq * p.group;
 
   if (nsteps > 0) {
-    // this lane's key row: K for side A (S = Q K^T), V for side B (dP = G_O V^T)
-    constexpr int NOP = (DH > DV ? DH : DV) / 16;
-    op_t kv[NOP];
-    {
+    if (side_x) {
       const bool ok = key < p.n_k;
-      const T* src = side_a ? Kb + (int64_t)key * p.k_sr : Vb + (int64_t)key * p.v_sr;
-      const int nks = side_a ? DH / 16 : DV / 16;
+      const T* ksrc = Kb + (int64_t)key * p.k_sr + 8 * kg;
+      const T* vsrc = Vb + (int64_t)key * p.v_sr + 8 * kg;
 #pragma unroll
-      for (int ks = 0; ks < NOP; ++ks)
-        kv[ks] = (ok && ks < nks) ? ld8<T>(src + 16 * ks + 8 * kg) : zero_op<T>();
+      for (int ks = 0; ks < DH / 16; ++ks)
+        set_op_part(R[ks / 4], ks % 4, ok ? ld8<T>(ksrc + 16 * ks) : zero_op<T>());
+#pragma unroll
+      for (int ks = 0; ks < DV / 16; ++ks)
+        set_op_part(R[(DH / 16 + ks) / 4], (DH / 16 + ks) % 4, ok ? ld8<T>(vsrc + 16 * ks) : zero_op<T>());
     }
 
-    // copies: arguments read once (no argument load behind the copies)
+    // Copies.  The per-lane part of every address is fixed for the whole loop
+    // (chunk position within the tile, swizzled); per step only the tile base
+    // moves, and lanes clamp their row only in the ragged last block.
     const T* const q_base = (const T*)p.q + b * p.q_sb;
     const T* const o_base = (const T*)p.dout + b * p.o_sb;
-    const float* const rows_base = (lane < 32 ? p.lse : p.delta) + (int64_t)b * p.H_q * p.n_q;
     const int64_t q_sh = p.q_sh, o_sh = p.o_sh, q_sr = p.q_sr, o_sr = p.o_sr;
     const int n_q = p.n_q, group = p.group;
-    auto issue = [&](int s, int st) {
-      const int rr = s / nq, qb = qb_first + s % nq;
+    const float* const rows_lane = (lane < 32 ? p.lse : p.delta) + (int64_t)b * p.H_q * n_q + (lane & 31);
+    int64_t c_off[C::JPW];  // (Y) element offset of this lane's chunk from the tile's first row
+    int c_row[C::JPW];      // ... and its row within the tile
+#pragma unroll
+    for (int i = 0; i < C::JPW; ++i) {
+      const int job = pair + C::PAIRS * i;
+      if (job < C::QCH / 64) {
+        using L = Tile<T, DH>;
+        const int pc = job * 64 + lane, row = pc / L::CH;
+        c_row[i] = row;
+        c_off[i] = row * q_sr + ((pc % L::CH) ^ L::f(row)) * L::EPC;
+      } else {
+        using L = Tile<T, DV>;
+        const int pc = (job - C::QCH / 64) * 64 + lane, row = pc / L::CH;
+        c_row[i] = row;
+        c_off[i] = row * o_sr + ((pc % L::CH) ^ L::f(row)) * L::EPC;
+      }
+    }
+    auto issue = [&](int rr, int qb, auto ST) {
       const int r = g * group + rr;
       const int q0 = qb * C::BM;
-      const T* qsrc = q_base + r * q_sh;
-      const T* osrc = o_base + r * o_sh;
+      const bool whole = q0 + C::BM <= n_q;
+      const T* qt = q_base + r * q_sh + (int64_t)q0 * q_sr;
+      const T* ot = o_base + r * o_sh + (int64_t)q0 * o_sr;
 #pragma unroll
       for (int i = 0; i < C::JPW; ++i) {
-        const int job = w + C::NW * i;
-        int pc, row, chunk;
+        const int job = pair + C::PAIRS * i;
         const T* src;
         T* dst;
         if (job < C::QCH / 64) {
-          using L = Tile<T, DH>;
-          pc = job * 64 + lane;
-          row = pc / L::CH;
-          chunk = (pc % L::CH) ^ L::f(row);
-          src = qsrc + (int64_t)min(q0 + row, n_q - 1) * q_sr + chunk * L::EPC;
-          dst = q_st(st) + job * 64 * L::EPC;
-        } else if (job < C::JOBS) {
-          using L = Tile<T, DV>;
-          pc = (job - C::QCH / 64) * 64 + lane;
-          row = pc / L::CH;
-          chunk = (pc % L::CH) ^ L::f(row);
-          src = osrc + (int64_t)min(q0 + row, n_q - 1) * o_sr + chunk * L::EPC;
-          dst = o_st(st) + (job - C::QCH / 64) * 64 * L::EPC;
-        } else {  // padding copy keeps every wave's count equal
-          src = qsrc + (int64_t)min(q0, n_q - 1) * q_sr;
-          dst = junk;
+          src = qt + (whole ? c_off[i] : c_off[i] + (int64_t)(min(q0 + c_row[i], n_q - 1) - q0 - c_row[i]) * q_sr);
+          dst = q_st(ST) + job * 64 * Tile<T, DH>::EPC;
+        } else {
+          src = ot + (whole ? c_off[i] : c_off[i] + (int64_t)(min(q0 + c_row[i], n_q - 1) - q0 - c_row[i]) * o_sr);
+          dst = o_st(ST) + (job - C::QCH / 64) * 64 * Tile<T, DV>::EPC;
         }
         __builtin_amdgcn_global_load_lds((const void*)src, (ATTN_LDS void*)dst, 16, 0, 0);
       }
-      const int qq = min(q0 + (lane & 31), n_q - 1);
-      load_lane_floats(rows_base + (int64_t)r * n_q + qq, r_st(st) + w * 2 * C::BM);
+      const int qq = whole ? q0 : min(q0 + (lane & 31), n_q - 1) - (lane & 31);
+      load_lane_floats(rows_lane + (int64_t)r * n_q + qq, r_st(ST) + pair * 2 * C::BM);
     };
 
-    RowOffsets<T, DH> qro;
-    RowOffsets<T, DV> oro;
-    TrOffsets<T, DH> qto;
-    TrOffsets<T, DV> oto;
-    if (side_a) { qro.init(lane); oto.init(lane); } else { oro.init(lane); qto.init(lane); }
+    // LDS operand offsets, one table shared by the roles (each needs
+    // DH/16 + DV/16 of them): X reads Q and G_O rows, Y reads them transposed.
+    //   X: ofs[ks] Q row operand, ofs[DH/16 + ks] G_O row operand;
+    //   Y: ofs[h * DV/32 + nt] G_O^T halves, ofs[DV/16 + h * DH/32 + nt] Q^T halves.
+    int ofs[DH / 16 + DV / 16];
+    if (side_x) {
+#pragma unroll
+      for (int ks = 0; ks < DH / 16; ++ks) ofs[ks] = RowOffsets<T, DH>::at(lane, ks);
+#pragma unroll
+      for (int ks = 0; ks < DV / 16; ++ks) ofs[DH / 16 + ks] = RowOffsets<T, DV>::at(lane, ks);
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int nt = 0; nt < DV / 32; ++nt) ofs[h * (DV / 32) + nt] = TrOffsets<T, DV>::at(lane, h, nt);
+#pragma unroll
+        for (int nt = 0; nt < DH / 32; ++nt) ofs[DV / 16 + h * (DH / 32) + nt] = TrOffsets<T, DH>::at(lane, h, nt);
+      }
+    }
+    auto row_op = [&](const T* tile, int off) -> op_t {
+      return *reinterpret_cast<const op_t*>(reinterpret_cast<const char*>(tile) + off);
+    };
 
     const int off_eff = p.causal ? p.offset : p.n_k;  // j <= i + n_k always holds
-    // ---- side A, step s: S, P (to LDS), G_V += P^T G_O
-    auto side_a_step = [&](int s, const T* Qs, const T* Os, const float* rows, float* px) {
-      const int q0 = (qb_first + s % nq) * C::BM;
-      f32x16 sv;
+    // ---- X: the products of one step
+    auto x_mfma = [&](const T* Qs, const T* Os, f32x16& sv, f32x16& dp) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sv[e] = 0.f;
+      for (int e = 0; e < 16; ++e) { sv[e] = 0.f; dp[e] = 0.f; }
+      constexpr int KS = (DH > DV ? DH : DV) / 16;
 #pragma unroll
-      for (int ks = 0; ks < DH / 16; ++ks) mma(sv, qro.read(Qs, 0, ks), kv[ks]);
-      f32x4 l4[4];
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks < DH / 16) mma(sv, row_op(Qs, ofs[ks]), op_part(R[ks / 4], ks % 4));
+        if (ks < DV / 16) mma(dp, row_op(Os, ofs[DH / 16 + ks]), op_part(R[(DH / 16 + ks) / 4], (DH / 16 + ks) % 4));
+      }
+    };
+    // ---- X: P on the visible set, G_S = P o (dP - D); both to LDS for Y
+    auto x_valu = [&](auto FULL, int q0, const float* rows, f32x16& sv, f32x16& dp, op_t* xb) {
+      f32x4 l4[4], d4[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j) {
         l4[j] = *reinterpret_cast<const f32x4*>(&rows[8 * j + 4 * kg]) * 1.4426950408889634f;
-      const bool full = (q0 + C::BM <= Lq) && (wk_hi <= Lk) && (!p.causal || wk_hi - 1 <= q0 + p.offset);
-      if (full) {
+        d4[j] = *reinterpret_cast<const f32x4*>(&rows[C::BM + 8 * j + 4 * kg]);
+      }
+      if constexpr (decltype(FULL)::value) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) sv[e] = __builtin_amdgcn_exp2f(fmaf(sv[e], p.scale_log2, -l4[e >> 2][e & 3]));
       } else {
@@ -670,94 +722,168 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(const KernelParam
           sv[e] = vis ? pv : 0.f;
         }
       }
-      // hand P to side B (element-major: float4 j of lane l at (j * 64 + l) * 4)
-      float* pp = px + pair * 4 * 64 * 4;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        f32x4 v;
-        v[0] = sv[4 * j]; v[1] = sv[4 * j + 1]; v[2] = sv[4 * j + 2]; v[3] = sv[4 * j + 3];
-        *reinterpret_cast<f32x4*>(pp + (j * 64 + lane) * 4) = v;
-      }
-      // G_V += P^T G_O
+      for (int e = 0; e < 16; ++e) dp[e] = sv[e] * (dp[e] - d4[e >> 2][e & 3]);
+      op_t* xp = xb + pair * 4 * 64;
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        float tmp[8];
+        float pt[8], dt[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) tmp[e] = sv[8 * st + e];
-        const op_t pa = to_op<T>(tmp);
-#pragma unroll
-        for (int nt = 0; nt < DV / 32; ++nt) mma(acc[nt], pa, oto.read(Os, 16 * st, nt));
+        for (int e = 0; e < 8; ++e) { pt[e] = sv[8 * st + e]; dt[e] = dp[8 * st + e]; }
+        xp[st * 64 + lane] = to_op<T>(pt);
+        xp[(2 + st) * 64 + lane] = to_op<T>(dt);
       }
     };
-    // ---- side B, step s: dP, G_S = P o (dP - D), G_K += G_S^T Q
-    auto side_b_step = [&](const T* Qs, const T* Os, const float* rows, const float* px) {
-      f32x16 dp;
+    // ---- X: products of one step interleaved with the element-wise work of
+    // the previous one: after the two products of each k-step, a share of the
+    // exponentials and G_S run while the matrix core is busy.  The scheduling
+    // barrier keeps that order (only LDS reads may move ahead of it).
+    auto x_fused = [&](auto FULL, const T* Qs, const T* Os, f32x16& sv, f32x16& dp, int q0,
+                       const float* rows, f32x16& so, f32x16& dpo, op_t* xb) {
+      constexpr int KS = (DH > DV ? DH : DV) / 16;
+      constexpr int EPK = 16 / KS;  // elements finished per k-step
+      f32x4 l4, d4;                 // lse and D of the current group of four rows
 #pragma unroll
-      for (int e = 0; e < 16; ++e) dp[e] = 0.f;
+      for (int e = 0; e < 16; ++e) { sv[e] = 0.f; dp[e] = 0.f; }
+      op_t* xp = xb + pair * 4 * 64;
 #pragma unroll
-      for (int ks = 0; ks < DV / 16; ++ks) mma(dp, oro.read(Os, 0, ks), kv[ks]);
-      const float* pp = px + pair * 4 * 64 * 4;
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks < DH / 16) mma(sv, row_op(Qs, ofs[ks]), op_part(R[ks / 4], ks % 4));
+        if (ks < DV / 16) mma(dp, row_op(Os, ofs[DH / 16 + ks]), op_part(R[(DH / 16 + ks) / 4], (DH / 16 + ks) % 4));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 pv = *reinterpret_cast<const f32x4*>(pp + (j * 64 + lane) * 4);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&rows[C::BM + 8 * j + 4 * kg]);
+        for (int e = EPK * ks; e < EPK * (ks + 1); ++e) {
+          if ((e & 3) == 0) {
+            l4 = *reinterpret_cast<const f32x4*>(&rows[8 * (e >> 2) + 4 * kg]) * 1.4426950408889634f;
+            d4 = *reinterpret_cast<const f32x4*>(&rows[C::BM + 8 * (e >> 2) + 4 * kg]);
+          }
+          const float pv = __builtin_amdgcn_exp2f(fmaf(so[e], p.scale_log2, -l4[e & 3]));
+          float pe;
+          if constexpr (decltype(FULL)::value) {
+            pe = pv;
+          } else {
+            const int q = q0 + 8 * (e >> 2) + 4 * kg + (e & 3);
+            const bool vis = (key < Lk) & (q < Lq) & (key <= q + off_eff);
+            pe = vis ? pv : 0.f;
+          }
+          so[e] = pe;
+          dpo[e] = pe * (dpo[e] - d4[e & 3]);
+        }
+        if (EPK * (ks + 1) % 8 == 0) {
+          const int st = EPK * (ks + 1) / 8 - 1;
+          float pt[8], dt[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dp[4 * j + i] = pv[i] * (dp[4 * j + i] - d4[i]);
+          for (int e = 0; e < 8; ++e) { pt[e] = so[8 * st + e]; dt[e] = dpo[8 * st + e]; }
+          xp[st * 64 + lane] = to_op<T>(pt);
+          xp[(2 + st) * 64 + lane] = to_op<T>(dt);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // ---- Y: G_V += P^T G_O, G_K += G_S^T Q
+    auto y_step = [&](const T* Qs, const T* Os, const op_t* xb) {
+      const op_t* xp = xb + pair * 4 * 64;
+      op_t pa[2], da[2];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        pa[st] = xp[st * 64 + lane];
+        da[st] = xp[(2 + st) * 64 + lane];
       }
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        float tmp[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) tmp[e] = dp[8 * st + e];
-        const op_t da = to_op<T>(tmp);
+        for (int nt = 0; nt < DV / 32; ++nt)
+          mma(R[nt], pa[st], TrOffsets<T, DV>::read_at(Os, 16 * st, ofs[nt], ofs[DV / 32 + nt]));
 #pragma unroll
-        for (int nt = 0; nt < DH / 32; ++nt) mma(acc[nt], da, qto.read(Qs, 16 * st, nt));
+        for (int nt = 0; nt < DH / 32; ++nt)
+          mma(R[DV / 32 + nt], da[st],
+              TrOffsets<T, DH>::read_at(Qs, 16 * st, ofs[DV / 16 + nt], ofs[DV / 16 + DH / 32 + nt]));
       }
     };
 
-    // Iteration s: side A does step s, side B step s - 1 (P of step s - 1 was
-    // written before the barrier).  Step s's copies must have landed; those
-    // of step s + 1 may stay in flight.  After the barrier the copies of step
-    // s + 2 go into the stage step s - 2 used (both sides are past it).
-    auto wait_for = [&](int s) {
-      if (s + 1 < nsteps) stage_barrier<C::CPS>();
-      else stage_barrier<0>();
+    // (head, query block) of the next step to copy, and the query block of
+    // the step whose element-wise work X does next
+    int i_rr = 0, i_qb = qb_first, v_qb = qb_first;
+    auto next = [&](int& rr, int& qb) {
+      if (++qb == qb_end) { qb = qb_first; ++rr; }
     };
-    issue(0, 0);
-    if (1 < nsteps) issue(1, 1);
-    for (int s0 = 0; s0 <= nsteps; s0 += NS) {
-#pragma unroll
-      for (int u = 0; u < NS; ++u) {
-        const int s = s0 + u;
-        if (s > nsteps) break;
-        wait_for(s);
-        if (s + 2 < nsteps) issue(s + 2, (u + 2) % NS);
-        if (side_a) {
-          if (s < nsteps) side_a_step(s, q_st(u), o_st(u), r_st(u) + w * 2 * C::BM, (u & 1) ? p_x1 : p_x0);
-        } else if (s >= 1) {
-          const int up = (u + NS - 1) % NS;
-          side_b_step(q_st(up), o_st(up), r_st(up) + w * 2 * C::BM, (u & 1) ? p_x0 : p_x1);
+    // Iteration s: X's products of step s and element-wise work of step s - 1,
+    // Y's step s - 2.  At its barrier the copies of step s must have landed;
+    // those of steps s + 1 .. s + PD - 1 may still be in flight.  After the
+    // barrier, step s + PD is copied into the stage step s - 3 used.
+    auto body = [&](int s, auto U) -> bool {
+      constexpr int u = decltype(U)::value;
+      if (s > nsteps + 1) return false;
+      const int ahead = min(PD - 1, nsteps - 1 - s);  // later steps whose copies are in flight
+      if (side_x || ahead <= 0) stage_barrier<0>();  // X issues no copies
+      else if (ahead >= 2) stage_barrier<2 * C::CPS>();
+      else stage_barrier<C::CPS>();
+      if (!side_x && s + PD < nsteps) { issue(i_rr, i_qb, IC<u + PD>()); next(i_rr, i_qb); }
+      if (side_x) {
+        f32x16& sv_new = R[KVB + 2 * (u & 1)];
+        f32x16& dp_new = R[KVB + 2 * (u & 1) + 1];
+        f32x16& sv_old = R[KVB + 2 * ((u + 1) & 1)];
+        f32x16& dp_old = R[KVB + 2 * ((u + 1) & 1) + 1];
+        op_t* xw = (u & 1) ? x_x0 : x_x1;           // exchange slot of step s - 1
+        const bool mf = s < nsteps, va = s >= 1 && s <= nsteps;
+        if (va) {
+          const int q0 = v_qb * C::BM;
+          const bool full = (q0 + C::BM <= Lq) && (wk_hi <= Lk) && (!p.causal || wk_hi - 1 <= q0 + p.offset);
+          const float* rows = r_st(IC<u + NS - 1>()) + pair * 2 * C::BM;
+          // each case one straight-line block, so products and exponentials interleave
+          if (mf && full) {
+            x_fused(IC<1>(), q_st(U), o_st(U), sv_new, dp_new, q0, rows, sv_old, dp_old, xw);
+          } else if (mf) {
+            x_fused(IC<0>(), q_st(U), o_st(U), sv_new, dp_new, q0, rows, sv_old, dp_old, xw);
+          } else if (full) {
+            x_valu(IC<1>(), q0, rows, sv_old, dp_old, xw);
+          } else {
+            x_valu(IC<0>(), q0, rows, sv_old, dp_old, xw);
+          }
+          if (++v_qb == qb_end) v_qb = qb_first;
+        } else if (mf) {
+          x_mfma(q_st(U), o_st(U), sv_new, dp_new);
         }
+      } else if (s >= 2) {
+        y_step(q_st(IC<u + NS - 2>()), o_st(IC<u + NS - 2>()), (u & 1) ? x_x1 : x_x0);
+      }
+      return true;
+    };
+#pragma unroll
+    for (int t = 0; t < PD; ++t) {
+      if (!side_x && t < nsteps) {
+        if (t == 0) issue(i_rr, i_qb, IC<0>());
+        else if (t == 1) issue(i_rr, i_qb, IC<1>());
+        else issue(i_rr, i_qb, IC<2>());
+        next(i_rr, i_qb);
+      }
+    }
+    for (int s0 = 0; s0 <= nsteps + 1; s0 += NS) {
+      if (!body(s0, IC<0>())) break;
+      if (!body(s0 + 1, IC<1>())) break;
+      if (!body(s0 + 2, IC<2>())) break;
+      if (!body(s0 + 3, IC<3>())) break;
+      if constexpr (NS > 4) {
+        if (!body(s0 + 4, IC<4>())) break;
+        if (!body(s0 + 5, IC<5>())) break;
       }
     }
   }
 
-  // store: side A holds G_V, side B G_K (scaled); lane = d, registers = keys
-  if (side_a) {
+  // store (Y): G_V and G_K (scaled); lane = column, registers = keys
+  if (!side_x) {
 #pragma unroll
     for (int nt = 0; nt < DV / 32; ++nt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int kk = kw0 + 8 * (e >> 2) + 4 * kg + (e & 3);
-        if (kk < p.n_k) dVb[(int64_t)kk * p.v_sr + 32 * nt + (lane & 31)] = (T)acc[nt][e];
+        if (kk < p.n_k) dVb[(int64_t)kk * p.v_sr + 32 * nt + (lane & 31)] = (T)R[nt][e];
       }
-  } else {
 #pragma unroll
     for (int nt = 0; nt < DH / 32; ++nt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int kk = kw0 + 8 * (e >> 2) + 4 * kg + (e & 3);
-        if (kk < p.n_k) dKb[(int64_t)kk * p.k_sr + 32 * nt + (lane & 31)] = (T)(acc[nt][e] * p.scale);
+        if (kk < p.n_k) dKb[(int64_t)kk * p.k_sr + 32 * nt + (lane & 31)] = (T)(R[DV / 32 + nt][e] * p.scale);
       }
   }
 }

@@ -69,6 +69,19 @@ template <typename T> __device__ __forceinline__ typename Op<T>::type zero_op() 
   return r;
 }
 
+// A 32x32 accumulator block doubles as storage for four bf16 operands (the
+// bits of operand `part` occupy elements 4 part .. 4 part + 3), so waves that
+// hold operands and waves that hold accumulators can share one register array.
+__device__ __forceinline__ bf16x8 op_part(const f32x16& r, int part) {
+  const f32x4 v = {r[4 * part], r[4 * part + 1], r[4 * part + 2], r[4 * part + 3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+__device__ __forceinline__ void set_op_part(f32x16& r, int part, const bf16x8& x) {
+  const f32x4 v = __builtin_bit_cast(f32x4, x);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[4 * part + i] = v[i];
+}
+
 // ---------------------------------------------------------------- LDS tiles
 // Layout of a row-major [rows][D] tile in LDS, without padding: the 16-byte
 // chunk c of row r is stored at chunk position c ^ f(r) of that row.  Two read
@@ -167,10 +180,13 @@ __device__ __forceinline__ typename Op<T>::type ld_tr(const T* X, int kb, int nb
 template <typename T, int D>
 struct RowOffsets {
   int off[D / 16];
+  // byte offset, within a 32-row block, of the operand lane `lane` reads for k-step ks
+  static __device__ __forceinline__ int at(int lane, int ks) {
+    return Tile<T, D>::off(lane & 31, 16 * ks + 8 * (lane >> 5)) * (int)sizeof(T);
+  }
   __device__ __forceinline__ void init(int lane) {
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
-      off[ks] = Tile<T, D>::off(lane & 31, 16 * ks + 8 * (lane >> 5)) * (int)sizeof(T);
+    for (int ks = 0; ks < D / 16; ++ks) off[ks] = at(lane, ks);
   }
   // rows rb .. rb+31 (rb a multiple of 32)
   __device__ __forceinline__ typename Op<T>::type read(const T* tile, int rb, int ks) const {
@@ -186,24 +202,32 @@ struct RowOffsets {
 template <typename T, int D>
 struct TrOffsets {
   int off[2][D / 32];
-  __device__ __forceinline__ void init(int lane) {
+  // byte offset of half h of the transposed operand of column block nt
+  static __device__ __forceinline__ int at(int lane, int h, int nt) {
     const int s = lane & 15, grp = lane >> 4;
     const int r0 = 4 * (grp >> 1) + (s >> 2);
     const int e0 = 16 * (grp & 1) + 4 * (s & 3);
+    return Tile<T, D>::off(r0 + 8 * h, 32 * nt + e0) * (int)sizeof(T);
+  }
+  __device__ __forceinline__ void init(int lane) {
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int nt = 0; nt < D / 32; ++nt) off[h][nt] = Tile<T, D>::off(r0 + 8 * h, 32 * nt + e0) * (int)sizeof(T);
+      for (int nt = 0; nt < D / 32; ++nt) off[h][nt] = at(lane, h, nt);
+  }
+  // bf16 only: the operand from the two byte offsets of at()
+  static __device__ __forceinline__ bf16x8 read_at(const T* tile, int kb, int off0, int off1) {
+    const char* base = reinterpret_cast<const char*>(tile) + kb * D * (int)sizeof(T);
+    i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4*)(base + off0));
+    i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4*)(base + off1));
+    union { i16x4 v[2]; bf16x8 b; } u;
+    u.v[0] = lo;
+    u.v[1] = hi;
+    return u.b;
   }
   __device__ __forceinline__ typename Op<T>::type read(const T* tile, int kb, int nt) const {
     if constexpr (sizeof(T) == 2) {
-      const char* base = reinterpret_cast<const char*>(tile) + kb * D * (int)sizeof(T);
-      i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4*)(base + off[0][nt]));
-      i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4*)(base + off[1][nt]));
-      union { i16x4 v[2]; bf16x8 b; } u;
-      u.v[0] = lo;
-      u.v[1] = hi;
-      return u.b;
+      return read_at(tile, kb, off[0][nt], off[1][nt]);
     } else {
       return ld_tr<T, D>(tile, kb, 32 * nt);
     }
