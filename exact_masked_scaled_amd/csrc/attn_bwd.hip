@@ -499,105 +499,105 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const KernelParams p) 
   }
 }
 
-// ============================================================== dK/dV pass, wave pairs (bf16)
+// ============================================================== dK/dV pass, four roles (bf16)
 // Same work unit as bwd_dkdv_kernel (128 keys of one sequence and KV head,
-// every query head of the group, 32-row query steps).  The work of one 32-key
-// tile is split over a PAIR of waves that share a SIMD:
-//   wave X (waves 0-3): holds the tile's K and V rows.  In iteration s it
-//       issues the products S = Q K^T and dP = G_O V^T of step s and, in the
-//       same instruction stream, the element-wise work of step s - 1:
-//       P = exp(S - lse) on the visible set and G_S = P o (dP - D), handed to
-//       its partner through LDS already in bf16 MFMA operand form.  The
-//       exponentials thus run while the matrix cores work on the next step.
-//   wave Y (waves 4-7): two steps behind, accumulates G_V += P^T G_O and
-//       G_K += G_S^T Q (sixteen products on eight independent accumulators).
-// Q / G_O tiles (and per pair the step's lse and D) arrive through an NS-stage
-// ring of direct global-to-LDS copies issued NS - 3 steps ahead (the other
-// three stages hold the tiles of steps s, s - 1 and s - 2); one workgroup
-// barrier per step.  Only Y waves issue copies, right after the barrier: a
-// wave stalls while its copies queue for the address unit, and this way X
-// keeps the matrix core busy meanwhile.
+// every query head of the group, 32-row query steps).  Each of the four
+// products of a step has its own wave per 64-key half, so every wave keeps a
+// 64-key operand or accumulator in registers and each LDS operand read feeds
+// two matrix products (half the LDS reads of 32-key waves):
+//   XS (waves 0, 1): holds K; S = Q K^T, then P = exp(S - lse) on the visible
+//       set, handed on as bf16 MFMA operands;
+//   XD (waves 2, 3): holds V; dP = G_O V^T, then G_S = P o (dP - D), handed on;
+//   YV (waves 4, 5): G_V += P^T G_O;     YK (waves 6, 7): G_K += G_S^T Q.
+// In iteration s, XS forms S of step s and the exponentials of step s - 1; XD
+// forms dP of step s - 1 and G_S of step s - 2; YV accumulates step s - 2 and
+// YK step s - 3.  Products and element-wise work of one wave are interleaved
+// so the exponentials run while the matrix core works; a SIMD holds one X and
+// one Y wave.  Q / G_O tiles (and the step's lse and D rows) come through an
+// NS-stage ring of direct global-to-LDS copies, issued by the Y waves two
+// steps ahead right after the barrier (a wave stalls while its copies queue,
+// and its X partner keeps the SIMD busy meanwhile).
 template <typename T, int DH, int DV>
-struct DkvPairCfg {
-  static constexpr int NW = 8;            // waves: 4 pairs
-  static constexpr int PAIRS = 4;
-  static constexpr int BN = 32 * PAIRS;   // keys per workgroup
+struct DkvQuadCfg {
+  static constexpr int NW = 8;
+  static constexpr int KH = 64;           // keys per half (per wave of a role)
+  static constexpr int BN = 2 * KH;       // keys per workgroup
   static constexpr int BM = 32;           // query rows per step
-  static constexpr int NS = 4;            // ring stages (even: exchange parity follows the stage)
-  static constexpr int PD = NS - 3;       // copy distance in steps
-  static constexpr int QCH = BM * Tile<T, DH>::CH;   // 16-byte chunks of a Q tile
-  static constexpr int OCH = BM * Tile<T, DV>::CH;   // ... of a G_O tile
-  static constexpr int JOBS = (QCH + OCH) / 64;      // wave-instructions of copies per step
-  static constexpr int JPW = JOBS / PAIRS;           // per Y wave (Y waves issue every copy)
-  static constexpr int CPS = JPW + 1;                // + the pair's lse/D copy
-  static constexpr int NR = DH / 32 + DV / 32;       // Y's accumulator blocks
-  static constexpr int KVB = (DH + DV) / 64;         // X's blocks holding K and V
-  static constexpr int NB = NR > KVB + 4 ? NR : KVB + 4;
-  static_assert(QCH % 64 == 0 && OCH % 64 == 0 && JOBS % PAIRS == 0, "tiles must be whole wave copies");
-  static_assert(NS % 2 == 0 && NS >= 4 && NS <= 6, "ring stages");
+  static constexpr int NS = 6;            // ring stages: steps s - 3 .. s + 2
+  static constexpr int PD = NS - 4;       // copy distance in steps
+  static constexpr int QCH = BM * Tile<T, DH>::CH;
+  static constexpr int OCH = BM * Tile<T, DV>::CH;
+  static constexpr int JOBS = (QCH + OCH) / 64;      // wave-instructions of tile copies per step
+  static constexpr int JPW = JOBS / 4;               // per Y wave
+  static constexpr int CPS = JPW + 1;                // + the lse/D row copy
+  static constexpr int KB_S = 2 * DH / 64;           // register blocks of XS's K rows
+  static constexpr int KB_D = 2 * DV / 64;           // ... of XD's V rows
+  static constexpr int NB_X = (KB_S > KB_D ? KB_S : KB_D) + 4;   // + two S / dP buffers
+  static constexpr int NB_Y = 2 * (DH > DV ? DH : DV) / 32;      // accumulators
+  static constexpr int NB = NB_X > NB_Y ? NB_X : NB_Y;
+  static_assert(QCH % 64 == 0 && OCH % 64 == 0 && JOBS % 4 == 0, "tiles must be whole wave copies");
+  static_assert(NS % 2 == 0, "exchange parity follows the stage");
 };
 
-template <int N> struct IC { static constexpr int value = N; };
-
 template <typename T, int DH, int DV>
-__global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(const KernelParams p) {
-  static_assert(sizeof(T) == 2, "wave-pair dK/dV pass is the bf16 path");
-  using C = DkvPairCfg<T, DH, DV>;
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParams p) {
+  static_assert(sizeof(T) == 2, "four-role dK/dV pass is the bf16 path");
+  using C = DkvQuadCfg<T, DH, DV>;
   using op_t = typename Op<T>::type;
-  constexpr int NS = C::NS, PD = C::PD, KVB = C::KVB;
-  // One __shared__ array per ring stage (its Q tile, G_O tile and lse/D rows),
-  // selected at compile time: the compiler then tells a stage being read from
-  // the one being copied into and does not wait for copies still in flight
-  // (it keeps only a few distinct copy targets apart, so a few large arrays).
+  constexpr int NS = C::NS, PD = C::PD;
+  // one __shared__ array per ring stage (Q tile, G_O tile, lse/D rows),
+  // selected at compile time so reads need not wait for unrelated copies
   constexpr int QB = C::BM * DH * (int)sizeof(T), OB = C::BM * DV * (int)sizeof(T);
-  constexpr int SB = QB + OB + C::PAIRS * 2 * C::BM * (int)sizeof(float);
+  constexpr int SB = QB + OB + 2 * C::BM * (int)sizeof(float);
   __shared__ __attribute__((aligned(16))) char st0[SB];
   __shared__ __attribute__((aligned(16))) char st1[SB];
   __shared__ __attribute__((aligned(16))) char st2[SB];
   __shared__ __attribute__((aligned(16))) char st3[SB];
   __shared__ __attribute__((aligned(16))) char st4[SB];
   __shared__ __attribute__((aligned(16))) char st5[SB];
-  // P and G_S handed from X to Y: per pair 4 operands per lane (P k-steps 0, 1,
-  // then G_S k-steps 0, 1), operand j of lane l at index j * 64 + l
-  __shared__ op_t x_x0[C::PAIRS * 4 * 64];
-  __shared__ op_t x_x1[C::PAIRS * 4 * 64];
-  auto stage = [&](auto K) -> char* {
+  // P (from XS) and G_S (from XD), two slots each: per half, per 32-key block
+  // and per 16-row k-step one operand per lane, at ((h * 2 + kb) * 2 + ks) * 64 + lane
+  __shared__ op_t xp0[2 * 2 * 2 * 64];
+  __shared__ op_t xp1[2 * 2 * 2 * 64];
+  __shared__ op_t xd0[2 * 2 * 2 * 64];
+  __shared__ op_t xd1[2 * 2 * 2 * 64];
+  auto stage = [&](auto K) __attribute__((always_inline)) -> char* {
     constexpr int k = decltype(K)::value % NS;
     if constexpr (k == 0) return st0; else if constexpr (k == 1) return st1;
     else if constexpr (k == 2) return st2; else if constexpr (k == 3) return st3;
     else if constexpr (k == 4) return st4; else return st5;
   };
-  auto q_st = [&](auto K) -> T* { return reinterpret_cast<T*>(stage(K)); };
-  auto o_st = [&](auto K) -> T* { return reinterpret_cast<T*>(stage(K) + QB); };
-  auto r_st = [&](auto K) -> float* { return reinterpret_cast<float*>(stage(K) + QB + OB); };
+  auto q_st = [&](auto K) __attribute__((always_inline)) -> T* { return reinterpret_cast<T*>(stage(K)); };
+  auto o_st = [&](auto K) __attribute__((always_inline)) -> T* { return reinterpret_cast<T*>(stage(K) + QB); };
+  auto r_st = [&](auto K) __attribute__((always_inline)) -> float* { return reinterpret_cast<float*>(stage(K) + QB + OB); };
 
   int unit, kb;
   if (!map_work(blockIdx.x, p.groups, p.per_group, p.xcd_map, unit, kb)) return;
   const int b = unit / p.H_kv, g = unit - (unit / p.H_kv) * p.H_kv;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, kg = lane >> 5;
-  const int pair = w & 3;
-  const bool side_x = w < C::PAIRS;
+  const int h = w & 1;                                   // key half
+  const bool is_x = w < 4, is_s = (w & 2) == 0;          // XS / YV use P, XD / YK use G_S
   const int Lq = p.has_lens ? p.lens_q[b] : p.n_q;
   const int Lk = p.has_lens ? p.lens_k[b] : p.n_k;
   const int k_lo = kb * C::BN;
-  const int kw0 = k_lo + 32 * pair;               // first key of the pair
-  const int key = kw0 + (lane & 31);              // this lane's key
-  const int wk_hi = kw0 + 32;
+  const int kh0 = k_lo + C::KH * h;                      // first key of the half
+  const int kh_hi = kh0 + C::KH;
 
   const T* Kb = (const T*)p.k + b * p.k_sb + g * p.k_sh;
   const T* Vb = (const T*)p.v + b * p.v_sb + g * p.v_sh;
   T* dKb = (T*)p.dk + b * p.k_sb + g * p.k_sh;
   T* dVb = (T*)p.dv + b * p.v_sb + g * p.v_sh;
 
-  // Y: R[0, DV/32) accumulate G_V, R[DV/32, NR) G_K.
-  // X: R[0, KVB) hold this lane's K row (operands 0 .. DH/16-1) and V row
-  //    (operands DH/16 ..); R[KVB + 2j], R[KVB + 2j + 1] the S and dP tiles of
-  //    the steps with parity j.
+  // XS: R[0, KB_S) this lane's K rows of both 32-key blocks (operand
+  //     kb2 * DH/16 + ks), R[NB_X - 4 + 2j + kb2] the S tile of parity j;
+  // XD: the same with V rows and dP tiles;
+  // YV / YK: R[kb2 * D/32 + nt] accumulate G_V / G_K.
   f32x16 R[C::NB];
 #pragma unroll
   for (int i = 0; i < C::NB; ++i)
 #pragma unroll
     for (int e = 0; e < 16; ++e) R[i][e] = 0.f;
+  constexpr int XB = C::NB_X - 4;  // first S / dP buffer block
 
   const int q_first = p.causal ? max(0, k_lo - p.offset) : 0;
   const int qb_first = q_first / C::BM;
@@ -606,31 +606,42 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(const KernelParam
   const int nsteps = nq * p.group;
 
   if (nsteps > 0) {
-    if (side_x) {
-      const bool ok = key < p.n_k;
-      const T* ksrc = Kb + (int64_t)key * p.k_sr + 8 * kg;
-      const T* vsrc = Vb + (int64_t)key * p.v_sr + 8 * kg;
+    if (is_x) {
+      const T* src = is_s ? Kb : Vb;
+      const int64_t sr = is_s ? p.k_sr : p.v_sr;
+      const int nks = is_s ? DH / 16 : DV / 16;
 #pragma unroll
-      for (int ks = 0; ks < DH / 16; ++ks)
-        set_op_part(R[ks / 4], ks % 4, ok ? ld8<T>(ksrc + 16 * ks) : zero_op<T>());
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        const int key = kh0 + 32 * kb2 + (lane & 31);
+        const bool ok = key < p.n_k;
+        const T* row = src + (int64_t)key * sr + 8 * kg;
+        constexpr int NK = (DH > DV ? DH : DV) / 16;
 #pragma unroll
-      for (int ks = 0; ks < DV / 16; ++ks)
-        set_op_part(R[(DH / 16 + ks) / 4], (DH / 16 + ks) % 4, ok ? ld8<T>(vsrc + 16 * ks) : zero_op<T>());
+        for (int ks = 0; ks < NK; ++ks) {
+          if (ks >= nks) continue;
+          const op_t v = ok ? ld8<T>(row + 16 * ks) : zero_op<T>();
+          // operand kb2 * nks + ks: the block index is a constant in each role's branch
+          if (is_s) {
+            if (ks < DH / 16) set_op_part(R[(kb2 * (DH / 16) + ks) / 4], (kb2 * (DH / 16) + ks) % 4, v);
+          } else {
+            if (ks < DV / 16) set_op_part(R[(kb2 * (DV / 16) + ks) / 4], (kb2 * (DV / 16) + ks) % 4, v);
+          }
+        }
+      }
     }
 
-    // Copies.  The per-lane part of every address is fixed for the whole loop
-    // (chunk position within the tile, swizzled); per step only the tile base
-    // moves, and lanes clamp their row only in the ragged last block.
+    // copies (Y waves): per-lane address parts fixed for the loop
     const T* const q_base = (const T*)p.q + b * p.q_sb;
     const T* const o_base = (const T*)p.dout + b * p.o_sb;
     const int64_t q_sh = p.q_sh, o_sh = p.o_sh, q_sr = p.q_sr, o_sr = p.o_sr;
     const int n_q = p.n_q, group = p.group;
     const float* const rows_lane = (lane < 32 ? p.lse : p.delta) + (int64_t)b * p.H_q * n_q + (lane & 31);
-    int64_t c_off[C::JPW];  // (Y) element offset of this lane's chunk from the tile's first row
-    int c_row[C::JPW];      // ... and its row within the tile
+    const int yw = w & 3;  // copy slot of a Y wave
+    int64_t c_off[C::JPW];
+    int c_row[C::JPW];
 #pragma unroll
     for (int i = 0; i < C::JPW; ++i) {
-      const int job = pair + C::PAIRS * i;
+      const int job = yw + 4 * i;
       if (job < C::QCH / 64) {
         using L = Tile<T, DH>;
         const int pc = job * 64 + lane, row = pc / L::CH;
@@ -643,7 +654,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(const KernelParam
         c_off[i] = row * o_sr + ((pc % L::CH) ^ L::f(row)) * L::EPC;
       }
     }
-    auto issue = [&](int rr, int qb, auto ST) {
+    auto issue = [&](int rr, int qb, auto ST) __attribute__((always_inline)) {
       const int r = g * group + rr;
       const int q0 = qb * C::BM;
       const bool whole = q0 + C::BM <= n_q;
@@ -651,7 +662,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(const KernelParam
       const T* ot = o_base + r * o_sh + (int64_t)q0 * o_sr;
 #pragma unroll
       for (int i = 0; i < C::JPW; ++i) {
-        const int job = pair + C::PAIRS * i;
+        const int job = yw + 4 * i;
         const T* src;
         T* dst;
         if (job < C::QCH / 64) {
@@ -663,228 +674,273 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(const KernelParam
         }
         __builtin_amdgcn_global_load_lds((const void*)src, (ATTN_LDS void*)dst, 16, 0, 0);
       }
+      // every Y wave copies the same lse / D rows (keeps the per-wave count equal)
       const int qq = whole ? q0 : min(q0 + (lane & 31), n_q - 1) - (lane & 31);
-      load_lane_floats(rows_lane + (int64_t)r * n_q + qq, r_st(ST) + pair * 2 * C::BM);
+      load_lane_floats(rows_lane + (int64_t)r * n_q + qq, r_st(ST));
     };
 
-    // LDS operand offsets, one table shared by the roles (each needs
-    // DH/16 + DV/16 of them): X reads Q and G_O rows, Y reads them transposed.
-    //   X: ofs[ks] Q row operand, ofs[DH/16 + ks] G_O row operand;
-    //   Y: ofs[h * DV/32 + nt] G_O^T halves, ofs[DV/16 + h * DH/32 + nt] Q^T halves.
-    int ofs[DH / 16 + DV / 16];
-    if (side_x) {
+    // LDS operand offsets, one table for all roles:
+    //   XS: Q row operands; XD: G_O row operands;
+    //   YV: G_O^T halves ofs[hh * DV/32 + nt]; YK: Q^T halves ofs[hh * DH/32 + nt]
+    constexpr int NOFS = (DH > DV ? DH : DV) / 16;
+    int ofs[NOFS];
+    if (is_x) {
 #pragma unroll
-      for (int ks = 0; ks < DH / 16; ++ks) ofs[ks] = RowOffsets<T, DH>::at(lane, ks);
-#pragma unroll
-      for (int ks = 0; ks < DV / 16; ++ks) ofs[DH / 16 + ks] = RowOffsets<T, DV>::at(lane, ks);
+      for (int ks = 0; ks < NOFS; ++ks) ofs[ks] = is_s ? RowOffsets<T, DH>::at(lane, ks) : RowOffsets<T, DV>::at(lane, ks);
     } else {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int nt = 0; nt < DV / 32; ++nt) ofs[h * (DV / 32) + nt] = TrOffsets<T, DV>::at(lane, h, nt);
-#pragma unroll
-        for (int nt = 0; nt < DH / 32; ++nt) ofs[DV / 16 + h * (DH / 32) + nt] = TrOffsets<T, DH>::at(lane, h, nt);
-      }
+        for (int nt = 0; nt < NOFS / 2; ++nt)
+          ofs[hh * (NOFS / 2) + nt] = is_s ? TrOffsets<T, DV>::at(lane, hh, nt) : TrOffsets<T, DH>::at(lane, hh, nt);
     }
-    auto row_op = [&](const T* tile, int off) -> op_t {
+    auto row_op = [&](const T* tile, int off) __attribute__((always_inline)) -> op_t {
       return *reinterpret_cast<const op_t*>(reinterpret_cast<const char*>(tile) + off);
     };
 
     const int off_eff = p.causal ? p.offset : p.n_k;  // j <= i + n_k always holds
-    // ---- X: the products of one step
-    auto x_mfma = [&](const T* Qs, const T* Os, f32x16& sv, f32x16& dp) {
+    auto full_tile = [&](int q0) __attribute__((always_inline)) {
+      return (q0 + C::BM <= Lq) && (kh_hi <= Lk) && (!p.causal || kh_hi - 1 <= q0 + p.offset);
+    };
+
+    // ---- XS: S of one step (both key blocks share each Q operand read)
+    // interleaved with the exponentials of the previous step
+    auto xs_iter = [&](auto MF, auto EX, auto FULL, auto J, const T* Qs, int q0_old, const float* rows,
+                       op_t* xb) __attribute__((always_inline)) {
+      constexpr bool mf = decltype(MF)::value, ex = decltype(EX)::value;
+      constexpr int jn = decltype(J)::value, jo = jn ^ 1;
+      f32x16& s0 = R[XB + 2 * jn];
+      f32x16& s1 = R[XB + 2 * jn + 1];
+      f32x16& o0 = R[XB + 2 * jo];
+      f32x16& o1 = R[XB + 2 * jo + 1];
+      if constexpr (mf) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) { sv[e] = 0.f; dp[e] = 0.f; }
-      constexpr int KS = (DH > DV ? DH : DV) / 16;
+        for (int e = 0; e < 16; ++e) { s0[e] = 0.f; s1[e] = 0.f; }
+      }
+      constexpr int KS = DH / 16;
+      constexpr int EPK = 16 / KS;  // elements of each block finished per k-step
+      // operands are read one k-step ahead of their products, the rows up front
+      f32x4 l4v[4];
+      if constexpr (ex) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) l4v[j] = *reinterpret_cast<const f32x4*>(&rows[8 * j + 4 * kg]);
+      }
+      op_t a_nxt;
+      if constexpr (mf) a_nxt = row_op(Qs, ofs[0]);
+      op_t* xo = xb + (h * 2) * 2 * 64;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        if (ks < DH / 16) mma(sv, row_op(Qs, ofs[ks]), op_part(R[ks / 4], ks % 4));
-        if (ks < DV / 16) mma(dp, row_op(Os, ofs[DH / 16 + ks]), op_part(R[(DH / 16 + ks) / 4], (DH / 16 + ks) % 4));
-      }
-    };
-    // ---- X: P on the visible set, G_S = P o (dP - D); both to LDS for Y
-    auto x_valu = [&](auto FULL, int q0, const float* rows, f32x16& sv, f32x16& dp, op_t* xb) {
-      f32x4 l4[4], d4[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        l4[j] = *reinterpret_cast<const f32x4*>(&rows[8 * j + 4 * kg]) * 1.4426950408889634f;
-        d4[j] = *reinterpret_cast<const f32x4*>(&rows[C::BM + 8 * j + 4 * kg]);
-      }
-      if constexpr (decltype(FULL)::value) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) sv[e] = __builtin_amdgcn_exp2f(fmaf(sv[e], p.scale_log2, -l4[e >> 2][e & 3]));
-      } else {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int q = q0 + 8 * (e >> 2) + 4 * kg + (e & 3);
-          const bool vis = (key < Lk) & (q < Lq) & (key <= q + off_eff);
-          const float pv = __builtin_amdgcn_exp2f(fmaf(sv[e], p.scale_log2, -l4[e >> 2][e & 3]));
-          sv[e] = vis ? pv : 0.f;
+        if constexpr (mf) {
+          const op_t a = a_nxt;
+          if (ks + 1 < KS) a_nxt = row_op(Qs, ofs[ks + 1]);
+          mma(s0, a, op_part(R[ks / 4], ks % 4));
+          mma(s1, a, op_part(R[(DH / 16 + ks) / 4], (DH / 16 + ks) % 4));
         }
-      }
+        if constexpr (ex) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) dp[e] = sv[e] * (dp[e] - d4[e >> 2][e & 3]);
-      op_t* xp = xb + pair * 4 * 64;
+          for (int e = EPK * ks; e < EPK * (ks + 1); ++e) {
+            const float lse2 = l4v[e >> 2][e & 3] * 1.4426950408889634f;
+            const int q = q0_old + 8 * (e >> 2) + 4 * kg + (e & 3);
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        float pt[8], dt[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) { pt[e] = sv[8 * st + e]; dt[e] = dp[8 * st + e]; }
-        xp[st * 64 + lane] = to_op<T>(pt);
-        xp[(2 + st) * 64 + lane] = to_op<T>(dt);
-      }
-    };
-    // ---- X: products of one step interleaved with the element-wise work of
-    // the previous one: after the two products of each k-step, a share of the
-    // exponentials and G_S run while the matrix core is busy.  The scheduling
-    // barrier keeps that order (only LDS reads may move ahead of it).
-    auto x_fused = [&](auto FULL, const T* Qs, const T* Os, f32x16& sv, f32x16& dp, int q0,
-                       const float* rows, f32x16& so, f32x16& dpo, op_t* xb) {
-      constexpr int KS = (DH > DV ? DH : DV) / 16;
-      constexpr int EPK = 16 / KS;  // elements finished per k-step
-      f32x4 l4, d4;                 // lse and D of the current group of four rows
-#pragma unroll
-      for (int e = 0; e < 16; ++e) { sv[e] = 0.f; dp[e] = 0.f; }
-      op_t* xp = xb + pair * 4 * 64;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if (ks < DH / 16) mma(sv, row_op(Qs, ofs[ks]), op_part(R[ks / 4], ks % 4));
-        if (ks < DV / 16) mma(dp, row_op(Os, ofs[DH / 16 + ks]), op_part(R[(DH / 16 + ks) / 4], (DH / 16 + ks) % 4));
-#pragma unroll
-        for (int e = EPK * ks; e < EPK * (ks + 1); ++e) {
-          if ((e & 3) == 0) {
-            l4 = *reinterpret_cast<const f32x4*>(&rows[8 * (e >> 2) + 4 * kg]) * 1.4426950408889634f;
-            d4 = *reinterpret_cast<const f32x4*>(&rows[C::BM + 8 * (e >> 2) + 4 * kg]);
+            for (int kb2 = 0; kb2 < 2; ++kb2) {
+              f32x16& so = kb2 ? o1 : o0;
+              const float pv = __builtin_amdgcn_exp2f(fmaf(so[e], p.scale_log2, -lse2));
+              if constexpr (decltype(FULL)::value) {
+                so[e] = pv;
+              } else {
+                const int key = kh0 + 32 * kb2 + (lane & 31);
+                so[e] = ((key < Lk) & (q < Lq) & (key <= q + off_eff)) ? pv : 0.f;
+              }
+            }
           }
-          const float pv = __builtin_amdgcn_exp2f(fmaf(so[e], p.scale_log2, -l4[e & 3]));
-          float pe;
-          if constexpr (decltype(FULL)::value) {
-            pe = pv;
-          } else {
-            const int q = q0 + 8 * (e >> 2) + 4 * kg + (e & 3);
-            const bool vis = (key < Lk) & (q < Lq) & (key <= q + off_eff);
-            pe = vis ? pv : 0.f;
-          }
-          so[e] = pe;
-          dpo[e] = pe * (dpo[e] - d4[e & 3]);
-        }
-        if (EPK * (ks + 1) % 8 == 0) {
-          const int st = EPK * (ks + 1) / 8 - 1;
-          float pt[8], dt[8];
+          if (EPK * (ks + 1) % 8 == 0) {
+            const int st = EPK * (ks + 1) / 8 - 1;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) { pt[e] = so[8 * st + e]; dt[e] = dpo[8 * st + e]; }
-          xp[st * 64 + lane] = to_op<T>(pt);
-          xp[(2 + st) * 64 + lane] = to_op<T>(dt);
+            for (int kb2 = 0; kb2 < 2; ++kb2) {
+              f32x16& so = kb2 ? o1 : o0;
+              float pt[8];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) pt[e] = so[8 * st + e];
+              xo[(kb2 * 2 + st) * 64 + lane] = to_op<T>(pt);
+            }
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
     };
-    // ---- Y: G_V += P^T G_O, G_K += G_S^T Q
-    auto y_step = [&](const T* Qs, const T* Os, const op_t* xb) {
-      const op_t* xp = xb + pair * 4 * 64;
-      op_t pa[2], da[2];
+    // ---- XD: dP of one step (both key blocks share each G_O operand read)
+    // interleaved with G_S of an earlier step (P from XS)
+    auto xd_iter = [&](auto MF, auto EX, auto J, const T* Os, const float* rows, const op_t* xpb, op_t* xb) __attribute__((always_inline)) {
+      constexpr bool mf = decltype(MF)::value, ex = decltype(EX)::value;
+      constexpr int jn = decltype(J)::value, jo = jn ^ 1;
+      f32x16& d0 = R[XB + 2 * jn];
+      f32x16& d1 = R[XB + 2 * jn + 1];
+      f32x16& o0 = R[XB + 2 * jo];
+      f32x16& o1 = R[XB + 2 * jo + 1];
+      if constexpr (mf) {
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        pa[st] = xp[st * 64 + lane];
-        da[st] = xp[(2 + st) * 64 + lane];
+        for (int e = 0; e < 16; ++e) { d0[e] = 0.f; d1[e] = 0.f; }
       }
+      constexpr int KS = DV / 16;
+      constexpr int EPK = 16 / KS;
+      const op_t* pin = xpb + (h * 2) * 2 * 64;
+      op_t* xo = xb + (h * 2) * 2 * 64;
+      // operands are read one k-step ahead of their products; D and P up front
+      f32x4 d4v[4];
+      op_t pp[2][2];
+      if constexpr (ex) {
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
+        for (int j = 0; j < 4; ++j) d4v[j] = *reinterpret_cast<const f32x4*>(&rows[C::BM + 8 * j + 4 * kg]);
 #pragma unroll
-        for (int nt = 0; nt < DV / 32; ++nt)
-          mma(R[nt], pa[st], TrOffsets<T, DV>::read_at(Os, 16 * st, ofs[nt], ofs[DV / 32 + nt]));
+        for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-        for (int nt = 0; nt < DH / 32; ++nt)
-          mma(R[DV / 32 + nt], da[st],
-              TrOffsets<T, DH>::read_at(Qs, 16 * st, ofs[DV / 16 + nt], ofs[DV / 16 + DH / 32 + nt]));
+          for (int st = 0; st < 2; ++st) pp[kb2][st] = pin[(kb2 * 2 + st) * 64 + lane];
+      }
+      op_t a_nxt;
+      if constexpr (mf) a_nxt = row_op(Os, ofs[0]);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if constexpr (mf) {
+          const op_t a = a_nxt;
+          if (ks + 1 < KS) a_nxt = row_op(Os, ofs[ks + 1]);
+          mma(d0, a, op_part(R[ks / 4], ks % 4));
+          mma(d1, a, op_part(R[(DV / 16 + ks) / 4], (DV / 16 + ks) % 4));
+        }
+        if constexpr (ex) {
+#pragma unroll
+          for (int e = EPK * ks; e < EPK * (ks + 1); ++e) {
+            const float dd = d4v[e >> 2][e & 3];
+            o0[e] = (float)pp[0][e >> 3][e & 7] * (o0[e] - dd);
+            o1[e] = (float)pp[1][e >> 3][e & 7] * (o1[e] - dd);
+          }
+          if (EPK * (ks + 1) % 8 == 0) {
+            const int st = EPK * (ks + 1) / 8 - 1;
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2) {
+              f32x16& so = kb2 ? o1 : o0;
+              float dt[8];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) dt[e] = so[8 * st + e];
+              xo[(kb2 * 2 + st) * 64 + lane] = to_op<T>(dt);
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // ---- YV / YK: accumulate over one step (each transposed read feeds both key blocks)
+    auto y_iter = [&](const T* tile, const op_t* xb) __attribute__((always_inline)) {
+      const op_t* in = xb + (h * 2) * 2 * 64;
+      op_t a[2][2];
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) a[kb2][st] = in[(kb2 * 2 + st) * 64 + lane];
+      if (is_s) {  // YV: G_V += P^T G_O
+        constexpr int NT = DV / 32;
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            const op_t bt = TrOffsets<T, DV>::read_at(tile, 16 * st, ofs[nt], ofs[NOFS / 2 + nt]);
+            mma(R[nt], a[0][st], bt);
+            mma(R[NT + nt], a[1][st], bt);
+          }
+      } else {     // YK: G_K += G_S^T Q
+        constexpr int NT = DH / 32;
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            const op_t bt = TrOffsets<T, DH>::read_at(tile, 16 * st, ofs[nt], ofs[NOFS / 2 + nt]);
+            mma(R[nt], a[0][st], bt);
+            mma(R[NT + nt], a[1][st], bt);
+          }
       }
     };
 
-    // (head, query block) of the next step to copy, and the query block of
-    // the step whose element-wise work X does next
-    int i_rr = 0, i_qb = qb_first, v_qb = qb_first;
-    auto next = [&](int& rr, int& qb) {
+    int i_rr = 0, i_qb = qb_first;   // next step to copy
+    int xs_qb = qb_first;            // query block of the step XS exponentiates next
+    auto next = [&](int& rr, int& qb) __attribute__((always_inline)) {
       if (++qb == qb_end) { qb = qb_first; ++rr; }
     };
-    // Iteration s: X's products of step s and element-wise work of step s - 1,
-    // Y's step s - 2.  At its barrier the copies of step s must have landed;
-    // those of steps s + 1 .. s + PD - 1 may still be in flight.  After the
-    // barrier, step s + PD is copied into the stage step s - 3 used.
-    auto body = [&](int s, auto U) -> bool {
+    using F = IC<0>;
+    using TR = IC<1>;
+    auto body = [&](int s, auto U) __attribute__((always_inline)) -> bool {
       constexpr int u = decltype(U)::value;
-      if (s > nsteps + 1) return false;
-      const int ahead = min(PD - 1, nsteps - 1 - s);  // later steps whose copies are in flight
-      if (side_x || ahead <= 0) stage_barrier<0>();  // X issues no copies
-      else if (ahead >= 2) stage_barrier<2 * C::CPS>();
+      if (s > nsteps + 2) return false;
+      const int ahead = min(PD - 1, nsteps - 1 - s);
+      if (is_x || ahead <= 0) stage_barrier<0>();
       else stage_barrier<C::CPS>();
-      if (!side_x && s + PD < nsteps) { issue(i_rr, i_qb, IC<u + PD>()); next(i_rr, i_qb); }
-      if (side_x) {
-        f32x16& sv_new = R[KVB + 2 * (u & 1)];
-        f32x16& dp_new = R[KVB + 2 * (u & 1) + 1];
-        f32x16& sv_old = R[KVB + 2 * ((u + 1) & 1)];
-        f32x16& dp_old = R[KVB + 2 * ((u + 1) & 1) + 1];
-        op_t* xw = (u & 1) ? x_x0 : x_x1;           // exchange slot of step s - 1
-        const bool mf = s < nsteps, va = s >= 1 && s <= nsteps;
-        if (va) {
-          const int q0 = v_qb * C::BM;
-          const bool full = (q0 + C::BM <= Lq) && (wk_hi <= Lk) && (!p.causal || wk_hi - 1 <= q0 + p.offset);
-          const float* rows = r_st(IC<u + NS - 1>()) + pair * 2 * C::BM;
-          // each case one straight-line block, so products and exponentials interleave
-          if (mf && full) {
-            x_fused(IC<1>(), q_st(U), o_st(U), sv_new, dp_new, q0, rows, sv_old, dp_old, xw);
-          } else if (mf) {
-            x_fused(IC<0>(), q_st(U), o_st(U), sv_new, dp_new, q0, rows, sv_old, dp_old, xw);
-          } else if (full) {
-            x_valu(IC<1>(), q0, rows, sv_old, dp_old, xw);
-          } else {
-            x_valu(IC<0>(), q0, rows, sv_old, dp_old, xw);
-          }
-          if (++v_qb == qb_end) v_qb = qb_first;
+      if (!is_x && s + PD < nsteps) { issue(i_rr, i_qb, IC<u + PD>()); next(i_rr, i_qb); }
+      constexpr int jn = u & 1;  // parity of step s (NS even)
+      if (is_x && is_s) {
+        // XS: S(s) and P(s - 1) -> xp[(s - 1) & 1]
+        op_t* xw = jn ? xp0 : xp1;
+        const float* rows = r_st(IC<u + NS - 1>());
+        const bool mf = s < nsteps, ex = s >= 1 && s <= nsteps;
+        const int q0 = xs_qb * C::BM;
+        if (mf && ex) {
+          if (full_tile(q0)) xs_iter(TR(), TR(), TR(), IC<jn>(), q_st(U), q0, rows, xw);
+          else xs_iter(TR(), TR(), F(), IC<jn>(), q_st(U), q0, rows, xw);
+        } else if (ex) {
+          if (full_tile(q0)) xs_iter(F(), TR(), TR(), IC<jn>(), q_st(U), q0, rows, xw);
+          else xs_iter(F(), TR(), F(), IC<jn>(), q_st(U), q0, rows, xw);
         } else if (mf) {
-          x_mfma(q_st(U), o_st(U), sv_new, dp_new);
+          xs_iter(TR(), F(), TR(), IC<jn>(), q_st(U), q0, rows, xw);
         }
-      } else if (s >= 2) {
-        y_step(q_st(IC<u + NS - 2>()), o_st(IC<u + NS - 2>()), (u & 1) ? x_x1 : x_x0);
+        if (ex) { if (++xs_qb == qb_end) xs_qb = qb_first; }
+      } else if (is_x) {
+        // XD: dP(s - 1) into parity (s - 1) & 1, G_S(s - 2) -> xd[(s - 2) & 1]
+        constexpr int jd = (u + 1) & 1;
+        const bool mf = s >= 1 && s <= nsteps, ex = s >= 2 && s <= nsteps + 1;
+        const T* Os = o_st(IC<u + NS - 1>());
+        const float* rows = r_st(IC<u + NS - 2>());
+        const op_t* pin = jn ? xp1 : xp0;    // P(s - 2)
+        op_t* xw = jn ? xd1 : xd0;           // slot (s - 2) & 1
+        if (mf && ex) xd_iter(TR(), TR(), IC<jd>(), Os, rows, pin, xw);
+        else if (ex) xd_iter(F(), TR(), IC<jd>(), Os, rows, pin, xw);
+        else if (mf) xd_iter(TR(), F(), IC<jd>(), Os, rows, pin, xw);
+      } else if (is_s) {
+        // YV: step s - 2 with P from xp[(s - 2) & 1]
+        if (s >= 2 && s <= nsteps + 1) y_iter(o_st(IC<u + NS - 2>()), jn ? xp1 : xp0);
+      } else {
+        // YK: step s - 3 with G_S from xd[(s - 3) & 1]
+        if (s >= 3) y_iter(q_st(IC<u + NS - 3>()), jn ? xd0 : xd1);
       }
       return true;
     };
-#pragma unroll
-    for (int t = 0; t < PD; ++t) {
-      if (!side_x && t < nsteps) {
-        if (t == 0) issue(i_rr, i_qb, IC<0>());
-        else if (t == 1) issue(i_rr, i_qb, IC<1>());
-        else issue(i_rr, i_qb, IC<2>());
-        next(i_rr, i_qb);
-      }
+    if (!is_x) {
+      issue(i_rr, i_qb, IC<0>());
+      next(i_rr, i_qb);
+      if (1 < nsteps) { issue(i_rr, i_qb, IC<1>()); next(i_rr, i_qb); }
     }
-    for (int s0 = 0; s0 <= nsteps + 1; s0 += NS) {
+    for (int s0 = 0; s0 <= nsteps + 2; s0 += NS) {
       if (!body(s0, IC<0>())) break;
       if (!body(s0 + 1, IC<1>())) break;
       if (!body(s0 + 2, IC<2>())) break;
       if (!body(s0 + 3, IC<3>())) break;
-      if constexpr (NS > 4) {
-        if (!body(s0 + 4, IC<4>())) break;
-        if (!body(s0 + 5, IC<5>())) break;
-      }
+      if (!body(s0 + 4, IC<4>())) break;
+      if (!body(s0 + 5, IC<5>())) break;
     }
   }
 
-  // store (Y): G_V and G_K (scaled); lane = column, registers = keys
-  if (!side_x) {
+  // store: YV holds G_V, YK G_K (scaled) of both key blocks; lane = column, registers = keys
+  auto store = [&](auto NTC, T* dst, int64_t sr, float sc) __attribute__((always_inline)) {
+    constexpr int NT = decltype(NTC)::value;
 #pragma unroll
-    for (int nt = 0; nt < DV / 32; ++nt)
+    for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int kk = kw0 + 8 * (e >> 2) + 4 * kg + (e & 3);
-        if (kk < p.n_k) dVb[(int64_t)kk * p.v_sr + 32 * nt + (lane & 31)] = (T)R[nt][e];
-      }
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-    for (int nt = 0; nt < DH / 32; ++nt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int kk = kw0 + 8 * (e >> 2) + 4 * kg + (e & 3);
-        if (kk < p.n_k) dKb[(int64_t)kk * p.k_sr + 32 * nt + (lane & 31)] = (T)(R[DV / 32 + nt][e] * p.scale);
-      }
+        for (int e = 0; e < 16; ++e) {
+          const int kk = kh0 + 32 * kb2 + 8 * (e >> 2) + 4 * kg + (e & 3);
+          if (kk < p.n_k) dst[(int64_t)kk * sr + 32 * nt + (lane & 31)] = (T)(R[kb2 * NT + nt][e] * sc);
+        }
+  };
+  if (!is_x) {
+    if (is_s) store(IC<DV / 32>(), dVb, p.v_sr, 1.f);
+    else store(IC<DH / 32>(), dKb, p.k_sr, p.scale);
   }
 }
 
@@ -904,7 +960,7 @@ static int launch_dkdv_t(const KernelParams& p, void* stream) {
   const int64_t grid = units * p.per_group;
   if (grid <= 0) return (int)hipSuccess;
   if constexpr (sizeof(T) == 2) {
-    hipLaunchKernelGGL((bwd_dkdv_pair_kernel<T, DH, DV>), dim3((unsigned)grid), dim3(512), 0, (hipStream_t)stream,
+    hipLaunchKernelGGL((bwd_dkdv_quad_kernel<T, DH, DV>), dim3((unsigned)grid), dim3(512), 0, (hipStream_t)stream,
                        p);
   } else {
     hipLaunchKernelGGL((bwd_dkdv_kernel<T, DH, DV>), dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, p);

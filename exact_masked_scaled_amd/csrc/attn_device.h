@@ -38,6 +38,11 @@ template <> struct Op<float> { using type = f32x8; };
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// A compile-time integer passed as a value, so generic lambdas can specialise
+// on it (register-array indices must be constants for the arrays to stay in
+// registers).
+template <int N> struct IC { static constexpr int value = N; };
+
 // ---------------------------------------------------------------- MFMA
 __device__ __forceinline__ void mma(f32x16& acc, const bf16x8& a, const bf16x8& b) {
   acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
