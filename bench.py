@@ -4,10 +4,12 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3] [--uniform-len N]
 
 One step = the whole hot path over one batch of synthetic input: the forward
-(O and lse) and the backward's three stages (D and accumulator clear; G_K, G_V
-and the G_Q accumulation; G_Q conversion), all through the C ABI on one HIP
+(O and lse) and the backward's two passes (the query-stationary pass: D and
+G_Q; the key-stationary pass: G_K and G_V), all through the C ABI on one HIP
 stream, inputs resident in HBM.  Default workload: bf16 causal GQA with key and
 row padding, B=8, H_q=32, H_kv=8, n=4096, d=128 (lengths drawn in [2048, 4096]).
+The other configurations (and this one with every length 4096) follow in
+`other_workloads`, timed over fewer steps.
 
 Prints ONE JSON line.  `value` is algorithmic TFLOP/s: only visible
 (query, key) pairs are credited, 2(d_h + d_v) FLOPs per pair forward and
@@ -110,6 +112,62 @@ def cpu_baseline(inp, seconds: float):
     }
 
 
+def measure(torch, attn, W, wl, uniform_len, steps, warmup):
+    """Time `steps` steps (forward, dQ pass, dK/dV pass) of one workload with
+    its inputs resident; returns (inputs, work, ms per step, ms per kernel, device)."""
+    import numpy as np
+
+    inp = W.make_inputs(wl, uniform_len=uniform_len)
+    kw = inp.mask_kwargs()
+    work = W.work(wl, inp.seqlens_q, inp.seqlens_k)
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    q, k, v, do = dev(inp.Q), dev(inp.K), dev(inp.V), dev(inp.GO)
+    o = torch.empty(wl.B, wl.H_q, wl.n_q, wl.d_v, dtype=q.dtype, device=q.device)
+    lse = torch.empty(wl.B, wl.H_q, wl.n_q, dtype=torch.float32, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    prob = attn.make_problem(wl.B, wl.H_q, wl.H_kv, wl.n_q, wl.n_k, wl.d_h, wl.d_v,
+                             attn.BF16 if wl.dtype == W.BF16 else attn.F32)
+    ws = torch.empty(attn.workspace_size(prob), dtype=torch.uint8, device=q.device)
+    staged = attn.StagedBackward(q, k, v, o, lse, do, dq, dk, dv, ws, **kw)
+    stream = torch.cuda.current_stream()
+    names = ("fwd", "bwd_dq", "bwd_dkdv")
+
+    def step(events=None):
+        if events is not None:
+            events[0].record(stream)
+        attn.fwd(q, k, v, out=o, lse=lse, stream=stream, **kw)
+        if events is not None:
+            events[1].record(stream)
+        staged.dq(stream)
+        if events is not None:
+            events[2].record(stream)
+        staged.dkdv(stream)
+        if events is not None:
+            events[3].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / steps
+    kern_ms = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps for j, n in enumerate(names)}
+    device = q.device
+    del q, k, v, do, o, lse, dq, dk, dv, ws, staged
+    torch.cuda.synchronize()
+    return inp, work, ms_per_step, kern_ms, device
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -120,6 +178,8 @@ def main(argv=None):
                     help="replace the drawn sequence lengths by this length (e.g. 4096: unpadded)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="time only the selected workload (default: also every other configuration, briefly)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after timing, run a plain elementwise copy of this many MiB (3 launches) "
                          "so HBM byte counters can be scaled against a kernel of known traffic")
@@ -141,54 +201,8 @@ def main(argv=None):
         return 2
     attn.lib()  # fail loudly without the library
     wl = W.WORKLOADS[args.workload]
-    inp = W.make_inputs(wl, uniform_len=args.uniform_len)
-    kw = inp.mask_kwargs()
-    work = W.work(wl, inp.seqlens_q, inp.seqlens_k)
-
-    import numpy as np
-
-    def dev(a):
-        if a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
-        return torch.from_numpy(a).cuda()
-
-    q, k, v, do = dev(inp.Q), dev(inp.K), dev(inp.V), dev(inp.GO)
-    o = torch.empty(wl.B, wl.H_q, wl.n_q, wl.d_v, dtype=q.dtype, device=q.device)
-    lse = torch.empty(wl.B, wl.H_q, wl.n_q, dtype=torch.float32, device=q.device)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    prob = attn.make_problem(wl.B, wl.H_q, wl.H_kv, wl.n_q, wl.n_k, wl.d_h, wl.d_v,
-                             attn.BF16 if wl.dtype == W.BF16 else attn.F32)
-    ws = torch.empty(attn.workspace_size(prob), dtype=torch.uint8, device=q.device)
-    staged = attn.StagedBackward(q, k, v, o, lse, do, dq, dk, dv, ws, **kw)
-    stream = torch.cuda.current_stream()
-
+    inp, work, ms_per_step, kern_ms, dev_of = measure(torch, attn, W, wl, args.uniform_len, args.steps, args.warmup)
     names = ("fwd", "bwd_dq", "bwd_dkdv")
-
-    def step(events=None):
-        if events is not None:
-            events[0].record(stream)
-        attn.fwd(q, k, v, out=o, lse=lse, stream=stream, **kw)
-        if events is not None:
-            events[1].record(stream)
-        staged.dq(stream)
-        if events is not None:
-            events[2].record(stream)
-        staged.dkdv(stream)
-        if events is not None:
-            events[3].record(stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    kern_ms = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j, n in enumerate(names)}
 
     flop = work["fwd_flop"] + work["bwd_flop"]
     value = flop / (ms_per_step * 1e-3) / 1e12
@@ -240,12 +254,28 @@ def main(argv=None):
     }
     if args.calibrate_copy_mib > 0:
         n = args.calibrate_copy_mib * (1 << 20) // 4
-        a = torch.ones(n, dtype=torch.float32, device=q.device)
+        a = torch.ones(n, dtype=torch.float32, device=dev_of)
         c = torch.empty_like(a)
         for _ in range(3):
             torch.mul(a, 1.0, out=c)  # reads and writes exactly n * 4 bytes
         torch.cuda.synchronize()
         result["copy_calibration"] = {"bytes_read": n * 4, "bytes_written": n * 4, "launches": 3}
+    if not args.no_other_workloads:
+        # every other configuration, shorter runs (the headline target is the one above)
+        others = []
+        for wid, ulen in [(1, None), (2, None), (4, None), (5, None), (3, 4096)]:
+            if wid == args.workload and ulen == args.uniform_len:
+                continue
+            owl = W.WORKLOADS[wid]
+            _, ow, oms, okern, _ = measure(torch, attn, W, owl, ulen, 10, 3)
+            oflop = ow["fwd_flop"] + ow["bwd_flop"]
+            ov = oflop / (oms * 1e-3) / 1e12
+            others.append({"workload": owl.name + (f"_uniform{ulen}" if ulen else ""), "dtype": owl.dtype,
+                           "value": round(ov, 2), "unit": "TFLOP/s", "ms_per_step": round(oms, 4),
+                           "pct_of_peak": round(100 * ov / PEAK_TFLOPS[owl.dtype], 2),
+                           "visible_pairs": ow["pairs"], "kernels_ms": {n: round(t, 4) for n, t in okern.items()},
+                           "steps": 10, "warmup": 3})
+        result["other_workloads"] = others
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)
