@@ -29,6 +29,8 @@ from .attention import (  # noqa: F401
     attention_forward,
     attention_backward,
     attention_group,
+    attention_backward_packed,
+    offsets_per_sequence,
     scores,
     masked_softmax,
     score_grad,

@@ -16,11 +16,15 @@ reader can check each line against the equations named beside it.
 
 Readings of points the pages leave open (each is also listed in the design doc):
   * visible set of row i of sequence b:
-        V_i = { j : j < L_k[b]  and  (not causal  or  j <= i + offset) }
+        V_i = { j : j < L_k[b]  and  (not causal  or  j <= i + offset_b) }
     for active rows i < L_q[b]; 0-based indices.  The causal set {j <= i} is
     [A.10, sec. A.10.6]; the offset generalises the top-left rule of the
     [by-hand] exercise `causal_attention` (which defers offsets); padding
-    removal is [A.10, sec. A.10.6].
+    removal is [A.10, sec. A.10.6].  offset_b is one value for the batch or
+    one per sequence (each sequence's own cached history, [ch.31, sec. 1]).
+  * packed layout: the sequences' rows stored one after another with no
+    padding (row offsets cu_seqlens); sequence b is exactly the padded
+    problem restricted to its own L_q[b] rows and L_k[b] keys.
   * rows i >= L_q[b] are inactive padding rows: O = 0, lse = 0, G_Q = 0 and
     they contribute nothing to G_K / G_V.
   * an ACTIVE row with an empty visible set is rejected ([A.10, sec. A.10.1]
@@ -90,8 +94,18 @@ def _lengths(lens, B: int, n: int, what: str) -> list[int]:
     return lens
 
 
+def offsets_per_sequence(offset, B: int) -> list[int]:
+    """The causal offset of every sequence: one int for all, or B values."""
+    if np.ndim(offset) == 0:
+        return [int(offset)] * B
+    offs = [int(x) for x in offset]
+    if len(offs) != B:
+        raise InvalidArgument(f"offset: expected {B} per-sequence values, got {len(offs)}")
+    return offs
+
+
 def validate(B: int, H_q: int, H_kv: int, n_q: int, n_k: int,
-             causal: bool, offset: int, seqlens_q=None, seqlens_k=None):
+             causal: bool, offset, seqlens_q=None, seqlens_k=None):
     """Resolve the per-sequence lengths and reject undefined problems.
 
     Returns (L_q, L_k) as lists.  Raises InvalidArgument for inconsistent
@@ -104,8 +118,9 @@ def validate(B: int, H_q: int, H_kv: int, n_q: int, n_k: int,
         raise InvalidArgument("H_q must be a multiple of H_kv")
     L_q = _lengths(seqlens_q, B, n_q, "seqlens_q")
     L_k = _lengths(seqlens_k, B, n_k, "seqlens_k")
+    offs = offsets_per_sequence(offset, B)
     for b in range(B):
-        M = visible_mask(n_q, n_k, L_q[b], L_k[b], causal, offset)
+        M = visible_mask(n_q, n_k, L_q[b], L_k[b], causal, offs[b])
         counts = M.sum(axis=1)
         if np.any(counts[: L_q[b]] == 0):
             raise EmptyRow(f"sequence {b}: an active query row sees no key")
@@ -206,11 +221,12 @@ def attention_forward(Q, K, V, *, causal=False, offset=0,
     b*H_q + r) for inspection."""
     Q, K, V, (B, H_q, H_kv, n_q, n_k, d_h, d_v) = _shapes(Q, K, V)
     L_q, L_k = validate(B, H_q, H_kv, n_q, n_k, causal, offset, seqlens_q, seqlens_k)
+    offs = offsets_per_sequence(offset, B)
     O = np.zeros((B, H_q, n_q, d_v))
     lse = np.zeros((B, H_q, n_q))
     kept = {"S": [], "A": [], "M": []}
     for b in range(B):
-        M = visible_mask(n_q, n_k, L_q[b], L_k[b], causal, offset)
+        M = visible_mask(n_q, n_k, L_q[b], L_k[b], causal, offs[b])
         for r in range(H_q):
             g = kv_group(r, H_q, H_kv)
             f = head_forward(Q[b, r], K[b, g], V[b, g], M)
@@ -236,6 +252,7 @@ def attention_backward(Q, K, V, GO, *, causal=False, offset=0,
     if GO.shape != (B, H_q, n_q, d_v):
         raise InvalidArgument("G_O must have the shape of O")
     L_q, L_k = validate(B, H_q, H_kv, n_q, n_k, causal, offset, seqlens_q, seqlens_k)
+    offs = offsets_per_sequence(offset, B)
     O = np.zeros((B, H_q, n_q, d_v))
     lse = np.zeros((B, H_q, n_q))
     c = np.zeros((B, H_q, n_q))
@@ -244,7 +261,7 @@ def attention_backward(Q, K, V, GO, *, causal=False, offset=0,
     GV = np.zeros_like(V)
     kept = {"S": [], "A": [], "GS": [], "M": []}
     for b in range(B):
-        M = visible_mask(n_q, n_k, L_q[b], L_k[b], causal, offset)
+        M = visible_mask(n_q, n_k, L_q[b], L_k[b], causal, offs[b])
         for r in range(H_q):
             g = kv_group(r, H_q, H_kv)
             f = head_forward(Q[b, r], K[b, g], V[b, g], M)
@@ -276,7 +293,7 @@ def attention_group(Q, K, V, GO, b: int, g: int, *, causal=False, offset=0,
     B, H_q, n_q, d_h = Q.shape
     _, H_kv, n_k, d_v = V.shape
     L_q, L_k = validate(B, H_q, H_kv, n_q, n_k, causal, offset, seqlens_q, seqlens_k)
-    M = visible_mask(n_q, n_k, L_q[b], L_k[b], causal, offset)
+    M = visible_mask(n_q, n_k, L_q[b], L_k[b], causal, offsets_per_sequence(offset, B)[b])
     heads = [r for r in range(H_q) if kv_group(r, H_q, H_kv) == g]
     k = np.asarray(K[b, g], dtype=np.float64)
     v = np.asarray(V[b, g], dtype=np.float64)
@@ -296,3 +313,68 @@ def attention_group(Q, K, V, GO, b: int, g: int, *, causal=False, offset=0,
     for key in ("O", "lse", "GQ", "D"):
         out[key] = np.stack(out[key]) if out[key] else None
     return out
+
+
+# ----------------------------------------------------------------------------
+# packed ("varlen") layout
+# ----------------------------------------------------------------------------
+
+def _cu_lengths(cu, what: str) -> tuple[list[int], list[int]]:
+    cu = [int(x) for x in cu]
+    if len(cu) < 1 or cu[0] != 0:
+        raise InvalidArgument(f"{what}: row offsets must start at 0")
+    lens = [cu[i + 1] - cu[i] for i in range(len(cu) - 1)]
+    if any(x < 0 for x in lens):
+        raise InvalidArgument(f"{what}: row offsets must not decrease")
+    return cu, lens
+
+
+def attention_backward_packed(Q, K, V, GO, cu_seqlens_q, cu_seqlens_k, *, causal=False, offset=0) -> dict:
+    """Forward and backward with the sequences packed one after another.
+
+    Q [total_q, H_q, d_h], K [total_k, H_kv, d_h], V [total_k, H_kv, d_v],
+    GO [total_q, H_q, d_v]; sequence b owns rows cu_seqlens_q[b] ..
+    cu_seqlens_q[b+1]-1 of Q/GO and cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1 of
+    K/V.  Each sequence is computed on its own rows only (the padded
+    definition above with B = 1 and n = its lengths, so no row of one
+    sequence can reach another).  GO may be None (forward only).
+
+    Returns O, GQ [total_q, H_q, .], GK, GV [total_k, H_kv, .], and lse, D
+    [H_q, total_q]."""
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    cu_q, L_q = _cu_lengths(cu_seqlens_q, "cu_seqlens_q")
+    cu_k, L_k = _cu_lengths(cu_seqlens_k, "cu_seqlens_k")
+    B = len(L_q)
+    if len(L_k) != B:
+        raise InvalidArgument("cu_seqlens_q and cu_seqlens_k must describe the same sequences")
+    if Q.shape[0] < cu_q[-1] or K.shape[0] < cu_k[-1] or V.shape[0] < cu_k[-1]:
+        raise InvalidArgument("row offsets beyond the packed tensors")
+    offs = offsets_per_sequence(offset, B)
+    H_q, d_h = Q.shape[1], Q.shape[2]
+    H_kv, d_v = V.shape[1], V.shape[2]
+    O = np.zeros((Q.shape[0], H_q, d_v))
+    GQ = np.zeros_like(Q)
+    GK = np.zeros_like(K)
+    GV = np.zeros_like(V)
+    lse = np.zeros((H_q, Q.shape[0]))
+    D = np.zeros((H_q, Q.shape[0]))
+    for b in range(B):
+        qs, ks = slice(cu_q[b], cu_q[b + 1]), slice(cu_k[b], cu_k[b + 1])
+        # [rows, H, d] -> [1, H, rows, d]
+        q = Q[qs].transpose(1, 0, 2)[None]
+        k = K[ks].transpose(1, 0, 2)[None]
+        v = V[ks].transpose(1, 0, 2)[None]
+        if GO is None:
+            f = attention_forward(q, k, v, causal=causal, offset=offs[b])
+        else:
+            go = np.asarray(GO, dtype=np.float64)[qs].transpose(1, 0, 2)[None]
+            f = attention_backward(q, k, v, go, causal=causal, offset=offs[b])
+            GQ[qs] = f["GQ"][0].transpose(1, 0, 2)
+            GK[ks] = f["GK"][0].transpose(1, 0, 2)
+            GV[ks] = f["GV"][0].transpose(1, 0, 2)
+            D[:, qs] = f["D"][0]
+        O[qs] = f["O"][0].transpose(1, 0, 2)
+        lse[:, qs] = f["lse"][0]
+    return {"O": O, "lse": lse, "GQ": GQ, "GK": GK, "GV": GV, "D": D}

@@ -144,6 +144,8 @@ MASK_CASES = [
     dict(name="keypad", n_q=5, n_k=7, causal=False, offset=0, lq=None, lk=[7, 3]),
     dict(name="rowpad_causal", n_q=6, n_k=6, causal=True, offset=0, lq=[6, 4], lk=[6, 4]),
     dict(name="nonsquare_offset_pad", n_q=3, n_k=9, causal=True, offset=5, lq=[3, 2], lk=[9, 6]),
+    # one causal offset per sequence (each sequence's own cached history)
+    dict(name="per_sequence_offsets", n_q=4, n_k=8, causal=True, offset=[1, 4], lq=None, lk=[8, 6]),
 ]
 
 
@@ -219,12 +221,13 @@ def test_matches_torch_autograd(case):
     v = torch.tensor(V, requires_grad=True)
     mask = torch.zeros(B, 1, n_q, n_k, dtype=torch.bool)
     lk = kw["seqlens_k"] or [n_k] * B
+    offs = kw["offset"] if isinstance(kw["offset"], list) else [kw["offset"]] * B
     for b in range(B):
         i = torch.arange(n_q)[:, None]
         j = torch.arange(n_k)[None, :]
         m = j < lk[b]
         if kw["causal"]:
-            m = m & (j <= i + kw["offset"])
+            m = m & (j <= i + offs[b])
         mask[b, 0] = m
     o = torch.nn.functional.scaled_dot_product_attention(
         q, k.repeat_interleave(grp, dim=1), v.repeat_interleave(grp, dim=1), attn_mask=mask)
