@@ -10,6 +10,9 @@ no fallback: if the library is missing, every call raises.
 
 Tensors are [B, H, n, d] with unit stride in d (any batch/head/row strides that
 are multiples of 8 elements), dtype torch.bfloat16 or torch.float32, on the GPU.
+``offset`` is one causal offset for every sequence or a list of B of them.
+Packed ("varlen") sequences: pass cu_seqlens_q / cu_seqlens_k (B + 1 row
+offsets) and tensors [total_rows, H, d]; lse is then [H_q, total_q_rows].
 """
 
 from __future__ import annotations
@@ -47,7 +50,8 @@ class Mask(ctypes.Structure):
     _fields_ = [("causal", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("causal_offset", ctypes.c_int64),
                 ("seqlens_q", ctypes.POINTER(ctypes.c_int32)),
-                ("seqlens_k", ctypes.POINTER(ctypes.c_int32))]
+                ("seqlens_k", ctypes.POINTER(ctypes.c_int32)),
+                ("causal_offsets", ctypes.POINTER(ctypes.c_int64))]
 
 
 class Problem(ctypes.Structure):
@@ -55,7 +59,9 @@ class Problem(ctypes.Structure):
                 ("n_q", ctypes.c_int32), ("n_k", ctypes.c_int32),
                 ("d_h", ctypes.c_int32), ("d_v", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3),
-                ("v_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3)]
+                ("v_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3),
+                ("cu_seqlens_q", ctypes.POINTER(ctypes.c_int32)),
+                ("cu_seqlens_k", ctypes.POINTER(ctypes.c_int32))]
 
 
 _LIB = None
@@ -104,27 +110,54 @@ def status_string(status: int) -> str:
 # problem / mask construction (plain integers; usable without a GPU)
 # ---------------------------------------------------------------------------
 
+def _i32_array(vals):
+    arr = (ctypes.c_int32 * len(vals))(*[int(x) for x in vals])
+    return arr, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32))
+
+
 def make_problem(B, H_q, H_kv, n_q, n_k, d_h, d_v, dtype, q_stride=None, k_stride=None,
-                 v_stride=None, o_stride=None) -> Problem:
+                 v_stride=None, o_stride=None, cu_seqlens_q=None, cu_seqlens_k=None) -> Problem:
+    """With cu_seqlens_q / cu_seqlens_k (B + 1 row offsets each) the problem is in
+    the packed layout: default strides are then those of contiguous
+    [total_rows, H, d] tensors (batch stride 0).  The returned Problem keeps
+    its host arrays alive (attribute ``_keep``)."""
+    packed = cu_seqlens_q is not None or cu_seqlens_k is not None
+
     def contig(H, n, d):
-        return (H * n * d, n * d, d)
+        return (0, d, H * d) if packed else (H * n * d, n * d, d)
     p = Problem()
     p.B, p.H_q, p.H_kv, p.n_q, p.n_k, p.d_h, p.d_v, p.dtype = B, H_q, H_kv, n_q, n_k, d_h, d_v, dtype
     p.q_stride[:] = q_stride or contig(H_q, n_q, d_h)
     p.k_stride[:] = k_stride or contig(H_kv, n_k, d_h)
     p.v_stride[:] = v_stride or contig(H_kv, n_k, d_v)
     p.o_stride[:] = o_stride or contig(H_q, n_q, d_v)
+    p._keep = []
+    for name, cu in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if cu is None:
+            setattr(p, name, None)
+        else:
+            arr, ptr = _i32_array(cu)
+            p._keep.append(arr)
+            setattr(p, name, ptr)
     return p
 
 
 def make_mask(causal=False, offset=0, seqlens_q: Optional[Sequence[int]] = None,
               seqlens_k: Optional[Sequence[int]] = None):
-    """Returns (Mask, keepalive) -- the host length arrays must outlive the call."""
+    """Returns (Mask, keepalive) -- the host arrays must outlive the call.
+    ``offset``: one causal offset, or a sequence of per-sequence offsets."""
     m = Mask()
     m.causal = 1 if causal else 0
     m.reserved = 0
-    m.causal_offset = int(offset)
     keep = []
+    if isinstance(offset, (int,)) or (hasattr(offset, "ndim") and offset.ndim == 0):
+        m.causal_offset = int(offset)
+        m.causal_offsets = None
+    else:
+        m.causal_offset = 0
+        arr = (ctypes.c_int64 * len(offset))(*[int(x) for x in offset])
+        keep.append(arr)
+        m.causal_offsets = ctypes.cast(arr, ctypes.POINTER(ctypes.c_int64))
     for name, lens in (("seqlens_q", seqlens_q), ("seqlens_k", seqlens_k)):
         if lens is None:
             setattr(m, name, None)
@@ -161,9 +194,9 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
-def _check4(name, t, dtype):
-    if t.dim() != 4:
-        raise ValueError(f"{name} must be [B, H, n, d]")
+def _check4(name, t, dtype, ndim=4):
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must be " + ("[B, H, n, d]" if ndim == 4 else "[rows, H, d]"))
     if t.dtype != dtype:
         raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
     if not t.is_cuda:
@@ -173,6 +206,10 @@ def _check4(name, t, dtype):
 
 
 def _strides(t):
+    """ABI strides (batch, head, row): [B, H, n, d] tensors directly, packed
+    [rows, H, d] tensors with batch stride 0."""
+    if t.dim() == 3:
+        return (0, int(t.stride(1)), int(t.stride(0)))
     return tuple(int(s) for s in t.stride()[:3])
 
 
@@ -180,11 +217,30 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else ctypes.c_void_p(0)
 
 
-def _problem_from(q, k, v, o_like_stride=None):
-    B, H_q, n_q, d_h = q.shape
-    _, H_kv, n_k, d_v = v.shape
-    return make_problem(B, H_q, H_kv, n_q, n_k, d_h, d_v, _dtype_code(q), _strides(q), _strides(k),
-                        _strides(v), o_like_stride)
+def _packed_lengths(cu):
+    cu = [int(x) for x in cu]
+    return cu, [cu[i + 1] - cu[i] for i in range(len(cu) - 1)]
+
+
+def _problem_from(q, k, v, o_like_stride=None, cu_seqlens_q=None, cu_seqlens_k=None,
+                  max_seqlen_q=None, max_seqlen_k=None):
+    if cu_seqlens_q is None and cu_seqlens_k is None:
+        B, H_q, n_q, d_h = q.shape
+        _, H_kv, n_k, d_v = v.shape
+        return make_problem(B, H_q, H_kv, n_q, n_k, d_h, d_v, _dtype_code(q), _strides(q), _strides(k),
+                            _strides(v), o_like_stride)
+    if cu_seqlens_q is None or cu_seqlens_k is None:
+        raise ValueError("the packed layout needs both cu_seqlens_q and cu_seqlens_k")
+    cu_q, lq = _packed_lengths(cu_seqlens_q)
+    cu_k, lk = _packed_lengths(cu_seqlens_k)
+    if len(cu_q) != len(cu_k) or len(cu_q) < 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold B + 1 offsets")
+    _, H_q, d_h = q.shape
+    _, H_kv, d_v = v.shape
+    n_q = int(max_seqlen_q) if max_seqlen_q is not None else max(lq, default=0)
+    n_k = int(max_seqlen_k) if max_seqlen_k is not None else max(lk, default=0)
+    return make_problem(len(cu_q) - 1, H_q, H_kv, n_q, n_k, d_h, d_v, _dtype_code(q), _strides(q),
+                        _strides(k), _strides(v), o_like_stride, cu_q, cu_k)
 
 
 def _stream(stream):
@@ -194,21 +250,29 @@ def _stream(stream):
 
 
 def fwd(q, k, v, *, causal=False, offset=0, seqlens_q=None, seqlens_k=None, out=None, lse=None,
-        stream=None):
-    """O [B,H_q,n_q,d_v] (dtype of q) and lse [B,H_q,n_q] float32."""
+        stream=None, cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None):
+    """O (dtype of q) and float32 lse: [B,H_q,n_q,d_v] and [B,H_q,n_q], or in
+    the packed layout [total_q,H_q,d_v] and [H_q,total_q]."""
     torch = _torch()
+    packed = cu_seqlens_q is not None or cu_seqlens_k is not None
+    nd = 3 if packed else 4
     for name, t in (("q", q), ("k", k), ("v", v)):
-        _check4(name, t, q.dtype)
-    B, H_q, n_q, _ = q.shape
+        _check4(name, t, q.dtype, nd)
     d_v = v.shape[-1]
+    if packed:
+        total_q, H_q, _ = q.shape
+        o_shape, lse_shape = (total_q, H_q, d_v), (H_q, total_q)
+    else:
+        B, H_q, n_q, _ = q.shape
+        o_shape, lse_shape = (B, H_q, n_q, d_v), (B, H_q, n_q)
     if out is None:
-        out = torch.empty(B, H_q, n_q, d_v, dtype=q.dtype, device=q.device)
+        out = torch.empty(*o_shape, dtype=q.dtype, device=q.device)
     if lse is None:
-        lse = torch.empty(B, H_q, n_q, dtype=torch.float32, device=q.device)
-    _check4("out", out, q.dtype)
-    if not lse.is_contiguous() or lse.dtype != torch.float32:
-        raise ValueError("lse must be contiguous float32")
-    prob = _problem_from(q, k, v, _strides(out))
+        lse = torch.empty(*lse_shape, dtype=torch.float32, device=q.device)
+    _check4("out", out, q.dtype, nd)
+    if not lse.is_contiguous() or lse.dtype != torch.float32 or tuple(lse.shape) != lse_shape:
+        raise ValueError(f"lse must be contiguous float32 of shape {lse_shape}")
+    prob = _problem_from(q, k, v, _strides(out), cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
     mask, keep = make_mask(causal, offset, seqlens_q, seqlens_k)
     st = lib().attn_fwd(ctypes.byref(prob), ctypes.byref(mask), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                         _ptr(lse), _stream(stream))
@@ -219,12 +283,14 @@ def fwd(q, k, v, *, causal=False, offset=0, seqlens_q=None, seqlens_k=None, out=
 
 
 def bwd(q, k, v, o, lse, do, *, causal=False, offset=0, seqlens_q=None, seqlens_k=None,
-        dq=None, dk=None, dv=None, workspace=None, stream=None):
+        dq=None, dk=None, dv=None, workspace=None, stream=None, cu_seqlens_q=None, cu_seqlens_k=None,
+        max_seqlen_q=None, max_seqlen_k=None):
     """G_Q, G_K, G_V.  ``do`` must have the strides of ``o``; outputs are
     allocated contiguous unless given (then with the strides of q / k / v)."""
     torch = _torch()
+    nd = 3 if (cu_seqlens_q is not None or cu_seqlens_k is not None) else 4
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
-        _check4(name, t, q.dtype)
+        _check4(name, t, q.dtype, nd)
     if do.stride() != o.stride():
         raise ValueError("do must have the strides of o")
     if dq is None:
@@ -239,7 +305,7 @@ def bwd(q, k, v, o, lse, do, *, causal=False, offset=0, seqlens_q=None, seqlens_
         dv = torch.empty_like(v)
         if dv.stride() != v.stride():
             raise ValueError("v must be contiguous when dv is not given")
-    prob = _problem_from(q, k, v, _strides(o))
+    prob = _problem_from(q, k, v, _strides(o), cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
     need = workspace_size(prob)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
@@ -258,14 +324,17 @@ class StagedBackward:
     time or schedule them separately (dq() then dkdv() equals one bwd())."""
 
     def __init__(self, q, k, v, o, lse, do, dq, dk, dv, workspace, *, causal=False, offset=0,
-                 seqlens_q=None, seqlens_k=None):
+                 seqlens_q=None, seqlens_k=None, cu_seqlens_q=None, cu_seqlens_k=None,
+                 max_seqlen_q=None, max_seqlen_k=None):
+        nd = 3 if (cu_seqlens_q is not None or cu_seqlens_k is not None) else 4
         for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do), ("dq", dq),
                         ("dk", dk), ("dv", dv)):
-            _check4(name, t, q.dtype)
+            _check4(name, t, q.dtype, nd)
         if do.stride() != o.stride() or dq.stride() != q.stride() or dk.stride() != k.stride() \
                 or dv.stride() != v.stride():
             raise ValueError("gradient strides must match their tensors")
-        self.prob = _problem_from(q, k, v, _strides(o))
+        self.prob = _problem_from(q, k, v, _strides(o), cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                                  max_seqlen_k)
         self.mask, self._keep = make_mask(causal, offset, seqlens_q, seqlens_k)
         self.t = (q, k, v, o, lse, do, dq, dk, dv, workspace)
         self.ws = _ptr(workspace)

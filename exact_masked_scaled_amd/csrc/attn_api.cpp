@@ -36,17 +36,37 @@ void fill_common(KernelParams& kp, const attn_problem& p, const attn_mask& m) {
   kp.offset = (int32_t)std::min<int64_t>(std::max<int64_t>(m.causal_offset, 0), p.n_k);
   kp.scale = (float)(1.0 / sqrt((double)p.d_h));
   kp.scale_log2 = (float)(1.4426950408889634 / sqrt((double)p.d_h));
-  kp.has_lens = (m.seqlens_q != nullptr || m.seqlens_k != nullptr) ? 1 : 0;
+  kp.varlen = p.cu_seqlens_q != nullptr ? 1 : 0;
+  kp.has_lens = (m.seqlens_q != nullptr || m.seqlens_k != nullptr || kp.varlen) ? 1 : 0;
+  kp.has_offs = (m.causal && m.causal_offsets != nullptr) ? 1 : 0;
+  if (kp.varlen) {  // lse / D: [H_q][total rows]; the row offsets carry the sequence
+    kp.lse_sb = 0;
+    kp.lse_sh = p.cu_seqlens_q[p.B];
+  } else {
+    kp.lse_sb = (int64_t)p.H_q * p.n_q;
+    kp.lse_sh = p.n_q;
+  }
 }
 
-// Sequence chunk [b0, b0 + nb): lengths and unit counts.
+int32_t clamp_offset(int64_t off, int32_t n_k) {
+  return (int32_t)std::min<int64_t>(std::max<int64_t>(off, 0), n_k);
+}
+
+// Sequence chunk [b0, b0 + nb): per-sequence data and unit counts.
 void fill_chunk(KernelParams& kp, const attn_problem& p, const attn_mask& m, int b0, int nb) {
   kp.B = nb;
-  if (kp.has_lens) {
-    for (int i = 0; i < nb; ++i) {
-      kp.lens_q[i] = m.seqlens_q ? m.seqlens_q[b0 + i] : p.n_q;
-      kp.lens_k[i] = m.seqlens_k ? m.seqlens_k[b0 + i] : p.n_k;
+  for (int i = 0; i < nb; ++i) {
+    const int b = b0 + i;
+    if (kp.varlen) {
+      kp.row0_q[i] = p.cu_seqlens_q[b];
+      kp.row0_k[i] = p.cu_seqlens_k[b];
+      kp.lens_q[i] = p.cu_seqlens_q[b + 1] - p.cu_seqlens_q[b];
+      kp.lens_k[i] = p.cu_seqlens_k[b + 1] - p.cu_seqlens_k[b];
+    } else if (kp.has_lens) {
+      kp.lens_q[i] = m.seqlens_q ? m.seqlens_q[b] : p.n_q;
+      kp.lens_k[i] = m.seqlens_k ? m.seqlens_k[b] : p.n_k;
     }
+    if (kp.has_offs) kp.offs[i] = clamp_offset(m.causal_offsets[b], p.n_k);
   }
   kp.groups = nb * p.H_kv;
   kp.xcd_map = (kp.groups % 8 == 0) ? 1 : 0;
@@ -61,7 +81,9 @@ T* off(T* base, int64_t elems, size_t es) {
   return base ? (T*)((char*)base + elems * (int64_t)es) : nullptr;
 }
 
-int chunk_size(const KernelParams& kp, int B) { return kp.has_lens ? kMaxBatchChunk : std::max(B, 1); }
+int chunk_size(const KernelParams& kp, int B) {
+  return (kp.has_lens || kp.has_offs) ? kMaxBatchChunk : std::max(B, 1);
+}
 
 }  // namespace
 
@@ -99,7 +121,7 @@ attn_status attn_fwd(const attn_problem* prob, const attn_mask* mask, const void
     kp.k = off(K, b0 * p.k_stride[0], es);
     kp.v = off(V, b0 * p.v_stride[0], es);
     kp.o_out = off(O, b0 * p.o_stride[0], es);
-    kp.lse = lse + (int64_t)b0 * p.H_q * p.n_q;
+    kp.lse = lse + b0 * kp.lse_sb;
     if (launch_fwd(kp, p.dtype, p.d_h, p.d_v, stream) != 0) return ATTN_ERR_HIP;
   }
   return ATTN_OK;
@@ -150,7 +172,7 @@ attn_status bwd_passes(const attn_problem* prob, const attn_mask* mask, const Bw
   for (int b0 = 0; b0 < p.B; b0 += cs) {
     const int nb = std::min(cs, p.B - b0);
     fill_chunk(kp, p, m, b0, nb);
-    const int64_t row0 = (int64_t)b0 * p.H_q * p.n_q;
+    const int64_t row0 = b0 * kp.lse_sb;
     kp.q = off(t.Q, b0 * p.q_stride[0], es);
     kp.k = off(t.K, b0 * p.k_stride[0], es);
     kp.v = off(t.V, b0 * p.v_stride[0], es);

@@ -68,20 +68,20 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(con
   const int r = g * p.group + item % p.group;
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, kg = lane >> 5;
-  const int Lq = p.has_lens ? p.lens_q[b] : p.n_q;
-  const int Lk = p.has_lens ? p.lens_k[b] : p.n_k;
+  const SeqView sv = seq_view(p, b);
+  const int Lq = sv.Lq, Lk = sv.Lk, off = sv.off, nk_lim = sv.nk_lim;
   const int q_lo = qb * C::BM;
   const int qi = q_lo + 32 * w + (lane & 31);
-  const bool row_exists = qi < p.n_q;
+  const bool row_exists = qi < sv.nq_lim;
   const bool row_active = qi < Lq;
 
-  const T* Qb = (const T*)p.q + b * p.q_sb + r * p.q_sh;
-  const T* Kb = (const T*)p.k + b * p.k_sb + g * p.k_sh;
-  const T* Vb = (const T*)p.v + b * p.v_sb + g * p.v_sh;
-  const T* Ob = (const T*)p.o + b * p.o_sb + r * p.o_sh;
-  const T* dOb = (const T*)p.dout + b * p.o_sb + r * p.o_sh;
-  T* dQb = (T*)p.dq + b * p.q_sb + r * p.q_sh;
-  const int64_t rowbase = ((int64_t)b * p.H_q + r) * p.n_q;
+  const T* Qb = (const T*)p.q + b * p.q_sb + sv.q_row0 * p.q_sr + r * p.q_sh;
+  const T* Kb = (const T*)p.k + b * p.k_sb + sv.k_row0 * p.k_sr + g * p.k_sh;
+  const T* Vb = (const T*)p.v + b * p.v_sb + sv.k_row0 * p.v_sr + g * p.v_sh;
+  const T* Ob = (const T*)p.o + b * p.o_sb + sv.q_row0 * p.o_sr + r * p.o_sh;
+  const T* dOb = (const T*)p.dout + b * p.o_sb + sv.q_row0 * p.o_sr + r * p.o_sh;
+  T* dQb = (T*)p.dq + b * p.q_sb + sv.q_row0 * p.q_sr + r * p.q_sh;
+  const int64_t rowbase = b * p.lse_sb + r * p.lse_sh + sv.q_row0;
 
   // this lane's G_O row (B operand of dP^T = V G_O^T) and D_i = G_O . O
   op_t doreg[DV / 16];
@@ -104,12 +104,12 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(con
   const int act_hi = min(q_lo + C::BM, Lq);
   int ntiles = 0, nfull = 0;
   if (act_hi > q_lo) {
-    ntiles = (key_limit_b(act_hi - 1, Lk, p.causal, p.offset) + C::BN - 1) / C::BN;
-    nfull = key_limit_b(q_lo, Lk, p.causal, p.offset) / C::BN;
+    ntiles = (key_limit_b(act_hi - 1, Lk, p.causal, off) + C::BN - 1) / C::BN;
+    nfull = key_limit_b(q_lo, Lk, p.causal, off) / C::BN;
   }
   const int w_lo = q_lo + 32 * w, w_hi = min(w_lo + 32, Lq);
-  const int wtiles = w_hi > w_lo ? (key_limit_b(w_hi - 1, Lk, p.causal, p.offset) + C::BN - 1) / C::BN : 0;
-  const int kmax_lane = key_limit_b(qi, Lk, p.causal, p.offset);
+  const int wtiles = w_hi > w_lo ? (key_limit_b(w_hi - 1, Lk, p.causal, off) + C::BN - 1) / C::BN : 0;
+  const int kmax_lane = key_limit_b(qi, Lk, p.causal, off);
 
   f32x16 acc[DH / 32];
 #pragma unroll
@@ -177,23 +177,23 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(con
 
     using KL = TileLoad<T, C::BN, DH, 64 * C::NW>;
     using VL = TileLoad<T, C::BN, DV, 64 * C::NW>;
-    KL::issue(Kb, p.k_sr, 0, p.n_k, k_lds0, tid);
-    VL::issue(Vb, p.v_sr, 0, p.n_k, v_lds0, tid);
+    KL::issue(Kb, p.k_sr, 0, nk_lim, k_lds0, tid);
+    VL::issue(Vb, p.v_sr, 0, nk_lim, v_lds0, tid);
     wait_tile_loads();
     __syncthreads();
     // two tiles per trip so each LDS buffer address is a compile-time constant
     for (int t = 0; t < ntiles; t += 2) {
       if (t + 1 < ntiles) {
-        KL::issue(Kb, p.k_sr, (t + 1) * C::BN, p.n_k, k_lds1, tid);
-        VL::issue(Vb, p.v_sr, (t + 1) * C::BN, p.n_k, v_lds1, tid);
+        KL::issue(Kb, p.k_sr, (t + 1) * C::BN, nk_lim, k_lds1, tid);
+        VL::issue(Vb, p.v_sr, (t + 1) * C::BN, nk_lim, v_lds1, tid);
       }
       if (t < wtiles) tile(t, k_lds0, v_lds0);
       wait_tile_loads();
       __syncthreads();
       if (t + 1 >= ntiles) break;
       if (t + 2 < ntiles) {
-        KL::issue(Kb, p.k_sr, (t + 2) * C::BN, p.n_k, k_lds0, tid);
-        VL::issue(Vb, p.v_sr, (t + 2) * C::BN, p.n_k, v_lds0, tid);
+        KL::issue(Kb, p.k_sr, (t + 2) * C::BN, nk_lim, k_lds0, tid);
+        VL::issue(Vb, p.v_sr, (t + 2) * C::BN, nk_lim, v_lds0, tid);
       }
       if (t + 1 < wtiles) tile(t + 1, k_lds1, v_lds1);
       wait_tile_loads();
@@ -256,15 +256,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const KernelParams p) 
   if (!map_work(blockIdx.x, p.groups, p.per_group, p.xcd_map, unit, kb)) return;
   const int b = unit / p.H_kv, g = unit - (unit / p.H_kv) * p.H_kv;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, kg = lane >> 5;
-  const int Lq = p.has_lens ? p.lens_q[b] : p.n_q;
-  const int Lk = p.has_lens ? p.lens_k[b] : p.n_k;
+  const SeqView sv = seq_view(p, b);
+  const int Lq = sv.Lq, Lk = sv.Lk, off = sv.off, nk_lim = sv.nk_lim;
   const int k_lo = kb * C::BN;
   const int kw0 = k_lo + 32 * KT * w;                 // first key of this wave
 
-  const T* Kb = (const T*)p.k + b * p.k_sb + g * p.k_sh;
-  const T* Vb = (const T*)p.v + b * p.v_sb + g * p.v_sh;
-  T* dKb = (T*)p.dk + b * p.k_sb + g * p.k_sh;
-  T* dVb = (T*)p.dv + b * p.v_sb + g * p.v_sh;
+  const T* Kb = (const T*)p.k + b * p.k_sb + sv.k_row0 * p.k_sr + g * p.k_sh;
+  const T* Vb = (const T*)p.v + b * p.v_sb + sv.k_row0 * p.v_sr + g * p.v_sh;
+  T* dKb = (T*)p.dk + b * p.k_sb + sv.k_row0 * p.k_sr + g * p.k_sh;
+  T* dVb = (T*)p.dv + b * p.v_sb + sv.k_row0 * p.v_sr + g * p.v_sh;
 
   f32x16 dk[KT][DH / 32], dv[KT][DV / 32];
 #pragma unroll
@@ -280,7 +280,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const KernelParams p) 
   }
 
   // rows that see any key of this block: causal j <= i + off  =>  i >= k_lo - off
-  const int q_first = p.causal ? max(0, k_lo - p.offset) : 0;
+  const int q_first = p.causal ? max(0, k_lo - off) : 0;
   const int qb_first = q_first / C::BM;
   const int qb_end = (Lq + C::BM - 1) / C::BM;
   const int nq = k_lo < Lk && qb_first < qb_end ? qb_end - qb_first : 0;
@@ -292,7 +292,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const KernelParams p) 
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
       const int key = kw0 + 32 * kt + (lane & 31);
-      const bool ok = key < p.n_k;
+      const bool ok = key < nk_lim;
 #pragma unroll
       for (int ks = 0; ks < DH / 16; ++ks)
         kreg[kt][ks] = ok ? ld8<T>(Kb + (int64_t)key * p.k_sr + 16 * ks + 8 * kg) : zero_op<T>();
@@ -312,11 +312,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const KernelParams p) 
     // waves issue the same number of copies and each reads only its own slot.
     // (everything the copies need is read from the kernel arguments once,
     // here, so no argument load sits behind the copies in the memory queue)
-    const T* const q_base = (const T*)p.q + b * p.q_sb;
-    const T* const o_base = (const T*)p.dout + b * p.o_sb;
-    const float* const rows_base = (lane < 32 ? p.lse : p.delta) + (int64_t)b * p.H_q * p.n_q;
-    const int64_t q_sh = p.q_sh, o_sh = p.o_sh, q_sr = p.q_sr, o_sr = p.o_sr;
-    const int n_q = p.n_q, group = p.group;
+    const T* const q_base = (const T*)p.q + b * p.q_sb + sv.q_row0 * p.q_sr;
+    const T* const o_base = (const T*)p.dout + b * p.o_sb + sv.q_row0 * p.o_sr;
+    const float* const rows_base = (lane < 32 ? p.lse : p.delta) + b * p.lse_sb + sv.q_row0;
+    const int64_t q_sh = p.q_sh, o_sh = p.o_sh, q_sr = p.q_sr, o_sr = p.o_sr, r_sh = p.lse_sh;
+    // rows present in memory (copies of rows beyond repeat the last one)
+    const int n_q = sv.nq_lim, group = p.group;
     auto issue = [&](int s, int st) {
       const int rr = s / nq, qb = qb_first + s % nq;
       const int r = g * group + rr;
@@ -324,7 +325,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const KernelParams p) 
       QL::issue(q_base + r * q_sh, q_sr, q0, n_q, q_st(st), tid);
       OL::issue(o_base + r * o_sh, o_sr, q0, n_q, o_st(st), tid);
       const int qq = min(q0 + (lane & 31), n_q - 1);
-      load_lane_floats(rows_base + (int64_t)r * n_q + qq, r_st(st) + w * 2 * C::BM);
+      load_lane_floats(rows_base + (int64_t)r * r_sh + qq, r_st(st) + w * 2 * C::BM);
     };
 
     // per-lane LDS offsets (Q and G_O tiles share them when d_h == d_v)
@@ -393,7 +394,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const KernelParams p) 
 
       // P = exp(S/sqrt(d) - lse) on the visible set and G_S = P o (dP - D);
       // register e holds query q0 + 8*(e/4) + 4*kg + e%4
-      const bool full = (q0 + C::BM <= Lq) && (wk_hi <= Lk) && (!p.causal || wk_hi - 1 <= q0 + p.offset);
+      const bool full = (q0 + C::BM <= Lq) && (wk_hi <= Lk) && (!p.causal || wk_hi - 1 <= q0 + off);
       if (full) {
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt)
@@ -404,7 +405,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const KernelParams p) 
             dp[kt][e] = pv * (dp[kt][e] - d4[e >> 2][e & 3]);
           }
       } else {
-        const int off_eff = p.causal ? p.offset : p.n_k;  // j <= i + n_k always holds
+        const int off_eff = p.causal ? off : p.n_k;  // j <= i + n_k always holds
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) {
           const int key = kw0 + 32 * kt + (lane & 31);
@@ -487,14 +488,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const KernelParams p) 
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int key = kbase + 8 * (e >> 2) + 4 * kg + (e & 3);
-        if (key < p.n_k) dKb[(int64_t)key * p.k_sr + 32 * nt + (lane & 31)] = (T)(dk[kt][nt][e] * p.scale);
+        if (key < nk_lim) dKb[(int64_t)key * p.k_sr + 32 * nt + (lane & 31)] = (T)(dk[kt][nt][e] * p.scale);
       }
 #pragma unroll
     for (int nt = 0; nt < DV / 32; ++nt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int key = kbase + 8 * (e >> 2) + 4 * kg + (e & 3);
-        if (key < p.n_k) dVb[(int64_t)key * p.v_sr + 32 * nt + (lane & 31)] = (T)dv[kt][nt][e];
+        if (key < nk_lim) dVb[(int64_t)key * p.v_sr + 32 * nt + (lane & 31)] = (T)dv[kt][nt][e];
       }
   }
 }
@@ -577,16 +578,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, kg = lane >> 5;
   const int h = w & 1;                                   // key half
   const bool is_x = w < 4, is_s = (w & 2) == 0;          // XS / YV use P, XD / YK use G_S
-  const int Lq = p.has_lens ? p.lens_q[b] : p.n_q;
-  const int Lk = p.has_lens ? p.lens_k[b] : p.n_k;
+  const SeqView sv = seq_view(p, b);
+  const int Lq = sv.Lq, Lk = sv.Lk, off = sv.off, nk_lim = sv.nk_lim;
   const int k_lo = kb * C::BN;
   const int kh0 = k_lo + C::KH * h;                      // first key of the half
   const int kh_hi = kh0 + C::KH;
 
-  const T* Kb = (const T*)p.k + b * p.k_sb + g * p.k_sh;
-  const T* Vb = (const T*)p.v + b * p.v_sb + g * p.v_sh;
-  T* dKb = (T*)p.dk + b * p.k_sb + g * p.k_sh;
-  T* dVb = (T*)p.dv + b * p.v_sb + g * p.v_sh;
+  const T* Kb = (const T*)p.k + b * p.k_sb + sv.k_row0 * p.k_sr + g * p.k_sh;
+  const T* Vb = (const T*)p.v + b * p.v_sb + sv.k_row0 * p.v_sr + g * p.v_sh;
+  T* dKb = (T*)p.dk + b * p.k_sb + sv.k_row0 * p.k_sr + g * p.k_sh;
+  T* dVb = (T*)p.dv + b * p.v_sb + sv.k_row0 * p.v_sr + g * p.v_sh;
 
   // XS: R[0, KB_S) this lane's K rows of both 32-key blocks (operand
   //     kb2 * DH/16 + ks), R[NB_X - 4 + 2j + kb2] the S tile of parity j;
@@ -599,7 +600,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
     for (int e = 0; e < 16; ++e) R[i][e] = 0.f;
   constexpr int XB = C::NB_X - 4;  // first S / dP buffer block
 
-  const int q_first = p.causal ? max(0, k_lo - p.offset) : 0;
+  const int q_first = p.causal ? max(0, k_lo - off) : 0;
   const int qb_first = q_first / C::BM;
   const int qb_end = (Lq + C::BM - 1) / C::BM;
   const int nq = k_lo < Lk && qb_first < qb_end ? qb_end - qb_first : 0;
@@ -613,7 +614,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
         const int key = kh0 + 32 * kb2 + (lane & 31);
-        const bool ok = key < p.n_k;
+        const bool ok = key < nk_lim;
         const T* row = src + (int64_t)key * sr + 8 * kg;
         constexpr int NK = (DH > DV ? DH : DV) / 16;
 #pragma unroll
@@ -631,11 +632,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
     }
 
     // copies (Y waves): per-lane address parts fixed for the loop
-    const T* const q_base = (const T*)p.q + b * p.q_sb;
-    const T* const o_base = (const T*)p.dout + b * p.o_sb;
-    const int64_t q_sh = p.q_sh, o_sh = p.o_sh, q_sr = p.q_sr, o_sr = p.o_sr;
-    const int n_q = p.n_q, group = p.group;
-    const float* const rows_lane = (lane < 32 ? p.lse : p.delta) + (int64_t)b * p.H_q * n_q + (lane & 31);
+    const T* const q_base = (const T*)p.q + b * p.q_sb + sv.q_row0 * p.q_sr;
+    const T* const o_base = (const T*)p.dout + b * p.o_sb + sv.q_row0 * p.o_sr;
+    const int64_t q_sh = p.q_sh, o_sh = p.o_sh, q_sr = p.q_sr, o_sr = p.o_sr, r_sh = p.lse_sh;
+    // rows present in memory (copies of rows beyond repeat the last one)
+    const int n_q = sv.nq_lim, group = p.group;
+    const float* const rows_lane = (lane < 32 ? p.lse : p.delta) + b * p.lse_sb + sv.q_row0 + (lane & 31);
     const int yw = w & 3;  // copy slot of a Y wave
     int64_t c_off[C::JPW];
     int c_row[C::JPW];
@@ -676,7 +678,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
       }
       // every Y wave copies the same lse / D rows (keeps the per-wave count equal)
       const int qq = whole ? q0 : min(q0 + (lane & 31), n_q - 1) - (lane & 31);
-      load_lane_floats(rows_lane + (int64_t)r * n_q + qq, r_st(ST));
+      load_lane_floats(rows_lane + (int64_t)r * r_sh + qq, r_st(ST));
     };
 
     // LDS operand offsets, one table for all roles:
@@ -698,9 +700,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
       return *reinterpret_cast<const op_t*>(reinterpret_cast<const char*>(tile) + off);
     };
 
-    const int off_eff = p.causal ? p.offset : p.n_k;  // j <= i + n_k always holds
+    const int off_eff = p.causal ? off : p.n_k;  // j <= i + n_k always holds
     auto full_tile = [&](int q0) __attribute__((always_inline)) {
-      return (q0 + C::BM <= Lq) && (kh_hi <= Lk) && (!p.causal || kh_hi - 1 <= q0 + p.offset);
+      return (q0 + C::BM <= Lq) && (kh_hi <= Lk) && (!p.causal || kh_hi - 1 <= q0 + off);
     };
 
     // ---- XS: S of one step (both key blocks share each Q operand read)
@@ -935,7 +937,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int kk = kh0 + 32 * kb2 + 8 * (e >> 2) + 4 * kg + (e & 3);
-          if (kk < p.n_k) dst[(int64_t)kk * sr + 32 * nt + (lane & 31)] = (T)(R[kb2 * NT + nt][e] * sc);
+          if (kk < nk_lim) dst[(int64_t)kk * sr + 32 * nt + (lane & 31)] = (T)(R[kb2 * NT + nt][e] * sc);
         }
   };
   if (!is_x) {

@@ -20,6 +20,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "attn_internal.h"
+
 namespace attn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -324,6 +326,27 @@ __device__ __forceinline__ void load_lane_floats(const float* src, float* lds) {
 // round-robin, so slot `wg / 8` of XCD `wg % 8` takes the slot-th item of that
 // XCD's units, and all items of one unit share one XCD's L2.  Returns false
 // for the padding workgroups of a unit count that is not a multiple of 8.
+// Per-sequence quantities of sequence b of a launch.
+struct SeqView {
+  int Lq, Lk;          // active query rows, valid keys
+  int off;             // causal offset of the sequence (clamped to [0, n_k])
+  int nq_lim, nk_lim;  // rows of the sequence present in memory: n_q / n_k in
+                       // the padded layout, L_q / L_k in the packed one
+                       // (copies clamp to them, stores stop at them)
+  int64_t q_row0, k_row0;  // first row of the sequence (packed layout; else 0)
+};
+__device__ __forceinline__ SeqView seq_view(const KernelParams& p, int b) {
+  SeqView s;
+  s.Lq = p.has_lens ? p.lens_q[b] : p.n_q;
+  s.Lk = p.has_lens ? p.lens_k[b] : p.n_k;
+  s.off = p.has_offs ? p.offs[b] : p.offset;
+  s.nq_lim = p.varlen ? s.Lq : p.n_q;
+  s.nk_lim = p.varlen ? s.Lk : p.n_k;
+  s.q_row0 = p.varlen ? p.row0_q[b] : 0;
+  s.k_row0 = p.varlen ? p.row0_k[b] : 0;
+  return s;
+}
+
 __device__ __forceinline__ bool map_work(int wg, int groups, int per_group, int xcd_map,
                                          int& unit, int& item) {
   if (!xcd_map) {

@@ -56,27 +56,27 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(const 
   const int r = g * p.group + item % p.group;
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int Lq = p.has_lens ? p.lens_q[b] : p.n_q;
-  const int Lk = p.has_lens ? p.lens_k[b] : p.n_k;
+  const SeqView sv = seq_view(p, b);
+  const int Lq = sv.Lq, Lk = sv.Lk, off = sv.off;
   const int q_lo = qb * C::BM;
 
-  const T* Qb = (const T*)p.q + b * p.q_sb + r * p.q_sh;
-  const T* Kb = (const T*)p.k + b * p.k_sb + g * p.k_sh;
-  const T* Vb = (const T*)p.v + b * p.v_sb + g * p.v_sh;
-  T* Ob = (T*)p.o_out + b * p.o_sb + r * p.o_sh;
-  float* lse_b = p.lse + ((int64_t)b * p.H_q + r) * p.n_q;
+  const T* Qb = (const T*)p.q + b * p.q_sb + sv.q_row0 * p.q_sr + r * p.q_sh;
+  const T* Kb = (const T*)p.k + b * p.k_sb + sv.k_row0 * p.k_sr + g * p.k_sh;
+  const T* Vb = (const T*)p.v + b * p.v_sb + sv.k_row0 * p.v_sr + g * p.v_sh;
+  T* Ob = (T*)p.o_out + b * p.o_sb + sv.q_row0 * p.o_sr + r * p.o_sh;
+  float* lse_b = p.lse + b * p.lse_sb + r * p.lse_sh + sv.q_row0;
 
   const int qi = q_lo + 32 * w + (lane & 31);          // this lane's query row
   const int kg = lane >> 5;                            // k-group of the lane
-  const bool row_exists = qi < p.n_q;
+  const bool row_exists = qi < sv.nq_lim;
   const bool row_active = qi < Lq;
 
   // rows of the block that are active
   const int act_hi = min(q_lo + C::BM, Lq);            // exclusive
   int ntiles = 0, nfull = 0;
   if (act_hi > q_lo) {
-    const int kend = key_limit(act_hi - 1, Lk, p.causal, p.offset);
-    const int kfull = key_limit(q_lo, Lk, p.causal, p.offset);
+    const int kend = key_limit(act_hi - 1, Lk, p.causal, off);
+    const int kfull = key_limit(q_lo, Lk, p.causal, off);
     ntiles = (kend + C::BN - 1) / C::BN;
     nfull = kfull / C::BN;
   }
@@ -84,8 +84,9 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(const 
   const int w_lo = q_lo + 32 * w;
   const int w_hi = min(w_lo + 32, Lq);
   int wtiles = 0;
-  if (w_hi > w_lo) wtiles = (key_limit(w_hi - 1, Lk, p.causal, p.offset) + C::BN - 1) / C::BN;
-  const int kmax_lane = key_limit(qi, Lk, p.causal, p.offset);
+  if (w_hi > w_lo) wtiles = (key_limit(w_hi - 1, Lk, p.causal, off) + C::BN - 1) / C::BN;
+  const int kmax_lane = key_limit(qi, Lk, p.causal, off);
+  const int nk_lim = sv.nk_lim;
 
   f32x16 oacc[DV / 32];
 #pragma unroll
@@ -109,8 +110,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(const 
     // K/V tiles stream through two LDS buffers with direct global-to-LDS loads
     using KL = TileLoad<T, C::BN, DH, 64 * C::NW>;
     using VL = TileLoad<T, C::BN, DV, 64 * C::NW>;
-    KL::issue(Kb, p.k_sr, 0, p.n_k, k_lds0, tid);
-    VL::issue(Vb, p.v_sr, 0, p.n_k, v_lds0, tid);
+    KL::issue(Kb, p.k_sr, 0, nk_lim, k_lds0, tid);
+    VL::issue(Vb, p.v_sr, 0, nk_lim, v_lds0, tid);
     wait_tile_loads();
     __syncthreads();
 
@@ -182,16 +183,16 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(const 
     // two tiles per trip so each LDS buffer address is a compile-time constant
     for (int t = 0; t < ntiles; t += 2) {
       if (t + 1 < ntiles) {
-        KL::issue(Kb, p.k_sr, (t + 1) * C::BN, p.n_k, k_lds1, tid);
-        VL::issue(Vb, p.v_sr, (t + 1) * C::BN, p.n_k, v_lds1, tid);
+        KL::issue(Kb, p.k_sr, (t + 1) * C::BN, nk_lim, k_lds1, tid);
+        VL::issue(Vb, p.v_sr, (t + 1) * C::BN, nk_lim, v_lds1, tid);
       }
       if (t < wtiles) tile(t, k_lds0, v_lds0);
       wait_tile_loads();
       __syncthreads();
       if (t + 1 >= ntiles) break;
       if (t + 2 < ntiles) {
-        KL::issue(Kb, p.k_sr, (t + 2) * C::BN, p.n_k, k_lds0, tid);
-        VL::issue(Vb, p.v_sr, (t + 2) * C::BN, p.n_k, v_lds0, tid);
+        KL::issue(Kb, p.k_sr, (t + 2) * C::BN, nk_lim, k_lds0, tid);
+        VL::issue(Vb, p.v_sr, (t + 2) * C::BN, nk_lim, v_lds0, tid);
       }
       if (t + 1 < wtiles) tile(t + 1, k_lds1, v_lds1);
       wait_tile_loads();

@@ -9,10 +9,10 @@
 
 namespace attn {
 
-// Sequences per launch when per-sequence lengths are given: the lengths travel
-// by value in the kernel arguments (2 x 1 KiB), so longer batches are split
-// into several launches on the same stream.
-constexpr int kMaxBatchChunk = 256;
+// Sequences per launch when per-sequence data are given: lengths, offsets
+// and packed row starts travel by value in the kernel arguments (5 x 512 B),
+// so longer batches are split into several launches on the same stream.
+constexpr int kMaxBatchChunk = 128;
 
 // Everything a kernel needs, passed by value (__grid_constant__).
 struct KernelParams {
@@ -38,11 +38,17 @@ struct KernelParams {
   float scale;          // 1/sqrt(d_h)
   float scale_log2;     // log2(e)/sqrt(d_h)
   int32_t has_lens;     // 0: every row active, every key valid
+  int32_t has_offs;     // 1: per-sequence causal offsets in offs[]
+  int32_t varlen;       // 1: packed layout, sequence b starts at rows row0_q/k[b]
   int32_t groups;       // (b, kv-head) units of work
   int32_t per_group;    // work items per unit
   int32_t xcd_map;      // 1: unit u runs on XCD u % 8 (groups % 8 == 0)
+  int64_t lse_sb, lse_sh;  // element strides of lse and D: sequence, head (rows: 1)
   int32_t lens_q[kMaxBatchChunk];
   int32_t lens_k[kMaxBatchChunk];
+  int32_t offs[kMaxBatchChunk];    // causal offsets, clamped to [0, n_k]
+  int32_t row0_q[kMaxBatchChunk];  // packed layout: first row of each sequence
+  int32_t row0_k[kMaxBatchChunk];
 };
 
 // Host-only validation; pure C++ (no HIP), shared by attn_validate/fwd/bwd.

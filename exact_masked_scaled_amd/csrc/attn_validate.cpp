@@ -7,7 +7,7 @@
 // such rows are rejected, as "Chapter 31: attention backpropagation"
 // (eonloom handbook), sec. 3 does.  Row 0 has the smallest visible set of its
 // sequence, so the check is O(B): every sequence with an active row needs
-// L_k[b] >= 1 and, under the causal rule, offset >= 0.
+// L_k[b] >= 1 and, under the causal rule, its offset >= 0.
 #include <stdint.h>
 
 #include "attn_internal.h"
@@ -39,14 +39,33 @@ attn_status validate_problem(const attn_problem* prob, const attn_mask* mask) {
   const attn_mask& m = *mask;
   if (m.causal != 0 && m.causal != 1) return ATTN_ERR_INVALID_ARG;
   if (m.reserved != 0) return ATTN_ERR_INVALID_ARG;
+  // packed layout: both row-offset arrays, no per-sequence lengths besides
+  // them, no batch strides, monotone offsets starting at 0
+  const bool packed = p.cu_seqlens_q != nullptr || p.cu_seqlens_k != nullptr;
+  if (packed) {
+    if (p.cu_seqlens_q == nullptr || p.cu_seqlens_k == nullptr) return ATTN_ERR_INVALID_ARG;
+    if (m.seqlens_q != nullptr || m.seqlens_k != nullptr) return ATTN_ERR_INVALID_ARG;
+    if (p.q_stride[0] != 0 || p.k_stride[0] != 0 || p.v_stride[0] != 0 || p.o_stride[0] != 0)
+      return ATTN_ERR_INVALID_ARG;
+    if (p.cu_seqlens_q[0] != 0 || p.cu_seqlens_k[0] != 0) return ATTN_ERR_INVALID_ARG;
+  }
   for (int b = 0; b < p.B; ++b) {
-    const int64_t lq = m.seqlens_q ? (int64_t)m.seqlens_q[b] : (int64_t)p.n_q;
-    const int64_t lk = m.seqlens_k ? (int64_t)m.seqlens_k[b] : (int64_t)p.n_k;
+    int64_t lq, lk;
+    if (packed) {
+      lq = (int64_t)p.cu_seqlens_q[b + 1] - p.cu_seqlens_q[b];
+      lk = (int64_t)p.cu_seqlens_k[b + 1] - p.cu_seqlens_k[b];
+    } else {
+      lq = m.seqlens_q ? (int64_t)m.seqlens_q[b] : (int64_t)p.n_q;
+      lk = m.seqlens_k ? (int64_t)m.seqlens_k[b] : (int64_t)p.n_k;
+    }
     if (lq < 0 || lq > p.n_q || lk < 0 || lk > p.n_k) return ATTN_ERR_INVALID_ARG;
     if (lq == 0) continue;             // no active row: nothing to define
     if (lk == 0) return ATTN_ERR_EMPTY_ROW;
-    if (m.causal && m.causal_offset < 0) return ATTN_ERR_EMPTY_ROW;  // row 0 sees nothing
+    const int64_t off = m.causal_offsets ? m.causal_offsets[b] : m.causal_offset;
+    if (m.causal && off < 0) return ATTN_ERR_EMPTY_ROW;  // row 0 sees nothing
   }
+  // row offsets are int32 in the kernels (cu_seqlens_*[B] < 2^31 by type;
+  // the element offsets they scale are 64-bit)
   return ATTN_OK;
 }
 

@@ -191,14 +191,16 @@ def make_custom_inputs(wl: Workload, seed: int, seqlens_q=None, seqlens_k=None,
 # ----------------------------------------------------------------------------
 
 def visible_pairs_per_sequence(n_q, n_k, causal, offset, seqlens_q, seqlens_k, B):
-    """Number of visible (query, key) pairs of each sequence (one query head)."""
+    """Number of visible (query, key) pairs of each sequence (one query head);
+    ``offset`` is one causal offset or one per sequence."""
     lq = [n_q] * B if seqlens_q is None else list(seqlens_q)
     lk = [n_k] * B if seqlens_k is None else list(seqlens_k)
+    offs = [int(offset)] * B if np.ndim(offset) == 0 else [int(x) for x in offset]
     out = []
     for b in range(B):
         i = np.arange(lq[b], dtype=np.int64)
         if causal:
-            cnt = np.clip(np.minimum(lk[b], i + offset + 1), 0, None)
+            cnt = np.clip(np.minimum(lk[b], i + offs[b] + 1), 0, None)
         else:
             cnt = np.full(lq[b], lk[b], dtype=np.int64)
         out.append(int(cnt.sum()))

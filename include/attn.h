@@ -24,7 +24,9 @@
  *
  * Rows i >= L_q[b] are inactive padding rows: their O, lse and G_Q rows are
  * written as 0 and they contribute nothing to G_K / G_V.  Keys j >= L_k[b]
- * get G_K = G_V = 0 exactly.
+ * get G_K = G_V = 0 exactly.  The causal offset may differ per sequence
+ * (attn_mask.causal_offsets), and the sequences may be stored packed, one
+ * after the other with no padding rows (attn_problem.cu_seqlens_q/_k).
  *
  * Layout: every tensor is [B][H][n][d] with unit stride in d; the three outer
  * strides (batch, head, row) are given in ELEMENTS.  G_O and G_Q use the
@@ -37,6 +39,9 @@
  * Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the null
  * stream); nothing synchronises the host.  The library allocates no device
  * memory and keeps no global mutable state: calls are re-entrant.
+ *
+ * The per-sequence arrays (seqlens, causal_offsets, cu_seqlens) are HOST
+ * arrays read during the call.
  *
  * Errors: every argument check runs on the host before anything is enqueued;
  * on any error the outputs are untouched.  Calls on different streams that
@@ -73,12 +78,16 @@ typedef enum {
 
 /* The visible sets V_i (see above). */
 typedef struct {
-  int32_t causal;            /* 0: no causal rule; 1: j <= i + causal_offset   */
+  int32_t causal;            /* 0: no causal rule; 1: j <= i + offset_b        */
   int32_t reserved;          /* must be 0                                      */
-  int64_t causal_offset;     /* 0 = square top-left causal; n_k - n_q places a
-                                block of n_q new queries at the end of the keys */
+  int64_t causal_offset;     /* offset_b of every sequence when causal_offsets
+                                is NULL: 0 = square top-left causal; n_k - n_q
+                                places a block of n_q new queries at the end of
+                                the keys                                       */
   const int32_t* seqlens_q;  /* HOST [B] active rows per sequence, or NULL (= n_q) */
   const int32_t* seqlens_k;  /* HOST [B] valid keys per sequence, or NULL (= n_k)  */
+  const int64_t* causal_offsets; /* HOST [B] per-sequence offset_b (e.g. each
+                                sequence's own cached-history length), or NULL */
 } attn_mask;
 
 typedef struct {
@@ -90,6 +99,19 @@ typedef struct {
   int64_t k_stride[3];       /* K (and G_K)                                    */
   int64_t v_stride[3];       /* V (and G_V)                                    */
   int64_t o_stride[3];       /* O (and G_O)                                    */
+  /* Packed ("varlen") layout: HOST [B + 1] arrays of row offsets, or both
+   * NULL for the padded layout above.  Sequence b owns rows
+   * cu_seqlens_q[b] .. cu_seqlens_q[b + 1] - 1 of Q / O / G_O / G_Q and
+   * cu_seqlens_k[b] .. cu_seqlens_k[b + 1] - 1 of K / V / G_K / G_V, so
+   * L_q[b] and L_k[b] are the differences (seqlens_q / seqlens_k must then be
+   * NULL) and no padding rows exist.  Element (row t, head h, column c) of Q
+   * is at t * q_stride[2] + h * q_stride[1] + c: q_stride[0] (and the other
+   * batch strides) must be 0.  n_q and n_k are upper bounds of the lengths
+   * (they size the launch grids).  lse and the workspace's D are then
+   * [H_q][cu_seqlens_q[B]] float32.  Requires cu_seqlens_*[0] == 0,
+   * non-decreasing entries and row totals below 2^31. */
+  const int32_t* cu_seqlens_q;
+  const int32_t* cu_seqlens_k;
 } attn_problem;
 
 /* Host-only argument check (no device work, no pointers needed).  Returns the
@@ -98,8 +120,9 @@ typedef struct {
 attn_status attn_validate(const attn_problem* prob, const attn_mask* mask);
 
 /* Bytes of device workspace attn_bwd needs for `prob` (256-byte aligned
- * base): per-row float32 D_i = rowsum(G_O o O), B * H_q * n_q floats.  Its
- * contents on entry are ignored. */
+ * base): per-row float32 D_i = rowsum(G_O o O), B * H_q * n_q floats (an
+ * upper bound of H_q * cu_seqlens_q[B] in the packed layout).  Its contents
+ * on entry are ignored. */
 size_t attn_bwd_workspace_size(const attn_problem* prob);
 
 /* Forward.  Q [B,H_q,n_q,d_h], K [B,H_kv,n_k,d_h], V [B,H_kv,n_k,d_v] in;

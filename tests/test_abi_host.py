@@ -36,10 +36,14 @@ def test_exports_every_declared_function():
 
 
 def test_struct_layouts_match_header():
-    # attn_mask: int32, int32, int64, ptr, ptr ; attn_problem: 8 x int32 + 12 x int64
-    assert ctypes.sizeof(A.Mask) == 32
-    assert ctypes.sizeof(A.Problem) == 8 * 4 + 12 * 8
+    # attn_mask: int32, int32, int64, ptr, ptr, ptr
+    # attn_problem: 8 x int32 + 12 x int64 + 2 ptr
+    assert ctypes.sizeof(A.Mask) == 40
+    assert A.Mask.causal_offsets.offset == 32
+    assert ctypes.sizeof(A.Problem) == 8 * 4 + 12 * 8 + 2 * 8
     assert A.Problem.q_stride.offset == 32
+    assert A.Problem.cu_seqlens_q.offset == 128
+    assert A.Problem.cu_seqlens_k.offset == 136
 
 
 def prob(**kw):
@@ -110,3 +114,42 @@ def test_workspace_size():
     rows = 3 * 4 * 100
     assert A.workspace_size(p) == (rows * 4 + 255) // 256 * 256
     assert A.workspace_size(prob(B=0)) == 0
+
+
+def test_validation_per_sequence_offsets():
+    # each sequence's own causal offset decides whether its row 0 sees a key
+    assert status(prob(), causal=True, offset=[0, 7]) == A.OK
+    assert status(prob(), causal=True, offset=[3, -1]) == A.EMPTY_ROW
+    # ...which only matters for sequences with active rows
+    assert status(prob(), causal=True, offset=[3, -1], seqlens_q=[100, 0]) == A.OK
+    # without the causal rule the offsets are unused
+    assert status(prob(), causal=False, offset=[-5, -5]) == A.OK
+
+
+def packed(cu_q, cu_k, **kw):
+    base = dict(B=len(cu_q) - 1, H_q=4, H_kv=2, n_q=max(b - a for a, b in zip(cu_q, cu_q[1:])),
+                n_k=max(b - a for a, b in zip(cu_k, cu_k[1:])), d_h=128, d_v=64, dtype=A.BF16,
+                cu_seqlens_q=cu_q, cu_seqlens_k=cu_k)
+    base.update(kw)
+    return A.make_problem(**base)
+
+
+def test_validation_packed_layout():
+    assert status(packed([0, 10, 30], [0, 20, 40])) == A.OK
+    assert status(packed([0, 10, 30], [0, 20, 40]), causal=True, offset=[0, 3]) == A.OK
+    # n_q / n_k must bound every length
+    assert status(packed([0, 10, 30], [0, 20, 40], n_q=16)) == A.INVALID_ARG
+    assert status(packed([0, 10, 30], [0, 20, 40], n_k=19)) == A.INVALID_ARG
+    # offsets start at 0 and never decrease
+    assert status(packed([2, 10, 30], [0, 20, 40], n_q=28)) == A.INVALID_ARG
+    assert status(packed([0, 10, 5], [0, 20, 40], n_q=10)) == A.INVALID_ARG
+    # both arrays or neither; no per-sequence lengths besides them; batch strides 0
+    assert status(packed([0, 10, 30], [0, 20, 40], cu_seqlens_k=None)) == A.INVALID_ARG
+    assert status(packed([0, 10, 30], [0, 20, 40]), seqlens_q=[10, 20]) == A.INVALID_ARG
+    assert status(packed([0, 10, 30], [0, 20, 40], q_stride=(8, 128, 512))) == A.INVALID_ARG
+    # empty key range under active rows; empty sequences are fine
+    assert status(packed([0, 10, 30], [0, 20, 20])) == A.EMPTY_ROW
+    assert status(packed([0, 10, 10, 30], [0, 20, 20, 40])) == A.OK
+    # the workspace bound covers the packed rows
+    p = packed([0, 10, 30], [0, 20, 40])
+    assert A.workspace_size(p) >= 4 * 30 * 4
