@@ -8,8 +8,9 @@ One step = the whole hot path over one batch of synthetic input: the forward
 G_Q; the key-stationary pass: G_K and G_V), all through the C ABI on one HIP
 stream, inputs resident in HBM.  Default workload: bf16 causal GQA with key and
 row padding, B=8, H_q=32, H_kv=8, n=4096, d=128 (lengths drawn in [2048, 4096]).
-The other configurations (and this one with every length 4096) follow in
-`other_workloads`, timed over fewer steps.
+The other configurations (and this one with every length 4096, and this one
+with its sequences packed without padding rows) follow in `other_workloads`,
+timed over fewer steps.
 
 Prints ONE JSON line.  `value` is algorithmic TFLOP/s: only visible
 (query, key) pairs are credited, 2(d_h + d_v) FLOPs per pair forward and
@@ -112,9 +113,11 @@ def cpu_baseline(inp, seconds: float):
     }
 
 
-def measure(torch, attn, W, wl, uniform_len, steps, warmup):
+def measure(torch, attn, W, wl, uniform_len, steps, warmup, packed=False):
     """Time `steps` steps (forward, dQ pass, dK/dV pass) of one workload with
-    its inputs resident; returns (inputs, work, ms per step, ms per kernel, device)."""
+    its inputs resident; returns (inputs, work, ms per step, ms per kernel, device).
+    With ``packed`` the same sequences are stored one after another without
+    padding rows ([rows, H, d] tensors and row offsets): same visible pairs."""
     import numpy as np
 
     inp = W.make_inputs(wl, uniform_len=uniform_len)
@@ -126,9 +129,25 @@ def measure(torch, attn, W, wl, uniform_len, steps, warmup):
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
         return torch.from_numpy(a).cuda()
 
-    q, k, v, do = dev(inp.Q), dev(inp.K), dev(inp.V), dev(inp.GO)
-    o = torch.empty(wl.B, wl.H_q, wl.n_q, wl.d_v, dtype=q.dtype, device=q.device)
-    lse = torch.empty(wl.B, wl.H_q, wl.n_q, dtype=torch.float32, device=q.device)
+    if packed:
+        lq = inp.seqlens_q or [wl.n_q] * wl.B
+        lk = inp.seqlens_k or [wl.n_k] * wl.B
+
+        def pack(X, lens):  # [B, H, n, d] -> [sum(lens), H, d]
+            return np.ascontiguousarray(np.concatenate([X[b, :, :L].transpose(1, 0, 2)
+                                                        for b, L in enumerate(lens)], axis=0))
+        cu_q = [0] + np.cumsum(lq).astype(int).tolist()
+        cu_k = [0] + np.cumsum(lk).astype(int).tolist()
+        q, do = dev(pack(inp.Q, lq)), dev(pack(inp.GO, lq))
+        k, v = dev(pack(inp.K, lk)), dev(pack(inp.V, lk))
+        o = torch.empty(cu_q[-1], wl.H_q, wl.d_v, dtype=q.dtype, device=q.device)
+        lse = torch.empty(wl.H_q, cu_q[-1], dtype=torch.float32, device=q.device)
+        kw = dict(causal=wl.causal, offset=wl.offset, cu_seqlens_q=cu_q, cu_seqlens_k=cu_k,
+                  max_seqlen_q=wl.n_q, max_seqlen_k=wl.n_k)
+    else:
+        q, k, v, do = dev(inp.Q), dev(inp.K), dev(inp.V), dev(inp.GO)
+        o = torch.empty(wl.B, wl.H_q, wl.n_q, wl.d_v, dtype=q.dtype, device=q.device)
+        lse = torch.empty(wl.B, wl.H_q, wl.n_q, dtype=torch.float32, device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     prob = attn.make_problem(wl.B, wl.H_q, wl.H_kv, wl.n_q, wl.n_k, wl.d_h, wl.d_v,
                              attn.BF16 if wl.dtype == W.BF16 else attn.F32)
@@ -263,14 +282,16 @@ def main(argv=None):
     if not args.no_other_workloads:
         # every other configuration, shorter runs (the headline target is the one above)
         others = []
-        for wid, ulen in [(1, None), (2, None), (4, None), (5, None), (3, 4096)]:
-            if wid == args.workload and ulen == args.uniform_len:
+        for wid, ulen, pk in [(1, None, False), (2, None, False), (4, None, False), (5, None, False),
+                              (3, 4096, False), (3, None, True)]:
+            if wid == args.workload and ulen == args.uniform_len and not pk:
                 continue
             owl = W.WORKLOADS[wid]
-            _, ow, oms, okern, _ = measure(torch, attn, W, owl, ulen, 10, 3)
+            _, ow, oms, okern, _ = measure(torch, attn, W, owl, ulen, 10, 3, packed=pk)
             oflop = ow["fwd_flop"] + ow["bwd_flop"]
             ov = oflop / (oms * 1e-3) / 1e12
-            others.append({"workload": owl.name + (f"_uniform{ulen}" if ulen else ""), "dtype": owl.dtype,
+            label = owl.name + (f"_uniform{ulen}" if ulen else "") + ("_packed" if pk else "")
+            others.append({"workload": label, "dtype": owl.dtype,
                            "value": round(ov, 2), "unit": "TFLOP/s", "ms_per_step": round(oms, 4),
                            "pct_of_peak": round(100 * ov / PEAK_TFLOPS[owl.dtype], 2),
                            "visible_pairs": ow["pairs"], "kernels_ms": {n: round(t, 4) for n, t in okern.items()},
