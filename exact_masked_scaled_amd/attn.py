@@ -35,7 +35,7 @@ BF16 = 1
 
 # every symbol the header declares
 EXPORTS = ("attn_validate", "attn_bwd_workspace_size", "attn_fwd", "attn_bwd",
-           "attn_bwd_dq", "attn_bwd_dkdv",
+           "attn_bwd_dq", "attn_bwd_dkdv", "attn_fwd_splitkv_workspace_size", "attn_fwd_splitkv",
            "attn_status_string", "attn_version")
 
 
@@ -94,6 +94,10 @@ def lib():
     L.attn_bwd_dq.restype = ctypes.c_int
     L.attn_bwd_dkdv.argtypes = [P, M, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.attn_bwd_dkdv.restype = ctypes.c_int
+    L.attn_fwd_splitkv_workspace_size.argtypes = [P, ctypes.c_int32]
+    L.attn_fwd_splitkv_workspace_size.restype = ctypes.c_size_t
+    L.attn_fwd_splitkv.argtypes = [P, M, vp, vp, vp, vp, vp, ctypes.c_int32, vp, ctypes.c_size_t, vp]
+    L.attn_fwd_splitkv.restype = ctypes.c_int
     L.attn_status_string.argtypes = [ctypes.c_int]
     L.attn_status_string.restype = ctypes.c_char_p
     L.attn_version.argtypes = []
@@ -279,6 +283,48 @@ def fwd(q, k, v, *, causal=False, offset=0, seqlens_q=None, seqlens_k=None, out=
     del keep
     if st != OK:
         raise AttnError(st, "attn_fwd")
+    return out, lse
+
+
+def splitkv_workspace_size(prob: Problem, num_splits: int = 0) -> int:
+    return int(lib().attn_fwd_splitkv_workspace_size(ctypes.byref(prob), int(num_splits)))
+
+
+def fwd_splitkv(q, k, v, *, num_splits=0, causal=False, offset=0, seqlens_q=None, seqlens_k=None,
+                out=None, lse=None, workspace=None, stream=None, cu_seqlens_q=None, cu_seqlens_k=None,
+                max_seqlen_q=None, max_seqlen_k=None):
+    """The forward split over the keys (attn_fwd_splitkv): same results as
+    fwd(); num_splits <= 0 lets the library choose."""
+    torch = _torch()
+    packed = cu_seqlens_q is not None or cu_seqlens_k is not None
+    nd = 3 if packed else 4
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check4(name, t, q.dtype, nd)
+    d_v = v.shape[-1]
+    if packed:
+        total_q, H_q, _ = q.shape
+        o_shape, lse_shape = (total_q, H_q, d_v), (H_q, total_q)
+    else:
+        B, H_q, n_q, _ = q.shape
+        o_shape, lse_shape = (B, H_q, n_q, d_v), (B, H_q, n_q)
+    if out is None:
+        out = torch.empty(*o_shape, dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty(*lse_shape, dtype=torch.float32, device=q.device)
+    _check4("out", out, q.dtype, nd)
+    if not lse.is_contiguous() or lse.dtype != torch.float32 or tuple(lse.shape) != lse_shape:
+        raise ValueError(f"lse must be contiguous float32 of shape {lse_shape}")
+    prob = _problem_from(q, k, v, _strides(out), cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    need = splitkv_workspace_size(prob, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    mask, keep = make_mask(causal, offset, seqlens_q, seqlens_k)
+    st = lib().attn_fwd_splitkv(ctypes.byref(prob), ctypes.byref(mask), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                _ptr(lse), int(num_splits), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+                                _stream(stream))
+    del keep
+    if st != OK:
+        raise AttnError(st, "attn_fwd_splitkv")
     return out, lse
 
 

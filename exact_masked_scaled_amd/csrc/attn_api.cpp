@@ -127,6 +127,85 @@ attn_status attn_fwd(const attn_problem* prob, const attn_mask* mask, const void
   return ATTN_OK;
 }
 
+// ---------------------------------------------------------------- split forward
+
+namespace {
+
+// rows of the lse array (padded: B * H_q * n_q; packed: H_q * total rows)
+int64_t lse_rows(const attn_problem& p) {
+  if (p.cu_seqlens_q != nullptr) return (int64_t)p.H_q * p.cu_seqlens_q[p.B];
+  return (int64_t)p.B * p.H_q * p.n_q;
+}
+
+// Parts per row block: enough workgroups to give every CU two (the forward
+// runs two per CU), at most one part per key tile and at most 64.
+int32_t auto_splits(const attn_problem& p) {
+  const int64_t nqblk = (p.n_q + fwd_block_rows(p.dtype) - 1) / fwd_block_rows(p.dtype);
+  const int64_t base = std::max<int64_t>(1, (int64_t)std::min(p.B, kMaxBatchChunk) * p.H_q * nqblk);
+  const int64_t want = (512 + base - 1) / base;
+  const int64_t tiles = std::max<int64_t>(1, (p.n_k + 63) / 64);
+  return (int32_t)std::max<int64_t>(1, std::min<int64_t>({want, tiles, 64}));
+}
+
+int32_t resolve_splits(const attn_problem& p, int32_t num_splits) {
+  return num_splits > 0 ? num_splits : auto_splits(p);
+}
+
+}  // namespace
+
+size_t attn_fwd_splitkv_workspace_size(const attn_problem* prob, int32_t num_splits) {
+  if (prob == nullptr || prob->B < 0 || prob->H_q < 0 || prob->n_q < 0 || prob->n_k < 0 || prob->d_v < 0 ||
+      num_splits > 1024)
+    return 0;
+  if (prob->cu_seqlens_q != nullptr && prob->B > 0 && prob->cu_seqlens_q[prob->B] < 0) return 0;
+  const size_t rows = (size_t)lse_rows(*prob);
+  const size_t s = (size_t)resolve_splits(*prob, num_splits);
+  return align_up(s * rows * (size_t)prob->d_v * sizeof(float), kWsAlign) +
+         align_up(s * rows * sizeof(float), kWsAlign);
+}
+
+attn_status attn_fwd_splitkv(const attn_problem* prob, const attn_mask* mask, const void* Q, const void* K,
+                             const void* V, void* O, float* lse, int32_t num_splits, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  attn_status st = validate_problem(prob, mask);
+  if (st != ATTN_OK) return st;
+  if (num_splits > 1024) return ATTN_ERR_INVALID_ARG;
+  const attn_problem& p = *prob;
+  const attn_mask& m = *mask;
+  if (p.B == 0 || p.n_q == 0) return ATTN_OK;
+  if (!Q || !O || !lse || !aligned16(Q) || !aligned16(O) || !aligned16(lse)) return ATTN_ERR_INVALID_ARG;
+  if (p.n_k > 0 && (!K || !V || !aligned16(K) || !aligned16(V))) return ATTN_ERR_INVALID_ARG;
+  const int32_t splits = resolve_splits(p, num_splits);
+  const size_t need = attn_fwd_splitkv_workspace_size(prob, num_splits);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || ((uintptr_t)workspace % kWsAlign) != 0))
+    return ATTN_ERR_WORKSPACE;
+  const size_t es = esize(p.dtype);
+  const int64_t rows = lse_rows(p);
+  float* part_o = (float*)workspace;
+  float* part_lse = (float*)((char*)workspace + align_up((size_t)splits * rows * p.d_v * sizeof(float), kWsAlign));
+  KernelParams kp;
+  fill_common(kp, p, m);
+  kp.splits = splits;
+  kp.part_rows = rows;
+  const int nqblk = (p.n_q + fwd_block_rows(p.dtype) - 1) / fwd_block_rows(p.dtype);
+  const int cs = chunk_size(kp, p.B);
+  for (int b0 = 0; b0 < p.B; b0 += cs) {
+    const int nb = std::min(cs, p.B - b0);
+    fill_chunk(kp, p, m, b0, nb);
+    kp.per_group = kp.group * nqblk * splits;
+    kp.q = off(Q, b0 * p.q_stride[0], es);
+    kp.k = off(K, b0 * p.k_stride[0], es);
+    kp.v = off(V, b0 * p.v_stride[0], es);
+    kp.o_out = off(O, b0 * p.o_stride[0], es);
+    kp.lse = lse + b0 * kp.lse_sb;
+    kp.part_o = part_o + b0 * kp.lse_sb * p.d_v;
+    kp.part_lse = part_lse + b0 * kp.lse_sb;
+    if (launch_fwd_split(kp, p.dtype, p.d_h, p.d_v, stream) != 0) return ATTN_ERR_HIP;
+    if (launch_fwd_combine(kp, p.dtype, p.d_v, stream) != 0) return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
 }  // extern "C"
 
 namespace {

@@ -36,7 +36,10 @@ __device__ __forceinline__ int key_limit(int i, int Lk, int causal, int off) {
   return causal ? min(Lk, i + off + 1) : Lk;
 }
 
-template <typename T, int DH, int DV>
+// SPLIT: the workgroup covers only part s of its row block's key tiles and
+// writes a normalised float32 partial output and partial lse (merged by
+// fwd_combine_kernel); otherwise it covers all of them and writes O and lse.
+template <typename T, int DH, int DV, bool SPLIT>
 __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(const KernelParams p) {
   using C = FwdCfg<T, DH, DV>;
   using op_t = typename Op<T>::type;
@@ -51,6 +54,11 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(const 
   int unit, item;
   if (!map_work(blockIdx.x, p.groups, p.per_group, p.xcd_map, unit, item)) return;
   const int b = unit / p.H_kv, g = unit - (unit / p.H_kv) * p.H_kv;
+  int sidx = 0;  // key part of this workgroup (SPLIT)
+  if constexpr (SPLIT) {
+    sidx = item % p.splits;
+    item /= p.splits;
+  }
   // heavy (late) row blocks first; all query heads of the unit interleaved
   const int qb = nqblk - 1 - item / p.group;
   const int r = g * p.group + item % p.group;
@@ -87,6 +95,13 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(const 
   if (w_hi > w_lo) wtiles = (key_limit(w_hi - 1, Lk, p.causal, off) + C::BN - 1) / C::BN;
   const int kmax_lane = key_limit(qi, Lk, p.causal, off);
   const int nk_lim = sv.nk_lim;
+  // key tiles [t_lo, t_hi) of this workgroup: all of them, or part sidx of
+  // `splits` nearly equal parts
+  int t_lo = 0, t_hi = ntiles;
+  if constexpr (SPLIT) {
+    t_lo = (int)((int64_t)sidx * ntiles / p.splits);
+    t_hi = (int)((int64_t)(sidx + 1) * ntiles / p.splits);
+  }
 
   f32x16 oacc[DV / 32];
 #pragma unroll
@@ -95,7 +110,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(const 
     for (int e = 0; e < 16; ++e) oacc[i][e] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  if (ntiles > 0) {
+  if (t_hi > t_lo) {
     // Q of this lane's row as the B operand of S^T = K Q^T (row k order)
     op_t qreg[DH / 16];
 #pragma unroll
@@ -110,8 +125,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(const 
     // K/V tiles stream through two LDS buffers with direct global-to-LDS loads
     using KL = TileLoad<T, C::BN, DH, 64 * C::NW>;
     using VL = TileLoad<T, C::BN, DV, 64 * C::NW>;
-    KL::issue(Kb, p.k_sr, 0, nk_lim, k_lds0, tid);
-    VL::issue(Vb, p.v_sr, 0, nk_lim, v_lds0, tid);
+    KL::issue(Kb, p.k_sr, t_lo * C::BN, nk_lim, k_lds0, tid);
+    VL::issue(Vb, p.v_sr, t_lo * C::BN, nk_lim, v_lds0, tid);
     wait_tile_loads();
     __syncthreads();
 
@@ -181,16 +196,16 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(const 
     };
 
     // two tiles per trip so each LDS buffer address is a compile-time constant
-    for (int t = 0; t < ntiles; t += 2) {
-      if (t + 1 < ntiles) {
+    for (int t = t_lo; t < t_hi; t += 2) {
+      if (t + 1 < t_hi) {
         KL::issue(Kb, p.k_sr, (t + 1) * C::BN, nk_lim, k_lds1, tid);
         VL::issue(Vb, p.v_sr, (t + 1) * C::BN, nk_lim, v_lds1, tid);
       }
       if (t < wtiles) tile(t, k_lds0, v_lds0);
       wait_tile_loads();
       __syncthreads();
-      if (t + 1 >= ntiles) break;
-      if (t + 2 < ntiles) {
+      if (t + 1 >= t_hi) break;
+      if (t + 2 < t_hi) {
         KL::issue(Kb, p.k_sr, (t + 2) * C::BN, nk_lim, k_lds0, tid);
         VL::issue(Vb, p.v_sr, (t + 2) * C::BN, nk_lim, v_lds0, tid);
       }
@@ -203,6 +218,28 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(const 
   // epilogue: O = acc / l, lse = ln2 * (m + log2 l); inactive rows get zeros
   const float l_tot = l_run + partner32(l_run);
   const float inv = (row_active && l_tot > 0.f) ? 1.f / l_tot : 0.f;
+  if constexpr (SPLIT) {
+    // partial of split sidx: a row that saw no key of this part gets lse = -inf
+    if (row_exists) {
+      const int64_t prow = (int64_t)sidx * p.part_rows + b * p.lse_sb + r * p.lse_sh + sv.q_row0 + qi;
+      float* po = p.part_o + prow * DV;
+#pragma unroll
+      for (int dt = 0; dt < DV / 32; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int d = 32 * dt + 8 * j + 4 * kg;
+          f32x4 v4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v4[e] = oacc[dt][4 * j + e] * inv;
+          *reinterpret_cast<f32x4*>(po + d) = v4;
+        }
+      if (kg == 0)
+        p.part_lse[prow] = (row_active && l_tot > 0.f)
+                               ? (m_run * p.scale_log2 + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994530942f
+                               : -INFINITY;
+    }
+    return;
+  }
   if (row_exists) {
 #pragma unroll
     for (int dt = 0; dt < DV / 32; ++dt)
@@ -218,34 +255,97 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(const 
   }
 }
 
-template <typename T, int DH, int DV>
+// Merge of the key parts of a split forward, one wave per row: with the
+// partial logsumexps l_s and outputs O_s (each normalised over its part),
+//   lse = log sum_s exp(l_s),  O = sum_s exp(l_s - lse) O_s,
+// which is the softmax-weighted sum over the union of the parts (the parts
+// partition the visible set; a part the row does not see has l_s = -inf).
+// Inactive rows get O = 0 and lse = 0 as in the unsplit forward.
+template <typename T, int DV>
+__global__ __launch_bounds__(256) void fwd_combine_kernel(const KernelParams p) {
+  constexpr int CPL = DV / 64;  // columns per lane
+  const int b = blockIdx.z, r = blockIdx.y, lane = threadIdx.x & 63;
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const SeqView sv = seq_view(p, b);
+  if (i >= sv.nq_lim) return;
+  const int64_t row = b * p.lse_sb + r * p.lse_sh + sv.q_row0 + i;
+  T* orow = (T*)p.o_out + b * p.o_sb + (sv.q_row0 + i) * p.o_sr + r * p.o_sh + CPL * lane;
+  if (i >= sv.Lq) {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) orow[c] = (T)0.f;
+    if (lane == 0) p.lse[row] = 0.f;
+    return;
+  }
+  constexpr float kLog2e = 1.4426950408889634f;
+  float mx = -INFINITY;
+  for (int s = 0; s < p.splits; ++s) mx = fmaxf(mx, p.part_lse[s * p.part_rows + row]);
+  float sum = 0.f;
+  for (int s = 0; s < p.splits; ++s) sum += __builtin_amdgcn_exp2f((p.part_lse[s * p.part_rows + row] - mx) * kLog2e);
+  const float lse = mx + __builtin_amdgcn_logf(sum) * 0.69314718055994530942f;
+  float acc[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+  for (int s = 0; s < p.splits; ++s) {
+    const float wgt = __builtin_amdgcn_exp2f((p.part_lse[s * p.part_rows + row] - lse) * kLog2e);
+    const float* po = p.part_o + (s * p.part_rows + row) * DV + CPL * lane;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) acc[c] = fmaf(wgt, po[c], acc[c]);
+  }
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) orow[c] = (T)acc[c];
+  if (lane == 0) p.lse[row] = lse;
+}
+
+template <typename T, int DH, int DV, bool SPLIT>
 static int launch_fwd_t(const KernelParams& p, void* stream) {
   using C = FwdCfg<T, DH, DV>;
-  const int nqblk = (p.n_q + C::BM - 1) / C::BM;
-  (void)nqblk;
   const int64_t units = p.xcd_map ? ((p.groups + 7) / 8) * 8 : p.groups;
   const int64_t grid = units * p.per_group;
   if (grid <= 0) return (int)hipSuccess;
-  hipLaunchKernelGGL((fwd_kernel<T, DH, DV>), dim3((unsigned)grid), dim3(64 * C::NW), 0,
+  hipLaunchKernelGGL((fwd_kernel<T, DH, DV, SPLIT>), dim3((unsigned)grid), dim3(64 * C::NW), 0,
                      (hipStream_t)stream, p);
   return (int)hipGetLastError();
 }
 
 int fwd_block_rows(int /*dtype*/) { return 128; }
 
-int launch_fwd(const KernelParams& p, int dtype, int d_h, int d_v, void* stream) {
+template <bool SPLIT>
+static int launch_fwd_any(const KernelParams& p, int dtype, int d_h, int d_v, void* stream) {
   if (dtype == ATTN_BF16) {
-    if (d_h == 128 && d_v == 128) return launch_fwd_t<__bf16, 128, 128>(p, stream);
-    if (d_h == 128 && d_v == 64) return launch_fwd_t<__bf16, 128, 64>(p, stream);
-    if (d_h == 64 && d_v == 64) return launch_fwd_t<__bf16, 64, 64>(p, stream);
-    if (d_h == 64 && d_v == 128) return launch_fwd_t<__bf16, 64, 128>(p, stream);
+    if (d_h == 128 && d_v == 128) return launch_fwd_t<__bf16, 128, 128, SPLIT>(p, stream);
+    if (d_h == 128 && d_v == 64) return launch_fwd_t<__bf16, 128, 64, SPLIT>(p, stream);
+    if (d_h == 64 && d_v == 64) return launch_fwd_t<__bf16, 64, 64, SPLIT>(p, stream);
+    if (d_h == 64 && d_v == 128) return launch_fwd_t<__bf16, 64, 128, SPLIT>(p, stream);
   } else {
-    if (d_h == 128 && d_v == 128) return launch_fwd_t<float, 128, 128>(p, stream);
-    if (d_h == 128 && d_v == 64) return launch_fwd_t<float, 128, 64>(p, stream);
-    if (d_h == 64 && d_v == 64) return launch_fwd_t<float, 64, 64>(p, stream);
-    if (d_h == 64 && d_v == 128) return launch_fwd_t<float, 64, 128>(p, stream);
+    if (d_h == 128 && d_v == 128) return launch_fwd_t<float, 128, 128, SPLIT>(p, stream);
+    if (d_h == 128 && d_v == 64) return launch_fwd_t<float, 128, 64, SPLIT>(p, stream);
+    if (d_h == 64 && d_v == 64) return launch_fwd_t<float, 64, 64, SPLIT>(p, stream);
+    if (d_h == 64 && d_v == 128) return launch_fwd_t<float, 64, 128, SPLIT>(p, stream);
   }
   return (int)hipErrorInvalidValue;
+}
+
+int launch_fwd(const KernelParams& p, int dtype, int d_h, int d_v, void* stream) {
+  return launch_fwd_any<false>(p, dtype, d_h, d_v, stream);
+}
+
+int launch_fwd_split(const KernelParams& p, int dtype, int d_h, int d_v, void* stream) {
+  return launch_fwd_any<true>(p, dtype, d_h, d_v, stream);
+}
+
+int launch_fwd_combine(const KernelParams& p, int dtype, int d_v, void* stream) {
+  const dim3 grid((unsigned)((p.n_q + 3) / 4), (unsigned)p.H_q, (unsigned)p.B);
+  if (p.n_q <= 0 || p.B <= 0) return (int)hipSuccess;
+  if (dtype == ATTN_BF16) {
+    if (d_v == 128) hipLaunchKernelGGL((fwd_combine_kernel<__bf16, 128>), grid, dim3(256), 0, (hipStream_t)stream, p);
+    else if (d_v == 64) hipLaunchKernelGGL((fwd_combine_kernel<__bf16, 64>), grid, dim3(256), 0, (hipStream_t)stream, p);
+    else return (int)hipErrorInvalidValue;
+  } else {
+    if (d_v == 128) hipLaunchKernelGGL((fwd_combine_kernel<float, 128>), grid, dim3(256), 0, (hipStream_t)stream, p);
+    else if (d_v == 64) hipLaunchKernelGGL((fwd_combine_kernel<float, 64>), grid, dim3(256), 0, (hipStream_t)stream, p);
+    else return (int)hipErrorInvalidValue;
+  }
+  return (int)hipGetLastError();
 }
 
 }  // namespace attn

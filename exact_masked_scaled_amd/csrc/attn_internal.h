@@ -44,6 +44,14 @@ struct KernelParams {
   int32_t per_group;    // work items per unit
   int32_t xcd_map;      // 1: unit u runs on XCD u % 8 (groups % 8 == 0)
   int64_t lse_sb, lse_sh;  // element strides of lse and D: sequence, head (rows: 1)
+  // forward split over the keys: `splits` parts per row block, each writing
+  // its normalised float32 partial output and partial lse at split s of
+  // part_o [s][rows][d_v] / part_lse [s][rows] (rows indexed like lse; the
+  // split stride is part_rows rows); a combine kernel merges them
+  int32_t splits;
+  float* part_o;
+  float* part_lse;
+  int64_t part_rows;
   int32_t lens_q[kMaxBatchChunk];
   int32_t lens_k[kMaxBatchChunk];
   int32_t offs[kMaxBatchChunk];    // causal offsets, clamped to [0, n_k]
@@ -59,6 +67,9 @@ attn_status validate_problem(const attn_problem* prob, const attn_mask* mask);
 int launch_fwd(const KernelParams& p, int dtype, int d_h, int d_v, void* stream);
 int launch_bwd_dq(const KernelParams& p, int dtype, int d_h, int d_v, void* stream);
 int launch_bwd_dkdv(const KernelParams& p, int dtype, int d_h, int d_v, void* stream);
+// forward split over the keys (p.splits > 1): partial pass, then the merge
+int launch_fwd_split(const KernelParams& p, int dtype, int d_h, int d_v, void* stream);
+int launch_fwd_combine(const KernelParams& p, int dtype, int d_v, void* stream);
 
 // Tile sizes the dispatcher needs to size grids.
 int fwd_block_rows(int dtype);

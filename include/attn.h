@@ -132,6 +132,25 @@ attn_status attn_fwd(const attn_problem* prob, const attn_mask* mask,
                      const void* Q, const void* K, const void* V,
                      void* O, float* lse, void* stream);
 
+/* Forward split over the keys, for problems with few query rows per KV head
+ * (a block of new queries, or single decoding rows, against a long cached
+ * history: "Chapter 31: attention backpropagation" (eonloom handbook),
+ * sec. 1).  Same arguments and results as attn_fwd: the key tiles of every
+ * row block are divided into num_splits nearly equal parts computed by
+ * separate workgroups, each giving a partial output normalised over its part
+ * and its partial logsumexp l_s; a second kernel merges them exactly:
+ *   lse = log sum_s exp(l_s),   O = sum_s exp(l_s - lse) O_s
+ * (the parts partition each row's visible set).  num_splits <= 0 chooses the
+ * count from the sizes (enough workgroups for the whole GPU); at most 1024.
+ * `workspace`: device memory of attn_fwd_splitkv_workspace_size(prob,
+ * num_splits) bytes, 256-byte aligned (float32 partials; contents on entry
+ * ignored).  Results equal attn_fwd's up to float32 rounding order. */
+size_t attn_fwd_splitkv_workspace_size(const attn_problem* prob, int32_t num_splits);
+attn_status attn_fwd_splitkv(const attn_problem* prob, const attn_mask* mask,
+                             const void* Q, const void* K, const void* V,
+                             void* O, float* lse, int32_t num_splits,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 /* Backward.  Takes the forward's inputs, its outputs O and lse, and G_O
  * (strides of O); writes G_Q (strides of Q), G_K (strides of K) and G_V
  * (strides of V).  `workspace` is device memory of at least

@@ -153,3 +153,33 @@ def test_validation_packed_layout():
     # the workspace bound covers the packed rows
     p = packed([0, 10, 30], [0, 20, 40])
     assert A.workspace_size(p) >= 4 * 30 * 4
+
+
+def test_splitkv_workspace_and_errors():
+    L = lib_or_skip()
+    p = prob(B=2, H_q=4, n_q=100, n_k=130, d_v=64)
+    rows = 2 * 4 * 100
+    # float32 partial outputs and logsumexps for every part, two aligned sections
+    for s in (1, 3, 8):
+        want = (s * rows * 64 * 4 + 255) // 256 * 256 + (s * rows * 4 + 255) // 256 * 256
+        assert A.splitkv_workspace_size(p, s) == want
+    auto = A.splitkv_workspace_size(p, 0)
+    assert auto >= A.splitkv_workspace_size(p, 1)
+    # packed layout: rows = H_q * total rows
+    pk = packed([0, 10, 30], [0, 20, 40])
+    assert A.splitkv_workspace_size(pk, 2) == ((2 * 4 * 30 * 64 * 4 + 255) // 256 * 256
+                                               + (2 * 4 * 30 * 4 + 255) // 256 * 256)
+    m, keep = A.make_mask()
+    null = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(0x10000)
+    # too many parts, then a missing workspace: rejected before any launch
+    st = L.attn_fwd_splitkv(ctypes.byref(p), ctypes.byref(m), fake, fake, fake, fake, fake, 2000, fake,
+                            ctypes.c_size_t(1 << 30), null)
+    assert st == A.INVALID_ARG
+    st = L.attn_fwd_splitkv(ctypes.byref(p), ctypes.byref(m), fake, fake, fake, fake, fake, 4, null,
+                            ctypes.c_size_t(0), null)
+    assert st == A.WORKSPACE
+    m2, keep2 = A.make_mask(causal=True, offset=-1)
+    st = L.attn_fwd_splitkv(ctypes.byref(p), ctypes.byref(m2), fake, fake, fake, fake, fake, 4, fake,
+                            ctypes.c_size_t(1 << 30), null)
+    assert st == A.EMPTY_ROW
