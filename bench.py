@@ -187,6 +187,44 @@ def measure(torch, attn, W, wl, uniform_len, steps, warmup, packed=False):
     return inp, work, ms_per_step, kern_ms, device
 
 
+def measure_forward_split(torch, attn, W, wl, steps, warmup):
+    """Forward only, unsplit (attn_fwd) against split over the keys
+    (attn_fwd_splitkv, automatic part count), inputs resident; ms per call."""
+    import numpy as np
+
+    inp = W.make_inputs(wl, with_grad=False) if wl.wid in W.WORKLOADS else \
+        W.make_custom_inputs(wl, seed=2000, with_grad=False)
+    kw = inp.mask_kwargs()
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+    q, k, v = dev(inp.Q), dev(inp.K), dev(inp.V)
+    o = torch.empty(wl.B, wl.H_q, wl.n_q, wl.d_v, dtype=q.dtype, device=q.device)
+    lse = torch.empty(wl.B, wl.H_q, wl.n_q, dtype=torch.float32, device=q.device)
+    prob = attn._problem_from(q, k, v, attn._strides(o))
+    ws = torch.empty(max(attn.splitkv_workspace_size(prob, 0), 1), dtype=torch.uint8, device=q.device)
+    stream = torch.cuda.current_stream()
+    calls = {"unsplit": lambda: attn.fwd(q, k, v, out=o, lse=lse, stream=stream, **kw),
+             "split": lambda: attn.fwd_splitkv(q, k, v, num_splits=0, out=o, lse=lse, workspace=ws,
+                                               stream=stream, **kw)}
+    out = {}
+    for name, fn in calls.items():
+        for _ in range(warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out[name] = e0.elapsed_time(e1) / steps
+    work = W.work(wl, inp.seqlens_q, inp.seqlens_k)
+    del q, k, v, o, lse, ws
+    return out, work
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -297,6 +335,21 @@ def main(argv=None):
                            "visible_pairs": ow["pairs"], "kernels_ms": {n: round(t, 4) for n, t in okern.items()},
                            "steps": 10, "warmup": 3})
         result["other_workloads"] = others
+        # forward only, split over the keys, where few query rows meet a long key range
+        fsplit = []
+        decode = W.custom_workload(W.BF16, 8, 32, 8, 1, 8192, 128, 128, True, 8191,
+                                   "decode_gqa_bf16_b8_hq32_hkv8_nq1_nk8192_d128")
+        for fwl in (W.WORKLOADS[5], W.WORKLOADS[4], decode):
+            t, fw = measure_forward_split(torch, attn, W, fwl, 20, 3)
+            s_ = 2 if fwl.dtype == W.BF16 else 4
+            byts = s_ * (fwl.B * fwl.H_kv * fwl.n_k * (fwl.d_h + fwl.d_v)
+                         + fwl.B * fwl.H_q * fwl.n_q * (fwl.d_h + fwl.d_v)) + 4 * fwl.B * fwl.H_q * fwl.n_q
+            ent = {"workload": fwl.name, "unsplit_ms": round(t["unsplit"], 4), "split_ms": round(t["split"], 4),
+                   "split_TFLOP/s": round(fw["fwd_flop"] / (t["split"] * 1e-3) / 1e12, 2),
+                   "split_GB/s_algorithmic": round(byts / (t["split"] * 1e-3) / 1e9, 1),
+                   "unsplit_TFLOP/s": round(fw["fwd_flop"] / (t["unsplit"] * 1e-3) / 1e12, 2)}
+            fsplit.append(ent)
+        result["forward_splitkv"] = fsplit
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)
