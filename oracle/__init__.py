@@ -30,6 +30,9 @@ from .attention import (  # noqa: F401
     attention_backward,
     attention_group,
     attention_backward_packed,
+    attention_backward_rope,
+    rope_rotate,
+    rope_table,
     offsets_per_sequence,
     scores,
     masked_softmax,

@@ -378,3 +378,70 @@ def attention_backward_packed(Q, K, V, GO, cu_seqlens_q, cu_seqlens_k, *, causal
         O[qs] = f["O"][0].transpose(1, 0, 2)
         lse[:, qs] = f["lse"][0]
     return {"O": O, "lse": lse, "GQ": GQ, "GK": GK, "GV": GV, "D": D}
+
+
+# ----------------------------------------------------------------------------
+# rotary position encoding (RoPE)
+# ----------------------------------------------------------------------------
+
+def rope_rotate(X, cos_sin, positions, inverse=False) -> np.ndarray:
+    """Rotate each adjacent pair of columns (2k, 2k+1) of every row of X by the
+    angle of that row's position: the 2-D block rotation of [ch.15, sec. 15.6]
+    applied to q_i (or k_j), x~ = R(theta) x with
+        x~_2k   = cos(theta) x_2k - sin(theta) x_2k+1
+        x~_2k+1 = sin(theta) x_2k + cos(theta) x_2k+1,
+    theta = theta(position, k) given by the table: cos_sin[pos, k] = (cos, sin).
+    ``inverse`` applies R(theta)^T (the rotation by -theta): the backward of the
+    rotation ([ch.31, sec. 5]: the transposed rotation of the upstream gradient).
+
+    X: [..., n, d] with positions[n] the position of each row."""
+    X = np.asarray(X, dtype=np.float64)
+    cs = np.asarray(cos_sin, dtype=np.float64)
+    pos = np.asarray(positions, dtype=np.int64)
+    c = cs[pos, :, 0]   # [n, d/2]
+    s = cs[pos, :, 1]
+    if inverse:
+        s = -s
+    x0, x1 = X[..., 0::2], X[..., 1::2]
+    Y = np.empty_like(X)
+    Y[..., 0::2] = c * x0 - s * x1
+    Y[..., 1::2] = s * x0 + c * x1
+    return Y
+
+
+def attention_backward_rope(Q, K, V, GO, cos_sin, *, causal=False, offset=0,
+                            seqlens_q=None, seqlens_k=None) -> dict:
+    """Attention with rotary positions on Q and K ([ch.15, sec. 15.6]): key j of
+    a sequence sits at position j, query row i at position i + offset_b (its
+    place in the key positions, the alignment the causal rule uses).  Forward
+    on Q~ = R Q, K~ = R K; gradients G_Q = R^T G_Q~, G_K = R^T G_K~
+    ([ch.31, sec. 5]); V is not rotated.  GO may be None (forward only)."""
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    B, H_q, n_q, _ = Q.shape
+    n_k = K.shape[2]
+    offs = offsets_per_sequence(offset, B)
+    Qr = np.empty_like(Q)
+    Kr = np.empty_like(K)
+    for b in range(B):
+        Qr[b] = rope_rotate(Q[b], cos_sin, np.arange(n_q) + offs[b])
+        Kr[b] = rope_rotate(K[b], cos_sin, np.arange(n_k))
+    kw = dict(causal=causal, offset=offset, seqlens_q=seqlens_q, seqlens_k=seqlens_k)
+    if GO is None:
+        return attention_forward(Qr, Kr, V, **kw)
+    out = attention_backward(Qr, Kr, V, GO, **kw)
+    for b in range(B):
+        out["GQ"][b] = rope_rotate(out["GQ"][b], cos_sin, np.arange(n_q) + offs[b], inverse=True)
+        out["GK"][b] = rope_rotate(out["GK"][b], cos_sin, np.arange(n_k), inverse=True)
+    return out
+
+
+def rope_table(n_pos: int, d_h: int, base: float = 10000.0) -> np.ndarray:
+    """A cos/sin table [n_pos, d_h/2, 2] with the geometric frequencies
+    omega_k = base^(-2k/d_h), theta = pos * omega_k (one common choice; the
+    pages fix only that each 2-D block turns by position times a fixed
+    frequency), rounded to float32 as the library receives it."""
+    k = np.arange(d_h // 2)
+    omega = base ** (-2.0 * k / d_h)
+    theta = np.arange(n_pos)[:, None] * omega[None, :]
+    return np.stack([np.cos(theta), np.sin(theta)], axis=-1).astype(np.float32)
