@@ -69,7 +69,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(con
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, kg = lane >> 5;
   const SeqView sv = seq_view(p, b);
-  const int Lq = sv.Lq, Lk = sv.Lk, off = sv.off, nk_lim = sv.nk_lim;
+  const int Lq = sv.Lq, Lk = sv.Lk, off = sv.off;
   const int q_lo = qb * C::BM;
   const int qi = q_lo + 32 * w + (lane & 31);
   const bool row_exists = qi < sv.nq_lim;
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(con
   float dpart = 0.f;
 #pragma unroll
   for (int ks = 0; ks < DV / 16; ++ks) {
-    if (row_exists) {
+    if (row_active) {
       doreg[ks] = ld8<T>(dOb + (int64_t)qi * p.o_sr + 16 * ks + 8 * kg);
       const op_t o8 = ld8<T>(Ob + (int64_t)qi * p.o_sr + 16 * ks + 8 * kg);
 #pragma unroll
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(con
     op_t qreg[DH / 16];
 #pragma unroll
     for (int ks = 0; ks < DH / 16; ++ks)
-      qreg[ks] = row_exists ? ld8<T>(Qb + (int64_t)qi * p.q_sr + 16 * ks + 8 * kg) : zero_op<T>();
+      qreg[ks] = row_active ? ld8<T>(Qb + (int64_t)qi * p.q_sr + 16 * ks + 8 * kg) : zero_op<T>();
 
     // per-lane LDS offsets (K and V tiles share them when d_h == d_v)
     RowOffsets<T, DH> kro;
@@ -177,23 +177,23 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(con
 
     using KL = TileLoad<T, C::BN, DH, 64 * C::NW>;
     using VL = TileLoad<T, C::BN, DV, 64 * C::NW>;
-    KL::issue(Kb, p.k_sr, 0, nk_lim, k_lds0, tid);
-    VL::issue(Vb, p.v_sr, 0, nk_lim, v_lds0, tid);
+    KL::issue(Kb, p.k_sr, 0, Lk, k_lds0, tid);
+    VL::issue(Vb, p.v_sr, 0, Lk, v_lds0, tid);
     wait_tile_loads();
     __syncthreads();
     // two tiles per trip so each LDS buffer address is a compile-time constant
     for (int t = 0; t < ntiles; t += 2) {
       if (t + 1 < ntiles) {
-        KL::issue(Kb, p.k_sr, (t + 1) * C::BN, nk_lim, k_lds1, tid);
-        VL::issue(Vb, p.v_sr, (t + 1) * C::BN, nk_lim, v_lds1, tid);
+        KL::issue(Kb, p.k_sr, (t + 1) * C::BN, Lk, k_lds1, tid);
+        VL::issue(Vb, p.v_sr, (t + 1) * C::BN, Lk, v_lds1, tid);
       }
       if (t < wtiles) tile(t, k_lds0, v_lds0);
       wait_tile_loads();
       __syncthreads();
       if (t + 1 >= ntiles) break;
       if (t + 2 < ntiles) {
-        KL::issue(Kb, p.k_sr, (t + 2) * C::BN, nk_lim, k_lds0, tid);
-        VL::issue(Vb, p.v_sr, (t + 2) * C::BN, nk_lim, v_lds0, tid);
+        KL::issue(Kb, p.k_sr, (t + 2) * C::BN, Lk, k_lds0, tid);
+        VL::issue(Vb, p.v_sr, (t + 2) * C::BN, Lk, v_lds0, tid);
       }
       if (t + 1 < wtiles) tile(t + 1, k_lds1, v_lds1);
       wait_tile_loads();
@@ -292,7 +292,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const KernelParams p) 
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
       const int key = kw0 + 32 * kt + (lane & 31);
-      const bool ok = key < nk_lim;
+      const bool ok = key < Lk;
 #pragma unroll
       for (int ks = 0; ks < DH / 16; ++ks)
         kreg[kt][ks] = ok ? ld8<T>(Kb + (int64_t)key * p.k_sr + 16 * ks + 8 * kg) : zero_op<T>();
@@ -316,8 +316,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const KernelParams p) 
     const T* const o_base = (const T*)p.dout + b * p.o_sb + sv.q_row0 * p.o_sr;
     const float* const rows_base = (lane < 32 ? p.lse : p.delta) + b * p.lse_sb + sv.q_row0;
     const int64_t q_sh = p.q_sh, o_sh = p.o_sh, q_sr = p.q_sr, o_sr = p.o_sr, r_sh = p.lse_sh;
-    // rows present in memory (copies of rows beyond repeat the last one)
-    const int n_q = sv.nq_lim, group = p.group;
+    // copies of rows past the last active one repeat it (finite data only)
+    const int n_q = Lq, group = p.group;
     auto issue = [&](int s, int st) {
       const int rr = s / nq, qb = qb_first + s % nq;
       const int r = g * group + rr;
@@ -614,7 +614,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
         const int key = kh0 + 32 * kb2 + (lane & 31);
-        const bool ok = key < nk_lim;
+        const bool ok = key < Lk;
         const T* row = src + (int64_t)key * sr + 8 * kg;
         constexpr int NK = (DH > DV ? DH : DV) / 16;
 #pragma unroll
@@ -635,8 +635,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
     const T* const q_base = (const T*)p.q + b * p.q_sb + sv.q_row0 * p.q_sr;
     const T* const o_base = (const T*)p.dout + b * p.o_sb + sv.q_row0 * p.o_sr;
     const int64_t q_sh = p.q_sh, o_sh = p.o_sh, q_sr = p.q_sr, o_sr = p.o_sr, r_sh = p.lse_sh;
-    // rows present in memory (copies of rows beyond repeat the last one)
-    const int n_q = sv.nq_lim, group = p.group;
+    // copies of rows past the last active one repeat it (finite data only)
+    const int n_q = Lq, group = p.group;
     const float* const rows_lane = (lane < 32 ? p.lse : p.delta) + b * p.lse_sb + sv.q_row0 + (lane & 31);
     const int yw = w & 3;  // copy slot of a Y wave
     int64_t c_off[C::JPW];

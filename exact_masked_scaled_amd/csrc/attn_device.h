@@ -332,7 +332,9 @@ struct SeqView {
   int off;             // causal offset of the sequence (clamped to [0, n_k])
   int nq_lim, nk_lim;  // rows of the sequence present in memory: n_q / n_k in
                        // the padded layout, L_q / L_k in the packed one
-                       // (copies clamp to them, stores stop at them)
+                       // (stores stop at them; tile copies clamp to the last
+                       // active row / valid key instead, so padding content
+                       // never meets a zero probability in a product)
   int64_t q_row0, k_row0;  // first row of the sequence (packed layout; else 0)
 };
 __device__ __forceinline__ SeqView seq_view(const KernelParams& p, int b) {

@@ -94,7 +94,6 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(const 
   int wtiles = 0;
   if (w_hi > w_lo) wtiles = (key_limit(w_hi - 1, Lk, p.causal, off) + C::BN - 1) / C::BN;
   const int kmax_lane = key_limit(qi, Lk, p.causal, off);
-  const int nk_lim = sv.nk_lim;
   // key tiles [t_lo, t_hi) of this workgroup: all of them, or part sidx of
   // `splits` nearly equal parts
   int t_lo = 0, t_hi = ntiles;
@@ -115,7 +114,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(const 
     op_t qreg[DH / 16];
 #pragma unroll
     for (int ks = 0; ks < DH / 16; ++ks)
-      qreg[ks] = row_exists ? ld8<T>(Qb + (int64_t)qi * p.q_sr + 16 * ks + 8 * kg) : zero_op<T>();
+      qreg[ks] = row_active ? ld8<T>(Qb + (int64_t)qi * p.q_sr + 16 * ks + 8 * kg) : zero_op<T>();
 
     RowOffsets<T, DH> kro;
     TrOffsets<T, DV> vto;
@@ -125,8 +124,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(const 
     // K/V tiles stream through two LDS buffers with direct global-to-LDS loads
     using KL = TileLoad<T, C::BN, DH, 64 * C::NW>;
     using VL = TileLoad<T, C::BN, DV, 64 * C::NW>;
-    KL::issue(Kb, p.k_sr, t_lo * C::BN, nk_lim, k_lds0, tid);
-    VL::issue(Vb, p.v_sr, t_lo * C::BN, nk_lim, v_lds0, tid);
+    KL::issue(Kb, p.k_sr, t_lo * C::BN, Lk, k_lds0, tid);
+    VL::issue(Vb, p.v_sr, t_lo * C::BN, Lk, v_lds0, tid);
     wait_tile_loads();
     __syncthreads();
 
@@ -198,16 +197,16 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(const 
     // two tiles per trip so each LDS buffer address is a compile-time constant
     for (int t = t_lo; t < t_hi; t += 2) {
       if (t + 1 < t_hi) {
-        KL::issue(Kb, p.k_sr, (t + 1) * C::BN, nk_lim, k_lds1, tid);
-        VL::issue(Vb, p.v_sr, (t + 1) * C::BN, nk_lim, v_lds1, tid);
+        KL::issue(Kb, p.k_sr, (t + 1) * C::BN, Lk, k_lds1, tid);
+        VL::issue(Vb, p.v_sr, (t + 1) * C::BN, Lk, v_lds1, tid);
       }
       if (t < wtiles) tile(t, k_lds0, v_lds0);
       wait_tile_loads();
       __syncthreads();
       if (t + 1 >= t_hi) break;
       if (t + 2 < t_hi) {
-        KL::issue(Kb, p.k_sr, (t + 2) * C::BN, nk_lim, k_lds0, tid);
-        VL::issue(Vb, p.v_sr, (t + 2) * C::BN, nk_lim, v_lds0, tid);
+        KL::issue(Kb, p.k_sr, (t + 2) * C::BN, Lk, k_lds0, tid);
+        VL::issue(Vb, p.v_sr, (t + 2) * C::BN, Lk, v_lds0, tid);
       }
       if (t + 1 < wtiles) tile(t + 1, k_lds1, v_lds1);
       wait_tile_loads();

@@ -171,3 +171,45 @@ def test_packed_equals_padded_on_gpu():
                          (dk[rows], pad["GK"][b, :, :L]), (dv[rows], pad["GV"][b, :, :L])):
             assert torch.equal(got.transpose(0, 1), ref)
         assert torch.equal(lse[:, rows], pad["lse"][b, :, :L])
+
+
+# --------------------------------------------------------------------- padding content
+NAN_PAD_CASES = [
+    # (name, dtype, B, H_q, H_kv, n_q, n_k, d_h, d_v, causal, offset, lens_q, lens_k)
+    ("bf16_gqa_causal_nanpad", W.BF16, 3, 8, 2, 200, 200, 128, 128, True, 0, [200, 77, 130], [200, 77, 130]),
+    ("bf16_cross_nanpad", W.BF16, 2, 4, 4, 150, 300, 128, 64, False, 0, [33, 150], [290, 65]),
+    ("f32_d64_nanpad", W.F32, 2, 2, 1, 96, 96, 64, 64, True, 0, [50, 96], [50, 96]),
+]
+
+
+@pytest.mark.parametrize("case", NAN_PAD_CASES, ids=lambda c: c[0])
+def test_padding_rows_never_read(case):
+    """Rows past L_q and keys past L_k in the padded layout may hold anything,
+    NaN included: every output, and every inactive row or padded key of the
+    outputs (zeros), is the same as with finite padding."""
+    torch = pytest.importorskip("torch")
+    name, dtype, B, H_q, H_kv, n_q, n_k, d_h, d_v, causal, off, lq, lk = case
+    P.say(f"[varlen] {name}")
+    wl = W.custom_workload(dtype, B, H_q, H_kv, n_q, n_k, d_h, d_v, causal, off, name)
+    inp = W.make_custom_inputs(wl, seed=zlib.crc32(name.encode()) % 10000, seqlens_q=lq, seqlens_k=lk)
+    kw = inp.mask_kwargs()
+    q, k, v, do = (P.to_device(inp.Q), P.to_device(inp.K), P.to_device(inp.V), P.to_device(inp.GO))
+    for b in range(B):
+        q[b, :, lq[b]:] = float("nan")
+        do[b, :, lq[b]:] = float("nan")
+        k[b, :, lk[b]:] = float("nan")
+        v[b, :, lk[b]:] = float("nan")
+    o, lse = A.fwd(q, k, v, **kw)
+    # the split forward takes the same copies
+    o_s, lse_s = A.fwd_splitkv(q, k, v, num_splits=3, **kw)
+    dq, dk, dv = A.bwd(q, k, v, o, lse, do, **kw)
+    torch.cuda.synchronize()
+    gpu = {"O": o, "lse": lse, "GQ": dq, "GK": dk, "GV": dv}
+    for nm, t in list(gpu.items()) + [("O_split", o_s), ("lse_split", lse_s)]:
+        assert torch.isfinite(t.float()).all(), f"{name}: {nm} not finite"
+    errs, ref = P.compare_full(inp, gpu)
+    P.assert_within(errs, dtype, name)
+    for b in range(B):
+        assert (P.to_f64(o[b, :, lq[b]:]) == 0).all() and (P.to_f64(dq[b, :, lq[b]:]) == 0).all()
+        assert (P.to_f64(o_s[b, :, lq[b]:]) == 0).all()
+        assert (P.to_f64(dk[b, :, lk[b]:]) == 0).all() and (P.to_f64(dv[b, :, lk[b]:]) == 0).all()
