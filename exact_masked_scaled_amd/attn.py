@@ -36,7 +36,8 @@ BF16 = 1
 # every symbol the header declares
 EXPORTS = ("attn_validate", "attn_bwd_workspace_size", "attn_fwd", "attn_bwd",
            "attn_bwd_dq", "attn_bwd_dkdv", "attn_fwd_splitkv_workspace_size", "attn_fwd_splitkv",
-           "attn_status_string", "attn_version")
+           "attn_rope_apply", "attn_fwd_rope_workspace_size", "attn_fwd_rope",
+           "attn_bwd_rope_workspace_size", "attn_bwd_rope", "attn_status_string", "attn_version")
 
 
 class AttnError(RuntimeError):
@@ -62,6 +63,10 @@ class Problem(ctypes.Structure):
                 ("v_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3),
                 ("cu_seqlens_q", ctypes.POINTER(ctypes.c_int32)),
                 ("cu_seqlens_k", ctypes.POINTER(ctypes.c_int32))]
+
+
+class Rope(ctypes.Structure):
+    _fields_ = [("cos_sin", ctypes.c_void_p), ("n_pos", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 _LIB = None
@@ -98,6 +103,17 @@ def lib():
     L.attn_fwd_splitkv_workspace_size.restype = ctypes.c_size_t
     L.attn_fwd_splitkv.argtypes = [P, M, vp, vp, vp, vp, vp, ctypes.c_int32, vp, ctypes.c_size_t, vp]
     L.attn_fwd_splitkv.restype = ctypes.c_int
+    R = ctypes.POINTER(Rope)
+    L.attn_rope_apply.argtypes = [P, M, R, ctypes.c_int32, ctypes.c_int32, vp, vp, vp]
+    L.attn_rope_apply.restype = ctypes.c_int
+    L.attn_fwd_rope_workspace_size.argtypes = [P]
+    L.attn_fwd_rope_workspace_size.restype = ctypes.c_size_t
+    L.attn_fwd_rope.argtypes = [P, M, R, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.attn_fwd_rope.restype = ctypes.c_int
+    L.attn_bwd_rope_workspace_size.argtypes = [P]
+    L.attn_bwd_rope_workspace_size.restype = ctypes.c_size_t
+    L.attn_bwd_rope.argtypes = [P, M, R, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.attn_bwd_rope.restype = ctypes.c_int
     L.attn_status_string.argtypes = [ctypes.c_int]
     L.attn_status_string.restype = ctypes.c_char_p
     L.attn_version.argtypes = []
@@ -401,3 +417,118 @@ class StagedBackward:
         self._check(lib().attn_bwd_dkdv(ctypes.byref(self.prob), ctypes.byref(self.mask), _ptr(q),
                                         _ptr(k), _ptr(v), _ptr(lse), _ptr(do), _ptr(dk), _ptr(dv),
                                         self.ws, self.ws_bytes, _stream(stream)), "attn_bwd_dkdv")
+
+
+# ---------------------------------------------------------------------------
+# rotary positions
+# ---------------------------------------------------------------------------
+def make_rope(cos_sin, n_pos: Optional[int] = None) -> Rope:
+    """cos_sin: contiguous float32 GPU tensor [n_pos, d_h / 2, 2] of (cos, sin),
+    or an integer device address with n_pos given (host-side checks only)."""
+    if isinstance(cos_sin, int) or cos_sin is None:
+        return Rope(ctypes.c_void_p(cos_sin or 0), int(n_pos or 0), 0)
+    torch = _torch()
+    if cos_sin.dtype != torch.float32 or not cos_sin.is_contiguous() or cos_sin.dim() != 3 \
+            or cos_sin.shape[-1] != 2:
+        raise ValueError("cos_sin must be a contiguous float32 [n_pos, d_h/2, 2] tensor")
+    return Rope(ctypes.c_void_p(cos_sin.data_ptr()), int(cos_sin.shape[0]), 0)
+
+
+def rope_workspace_size(prob: Problem, backward: bool) -> int:
+    fn = lib().attn_bwd_rope_workspace_size if backward else lib().attn_fwd_rope_workspace_size
+    return int(fn(ctypes.byref(prob)))
+
+
+def rope_apply(q, k, v, cos_sin, *, operand="q", inverse=False, out=None, causal=False, offset=0,
+               seqlens_q=None, seqlens_k=None, stream=None, cu_seqlens_q=None, cu_seqlens_k=None,
+               max_seqlen_q=None, max_seqlen_k=None):
+    """attn_rope_apply: q or k (operand "q" / "k") turned by its positions
+    (inverse: turned back).  ``out`` (default: a new tensor) must have the
+    strides of the input; it may be the input itself."""
+    torch = _torch()
+    nd = 3 if (cu_seqlens_q is not None or cu_seqlens_k is not None) else 4
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check4(name, t, q.dtype, nd)
+    x = q if operand == "q" else k
+    if out is None:
+        out = torch.empty_like(x)
+    if out.stride() != x.stride() or out.shape != x.shape:
+        raise ValueError("out must have the shape and strides of the input")
+    prob = _problem_from(q, k, v, None, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    mask, keep = make_mask(causal, offset, seqlens_q, seqlens_k)
+    rope = make_rope(cos_sin)
+    st = lib().attn_rope_apply(ctypes.byref(prob), ctypes.byref(mask), ctypes.byref(rope),
+                               0 if operand == "q" else 1, 1 if inverse else 0, _ptr(x), _ptr(out),
+                               _stream(stream))
+    del keep
+    if st != OK:
+        raise AttnError(st, "attn_rope_apply")
+    return out
+
+
+def fwd_rope(q, k, v, cos_sin, *, causal=False, offset=0, seqlens_q=None, seqlens_k=None, out=None,
+             lse=None, workspace=None, stream=None, cu_seqlens_q=None, cu_seqlens_k=None,
+             max_seqlen_q=None, max_seqlen_k=None):
+    """attn_fwd_rope: O and lse of attention on the rotated q and k."""
+    torch = _torch()
+    packed = cu_seqlens_q is not None or cu_seqlens_k is not None
+    nd = 3 if packed else 4
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check4(name, t, q.dtype, nd)
+    d_v = v.shape[-1]
+    if packed:
+        total_q, H_q, _ = q.shape
+        o_shape, lse_shape = (total_q, H_q, d_v), (H_q, total_q)
+    else:
+        B, H_q, n_q, _ = q.shape
+        o_shape, lse_shape = (B, H_q, n_q, d_v), (B, H_q, n_q)
+    if out is None:
+        out = torch.empty(*o_shape, dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty(*lse_shape, dtype=torch.float32, device=q.device)
+    _check4("out", out, q.dtype, nd)
+    if not lse.is_contiguous() or lse.dtype != torch.float32 or tuple(lse.shape) != lse_shape:
+        raise ValueError(f"lse must be contiguous float32 of shape {lse_shape}")
+    prob = _problem_from(q, k, v, _strides(out), cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    need = rope_workspace_size(prob, backward=False)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    mask, keep = make_mask(causal, offset, seqlens_q, seqlens_k)
+    rope = make_rope(cos_sin)
+    st = lib().attn_fwd_rope(ctypes.byref(prob), ctypes.byref(mask), ctypes.byref(rope), _ptr(q), _ptr(k),
+                             _ptr(v), _ptr(out), _ptr(lse), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+                             _stream(stream))
+    del keep
+    if st != OK:
+        raise AttnError(st, "attn_fwd_rope")
+    return out, lse
+
+
+def bwd_rope(q, k, v, o, lse, do, cos_sin, *, causal=False, offset=0, seqlens_q=None, seqlens_k=None,
+             dq=None, dk=None, dv=None, workspace=None, stream=None, cu_seqlens_q=None, cu_seqlens_k=None,
+             max_seqlen_q=None, max_seqlen_k=None):
+    """attn_bwd_rope: G_Q, G_K (turned back to the unrotated inputs) and G_V."""
+    torch = _torch()
+    nd = 3 if (cu_seqlens_q is not None or cu_seqlens_k is not None) else 4
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check4(name, t, q.dtype, nd)
+    if do.stride() != o.stride():
+        raise ValueError("do must have the strides of o")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if dq.stride() != q.stride() or dk.stride() != k.stride() or dv.stride() != v.stride():
+        raise ValueError("gradient strides must match their tensors")
+    prob = _problem_from(q, k, v, _strides(o), cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    need = rope_workspace_size(prob, backward=True)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    mask, keep = make_mask(causal, offset, seqlens_q, seqlens_k)
+    rope = make_rope(cos_sin)
+    st = lib().attn_bwd_rope(ctypes.byref(prob), ctypes.byref(mask), ctypes.byref(rope), _ptr(q), _ptr(k),
+                             _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
+                             _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(stream))
+    del keep
+    if st != OK:
+        raise AttnError(st, "attn_bwd_rope")
+    return dq, dk, dv

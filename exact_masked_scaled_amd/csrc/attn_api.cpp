@@ -28,6 +28,8 @@ void fill_common(KernelParams& kp, const attn_problem& p, const attn_mask& m) {
   kp.k_sb = p.k_stride[0]; kp.k_sh = p.k_stride[1]; kp.k_sr = p.k_stride[2];
   kp.v_sb = p.v_stride[0]; kp.v_sh = p.v_stride[1]; kp.v_sr = p.v_stride[2];
   kp.o_sb = p.o_stride[0]; kp.o_sh = p.o_stride[1]; kp.o_sr = p.o_stride[2];
+  kp.dq_sb = kp.q_sb; kp.dq_sh = kp.q_sh; kp.dq_sr = kp.q_sr;
+  kp.dk_sb = kp.k_sb; kp.dk_sh = kp.k_sh; kp.dk_sr = kp.k_sr;
   kp.H_q = p.H_q; kp.H_kv = p.H_kv; kp.n_q = p.n_q; kp.n_k = p.n_k;
   kp.group = p.H_q / p.H_kv;
   kp.causal = m.causal;
@@ -52,6 +54,17 @@ int32_t clamp_offset(int64_t off, int32_t n_k) {
   return (int32_t)std::min<int64_t>(std::max<int64_t>(off, 0), n_k);
 }
 
+// Active rows / valid keys of sequence b and its offset_b.
+int64_t seq_len_q(const attn_problem& p, const attn_mask& m, int b) {
+  if (p.cu_seqlens_q) return (int64_t)p.cu_seqlens_q[b + 1] - p.cu_seqlens_q[b];
+  return m.seqlens_q ? m.seqlens_q[b] : p.n_q;
+}
+int64_t seq_len_k(const attn_problem& p, const attn_mask& m, int b) {
+  if (p.cu_seqlens_k) return (int64_t)p.cu_seqlens_k[b + 1] - p.cu_seqlens_k[b];
+  return m.seqlens_k ? m.seqlens_k[b] : p.n_k;
+}
+int64_t seq_offset(const attn_mask& m, int b) { return m.causal_offsets ? m.causal_offsets[b] : m.causal_offset; }
+
 // Sequence chunk [b0, b0 + nb): per-sequence data and unit counts.
 void fill_chunk(KernelParams& kp, const attn_problem& p, const attn_mask& m, int b0, int nb) {
   kp.B = nb;
@@ -67,6 +80,9 @@ void fill_chunk(KernelParams& kp, const attn_problem& p, const attn_mask& m, int
       kp.lens_k[i] = m.seqlens_k ? m.seqlens_k[b] : p.n_k;
     }
     if (kp.has_offs) kp.offs[i] = clamp_offset(m.causal_offsets[b], p.n_k);
+    // rotary positions of the query rows start at offset_b (checked to fit
+    // the table for sequences with active rows)
+    if (kp.rope) kp.rope_pos[i] = seq_len_q(p, m, b) > 0 ? (int32_t)seq_offset(m, b) : 0;
   }
   kp.groups = nb * p.H_kv;
   kp.xcd_map = (kp.groups % 8 == 0) ? 1 : 0;
@@ -82,7 +98,7 @@ T* off(T* base, int64_t elems, size_t es) {
 }
 
 int chunk_size(const KernelParams& kp, int B) {
-  return (kp.has_lens || kp.has_offs) ? kMaxBatchChunk : std::max(B, 1);
+  return (kp.has_lens || kp.has_offs || kp.rope) ? kMaxBatchChunk : std::max(B, 1);
 }
 
 }  // namespace
@@ -218,14 +234,22 @@ struct BwdPtrs {
   void *dQ, *dK, *dV;
 };
 
-// Shared body of attn_bwd and its two passes: validate, check the pointers
-// the requested passes read or write, then enqueue them per sequence chunk.
-attn_status bwd_passes(const attn_problem* prob, const attn_mask* mask, const BwdPtrs& t,
-                       void* workspace, size_t workspace_bytes, void* stream, int passes) {
+// Rotated copies of Q and K the backward passes read instead of the caller's
+// (rotary positions): their element strides, and the rope flags.
+struct RopeCtx {
+  const float* cos_sin;
+  const void* Qt;
+  const void* Kt;
+  int64_t qt_s[3], kt_s[3];
+};
+
+// Checks of attn_bwd and its two passes: validate, then the pointers the
+// requested passes read or write and the workspace.
+attn_status bwd_check(const attn_problem* prob, const attn_mask* mask, const BwdPtrs& t, void* workspace,
+                      size_t workspace_bytes, int passes) {
   attn_status st = validate_problem(prob, mask);
   if (st != ATTN_OK) return st;
   const attn_problem& p = *prob;
-  const attn_mask& m = *mask;
   if (p.B == 0 || (p.n_q == 0 && p.n_k == 0)) return ATTN_OK;
   const bool has_q = p.n_q > 0, has_k = p.n_k > 0;
   auto ok = [](const void* ptr) { return ptr != nullptr && aligned16(ptr); };
@@ -241,10 +265,28 @@ attn_status bwd_passes(const attn_problem* prob, const attn_mask* mask, const Bw
   if (need_ws > 0 &&
       (workspace == nullptr || workspace_bytes < need_ws || ((uintptr_t)workspace % kWsAlign) != 0))
     return ATTN_ERR_WORKSPACE;
+  return ATTN_OK;
+}
+
+// Enqueue the requested passes per sequence chunk (arguments checked).
+attn_status bwd_enqueue(const attn_problem& p, const attn_mask& m, const BwdPtrs& t, float* delta, void* stream,
+                        int passes, const RopeCtx* rc) {
+  if (p.B == 0 || (p.n_q == 0 && p.n_k == 0)) return ATTN_OK;
+  const bool has_q = p.n_q > 0, has_k = p.n_k > 0;
   const size_t es = esize(p.dtype);
-  float* delta = (float*)workspace;
   KernelParams kp;
   fill_common(kp, p, m);
+  const void* Qsrc = t.Q;
+  const void* Ksrc = t.K;
+  int64_t q_sb = p.q_stride[0], k_sb = p.k_stride[0];
+  if (rc) {  // read the rotated copies; G_Q and G_K keep the caller's strides
+    kp.rope = kRopeDQ | kRopeDK;
+    kp.rope_cs = rc->cos_sin;
+    Qsrc = rc->Qt;
+    Ksrc = rc->Kt;
+    q_sb = rc->qt_s[0]; kp.q_sb = rc->qt_s[0]; kp.q_sh = rc->qt_s[1]; kp.q_sr = rc->qt_s[2];
+    k_sb = rc->kt_s[0]; kp.k_sb = rc->kt_s[0]; kp.k_sh = rc->kt_s[1]; kp.k_sr = rc->kt_s[2];
+  }
   const int nqblk = (p.n_q + bwd_dq_block_rows(p.dtype) - 1) / bwd_dq_block_rows(p.dtype);
   const int nkblk = (p.n_k + bwd_dkdv_block_keys(p.dtype) - 1) / bwd_dkdv_block_keys(p.dtype);
   const int cs = chunk_size(kp, p.B);
@@ -252,8 +294,8 @@ attn_status bwd_passes(const attn_problem* prob, const attn_mask* mask, const Bw
     const int nb = std::min(cs, p.B - b0);
     fill_chunk(kp, p, m, b0, nb);
     const int64_t row0 = b0 * kp.lse_sb;
-    kp.q = off(t.Q, b0 * p.q_stride[0], es);
-    kp.k = off(t.K, b0 * p.k_stride[0], es);
+    kp.q = off(Qsrc, b0 * q_sb, es);
+    kp.k = off(Ksrc, b0 * k_sb, es);
     kp.v = off(t.V, b0 * p.v_stride[0], es);
     kp.o = off(t.O, b0 * p.o_stride[0], es);
     kp.dout = off(t.dO, b0 * p.o_stride[0], es);
@@ -272,6 +314,13 @@ attn_status bwd_passes(const attn_problem* prob, const attn_mask* mask, const Bw
     }
   }
   return ATTN_OK;
+}
+
+attn_status bwd_passes(const attn_problem* prob, const attn_mask* mask, const BwdPtrs& t, void* workspace,
+                       size_t workspace_bytes, void* stream, int passes) {
+  const attn_status st = bwd_check(prob, mask, t, workspace, workspace_bytes, passes);
+  if (st != ATTN_OK) return st;
+  return bwd_enqueue(*prob, *mask, t, (float*)workspace, stream, passes, nullptr);
 }
 
 }  // namespace
@@ -299,6 +348,187 @@ attn_status attn_bwd_dkdv(const attn_problem* prob, const attn_mask* mask, const
   return bwd_passes(prob, mask, t, workspace, workspace_bytes, stream, kDkdv);
 }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------- rotary positions
+
+namespace {
+
+attn_status validate_rope(const attn_problem& p, const attn_mask& m, const attn_rope* r) {
+  if (r == nullptr || r->cos_sin == nullptr || !aligned16(r->cos_sin) || r->n_pos < 1 || r->reserved != 0)
+    return ATTN_ERR_INVALID_ARG;
+  for (int b = 0; b < p.B; ++b) {
+    if (seq_len_k(p, m, b) > r->n_pos) return ATTN_ERR_INVALID_ARG;
+    const int64_t lq = seq_len_q(p, m, b);
+    if (lq == 0) continue;
+    const int64_t off = seq_offset(m, b);
+    if (off < 0 || off > (int64_t)r->n_pos - lq) return ATTN_ERR_INVALID_ARG;
+  }
+  return ATTN_OK;
+}
+
+// A rotated copy in the workspace: rows of H heads x d columns, contiguous
+// ([B][H][n][d], or [total rows][H][d] in the packed layout).
+struct Rotated {
+  int64_t s[3];
+  size_t bytes;
+};
+Rotated rotated_layout(const attn_problem& p, bool keys) {
+  const int64_t H = keys ? p.H_kv : p.H_q, n = keys ? p.n_k : p.n_q, d = p.d_h;
+  const int32_t* cu = keys ? p.cu_seqlens_k : p.cu_seqlens_q;
+  Rotated r;
+  if (cu != nullptr) {
+    r.s[0] = 0; r.s[1] = d; r.s[2] = H * d;
+    r.bytes = (size_t)(p.B > 0 ? std::max(cu[p.B], 0) : 0) * H * d * esize(p.dtype);
+  } else {
+    r.s[0] = H * n * d; r.s[1] = n * d; r.s[2] = d;
+    r.bytes = (size_t)p.B * H * n * d * esize(p.dtype);
+  }
+  r.bytes = align_up(r.bytes, kWsAlign);
+  return r;
+}
+
+bool sizes_ok(const attn_problem* prob) {
+  return prob != nullptr && prob->B >= 0 && prob->H_q >= 0 && prob->H_kv >= 0 && prob->n_q >= 0 &&
+         prob->n_k >= 0 && prob->d_h >= 0;
+}
+
+// Rotate the active rows of every sequence (operand 0: Q rows at positions
+// i + offset_b; 1: K rows at positions j), per chunk of sequences.
+attn_status rope_enqueue(const attn_problem& p, const attn_mask& m, const float* cs, int operand, int inverse,
+                         const void* X, const int64_t xs[3], void* Y, const int64_t ys[3], void* stream) {
+  const bool keys = operand == 1;
+  const int32_t* cu = keys ? p.cu_seqlens_k : p.cu_seqlens_q;
+  const size_t es = esize(p.dtype);
+  RopeParams rp;
+  memset(&rp, 0, sizeof(rp));
+  rp.cs = cs;
+  rp.inverse = inverse;
+  rp.x_sb = xs[0]; rp.x_sh = xs[1]; rp.x_sr = xs[2];
+  rp.y_sb = ys[0]; rp.y_sh = ys[1]; rp.y_sr = ys[2];
+  rp.H = keys ? p.H_kv : p.H_q;
+  for (int b0 = 0; b0 < p.B; b0 += kMaxBatchChunk) {
+    const int nb = std::min(kMaxBatchChunk, p.B - b0);
+    rp.B = nb;
+    int32_t nmax = 0;
+    for (int i = 0; i < nb; ++i) {
+      const int b = b0 + i;
+      rp.len[i] = (int32_t)(keys ? seq_len_k(p, m, b) : seq_len_q(p, m, b));
+      rp.row0[i] = cu ? cu[b] : 0;
+      rp.pos0[i] = (!keys && rp.len[i] > 0) ? (int32_t)seq_offset(m, b) : 0;
+      nmax = std::max(nmax, rp.len[i]);
+    }
+    rp.n = nmax;
+    rp.x = off(X, b0 * xs[0], es);
+    rp.y = off(Y, b0 * ys[0], es);
+    if (launch_rope(rp, p.dtype, p.d_h, stream) != 0) return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_rope_apply(const attn_problem* prob, const attn_mask* mask, const attn_rope* rope,
+                            int32_t operand, int32_t inverse, const void* X, void* Y, void* stream) {
+  attn_status st = validate_problem(prob, mask);
+  if (st != ATTN_OK) return st;
+  const attn_problem& p = *prob;
+  const attn_mask& m = *mask;
+  if ((operand != 0 && operand != 1) || (inverse != 0 && inverse != 1)) return ATTN_ERR_INVALID_ARG;
+  st = validate_rope(p, m, rope);
+  if (st != ATTN_OK) return st;
+  if (p.B == 0 || (operand == 0 ? p.n_q : p.n_k) == 0) return ATTN_OK;
+  if (!X || !Y || !aligned16(X) || !aligned16(Y)) return ATTN_ERR_INVALID_ARG;
+  const int64_t* s = operand == 0 ? p.q_stride : p.k_stride;
+  return rope_enqueue(p, m, rope->cos_sin, operand, inverse, X, s, Y, s, stream);
+}
+
+size_t attn_fwd_rope_workspace_size(const attn_problem* prob) {
+  if (!sizes_ok(prob)) return 0;
+  return rotated_layout(*prob, true).bytes;
+}
+
+attn_status attn_fwd_rope(const attn_problem* prob, const attn_mask* mask, const attn_rope* rope, const void* Q,
+                          const void* K, const void* V, void* O, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  attn_status st = validate_problem(prob, mask);
+  if (st != ATTN_OK) return st;
+  const attn_problem& p = *prob;
+  const attn_mask& m = *mask;
+  st = validate_rope(p, m, rope);
+  if (st != ATTN_OK) return st;
+  if (p.B == 0 || p.n_q == 0) return ATTN_OK;
+  if (!Q || !O || !lse || !aligned16(Q) || !aligned16(O) || !aligned16(lse)) return ATTN_ERR_INVALID_ARG;
+  if (p.n_k > 0 && (!K || !V || !aligned16(K) || !aligned16(V))) return ATTN_ERR_INVALID_ARG;
+  const Rotated kt = rotated_layout(p, true);
+  if (kt.bytes > 0 && (workspace == nullptr || workspace_bytes < kt.bytes || ((uintptr_t)workspace % kWsAlign) != 0))
+    return ATTN_ERR_WORKSPACE;
+  // keys turned once into the workspace; queries turn in the forward's loads
+  if (p.n_k > 0) {
+    st = rope_enqueue(p, m, rope->cos_sin, 1, 0, K, p.k_stride, workspace, kt.s, stream);
+    if (st != ATTN_OK) return st;
+  }
+  const size_t es = esize(p.dtype);
+  KernelParams kp;
+  fill_common(kp, p, m);
+  kp.rope = kRopeQ;
+  kp.rope_cs = rope->cos_sin;
+  kp.k_sb = kt.s[0]; kp.k_sh = kt.s[1]; kp.k_sr = kt.s[2];
+  const int nqblk = (p.n_q + fwd_block_rows(p.dtype) - 1) / fwd_block_rows(p.dtype);
+  const int cs = chunk_size(kp, p.B);
+  for (int b0 = 0; b0 < p.B; b0 += cs) {
+    const int nb = std::min(cs, p.B - b0);
+    fill_chunk(kp, p, m, b0, nb);
+    kp.per_group = kp.group * nqblk;
+    kp.q = off(Q, b0 * p.q_stride[0], es);
+    kp.k = off((const void*)workspace, b0 * kt.s[0], es);
+    kp.v = off(V, b0 * p.v_stride[0], es);
+    kp.o_out = off(O, b0 * p.o_stride[0], es);
+    kp.lse = lse + b0 * kp.lse_sb;
+    if (launch_fwd(kp, p.dtype, p.d_h, p.d_v, stream) != 0) return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
+size_t attn_bwd_rope_workspace_size(const attn_problem* prob) {
+  if (!sizes_ok(prob)) return 0;
+  return attn_bwd_workspace_size(prob) + rotated_layout(*prob, false).bytes + rotated_layout(*prob, true).bytes;
+}
+
+attn_status attn_bwd_rope(const attn_problem* prob, const attn_mask* mask, const attn_rope* rope, const void* Q,
+                          const void* K, const void* V, const void* O, const float* lse, const void* dO, void* dQ,
+                          void* dK, void* dV, void* workspace, size_t workspace_bytes, void* stream) {
+  const BwdPtrs t{Q, K, V, O, dO, lse, dQ, dK, dV};
+  attn_status st = bwd_check(prob, mask, t, workspace, workspace_bytes, kDq | kDkdv);
+  if (st != ATTN_OK) return st;
+  const attn_problem& p = *prob;
+  const attn_mask& m = *mask;
+  st = validate_rope(p, m, rope);
+  if (st != ATTN_OK) return st;
+  if (p.B == 0 || (p.n_q == 0 && p.n_k == 0)) return ATTN_OK;
+  const size_t need = attn_bwd_rope_workspace_size(prob);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || ((uintptr_t)workspace % kWsAlign) != 0))
+    return ATTN_ERR_WORKSPACE;
+  const Rotated qt = rotated_layout(p, false), kt = rotated_layout(p, true);
+  char* ws = (char*)workspace;
+  RopeCtx rc;
+  rc.cos_sin = rope->cos_sin;
+  rc.Qt = ws + attn_bwd_workspace_size(prob);
+  rc.Kt = ws + attn_bwd_workspace_size(prob) + qt.bytes;
+  for (int i = 0; i < 3; ++i) { rc.qt_s[i] = qt.s[i]; rc.kt_s[i] = kt.s[i]; }
+  if (p.n_q > 0) {
+    st = rope_enqueue(p, m, rope->cos_sin, 0, 0, Q, p.q_stride, (void*)rc.Qt, qt.s, stream);
+    if (st != ATTN_OK) return st;
+  }
+  if (p.n_k > 0) {
+    st = rope_enqueue(p, m, rope->cos_sin, 1, 0, K, p.k_stride, (void*)rc.Kt, kt.s, stream);
+    if (st != ATTN_OK) return st;
+  }
+  return bwd_enqueue(p, m, t, (float*)workspace, stream, kDq | kDkdv, &rc);
+}
+
 const char* attn_status_string(attn_status s) {
   switch (s) {
     case ATTN_OK: return "ok";
@@ -311,6 +541,6 @@ const char* attn_status_string(attn_status s) {
   return "unknown status";
 }
 
-int32_t attn_version(void) { return 100; }
+int32_t attn_version(void) { return 200; }
 
 }  // extern "C"

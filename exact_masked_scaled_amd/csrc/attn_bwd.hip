@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(con
   const T* Vb = (const T*)p.v + b * p.v_sb + sv.k_row0 * p.v_sr + g * p.v_sh;
   const T* Ob = (const T*)p.o + b * p.o_sb + sv.q_row0 * p.o_sr + r * p.o_sh;
   const T* dOb = (const T*)p.dout + b * p.o_sb + sv.q_row0 * p.o_sr + r * p.o_sh;
-  T* dQb = (T*)p.dq + b * p.q_sb + sv.q_row0 * p.q_sr + r * p.q_sh;
+  T* dQb = (T*)p.dq + b * p.dq_sb + sv.q_row0 * p.dq_sr + r * p.dq_sh;
   const int64_t rowbase = b * p.lse_sb + r * p.lse_sh + sv.q_row0;
 
   // this lane's G_O row (B operand of dP^T = V G_O^T) and D_i = G_O . O
@@ -203,13 +203,23 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(con
 
   if (row_exists) {
     const float sc = row_active ? p.scale : 0.f;
+    // rotary positions: G_Q = R^T G_Q~ (the lane's four columns are two pairs)
+    const bool turn = (p.rope & kRopeDQ) && row_active;
+    const float* cs = p.rope_cs + (int64_t)(qi + p.rope_pos[b]) * DH;
 #pragma unroll
     for (int dt = 0; dt < DH / 32; ++dt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int d = 32 * dt + 8 * j + 4 * kg;
-        st4<T>(dQb + (int64_t)qi * p.q_sr + d, acc[dt][4 * j] * sc, acc[dt][4 * j + 1] * sc,
-               acc[dt][4 * j + 2] * sc, acc[dt][4 * j + 3] * sc);
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[dt][4 * j + e] * sc;
+        if (turn) {
+          const f32x4 t = *reinterpret_cast<const f32x4*>(cs + d);
+          rope_pair(t[0], -t[1], v[0], v[1]);
+          rope_pair(t[2], -t[3], v[2], v[3]);
+        }
+        st4<T>(dQb + (int64_t)qi * p.dq_sr + d, v[0], v[1], v[2], v[3]);
       }
   }
 }
@@ -263,7 +273,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const KernelParams p) 
 
   const T* Kb = (const T*)p.k + b * p.k_sb + sv.k_row0 * p.k_sr + g * p.k_sh;
   const T* Vb = (const T*)p.v + b * p.v_sb + sv.k_row0 * p.v_sr + g * p.v_sh;
-  T* dKb = (T*)p.dk + b * p.k_sb + sv.k_row0 * p.k_sr + g * p.k_sh;
+  T* dKb = (T*)p.dk + b * p.dk_sb + sv.k_row0 * p.dk_sr + g * p.dk_sh;
   T* dVb = (T*)p.dv + b * p.v_sb + sv.k_row0 * p.v_sr + g * p.v_sh;
 
   f32x16 dk[KT][DH / 32], dv[KT][DV / 32];
@@ -480,6 +490,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const KernelParams p) 
   }
 
   // store G_K (scaled) and G_V; lane = d, registers = keys
+  const bool turn = (p.rope & kRopeDK) != 0, odd = (lane & 1) != 0;
 #pragma unroll
   for (int kt = 0; kt < KT; ++kt) {
     const int kbase = kw0 + 32 * kt;
@@ -488,7 +499,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const KernelParams p) 
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int key = kbase + 8 * (e >> 2) + 4 * kg + (e & 3);
-        if (key < nk_lim) dKb[(int64_t)key * p.k_sr + 32 * nt + (lane & 31)] = (T)(dk[kt][nt][e] * p.scale);
+        float val = dk[kt][nt][e] * p.scale;
+        if (turn) {  // rotary positions: G_K = R^T G_K~, key at position key
+          float c = 1.f, sn = 0.f;
+          if (key < Lk) {
+            const float* t = p.rope_cs + (int64_t)key * DH + ((32 * nt + (lane & 31)) & ~1);
+            c = t[0];
+            sn = t[1];
+          }
+          val = rope_back_lanes(val, c, sn, odd);
+        }
+        if (key < nk_lim) dKb[(int64_t)key * p.dk_sr + 32 * nt + (lane & 31)] = (T)val;
       }
 #pragma unroll
     for (int nt = 0; nt < DV / 32; ++nt)
@@ -586,7 +607,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
 
   const T* Kb = (const T*)p.k + b * p.k_sb + sv.k_row0 * p.k_sr + g * p.k_sh;
   const T* Vb = (const T*)p.v + b * p.v_sb + sv.k_row0 * p.v_sr + g * p.v_sh;
-  T* dKb = (T*)p.dk + b * p.k_sb + sv.k_row0 * p.k_sr + g * p.k_sh;
+  T* dKb = (T*)p.dk + b * p.dk_sb + sv.k_row0 * p.dk_sr + g * p.dk_sh;
   T* dVb = (T*)p.dv + b * p.v_sb + sv.k_row0 * p.v_sr + g * p.v_sh;
 
   // XS: R[0, KB_S) this lane's K rows of both 32-key blocks (operand
@@ -928,8 +949,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
   }
 
   // store: YV holds G_V, YK G_K (scaled) of both key blocks; lane = column, registers = keys
-  auto store = [&](auto NTC, T* dst, int64_t sr, float sc) __attribute__((always_inline)) {
+  auto store = [&](auto NTC, auto TURN, T* dst, int64_t sr, float sc) __attribute__((always_inline)) {
     constexpr int NT = decltype(NTC)::value;
+    constexpr bool turn = decltype(TURN)::value;
+    const bool odd = (lane & 1) != 0;
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
@@ -937,12 +960,23 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int kk = kh0 + 32 * kb2 + 8 * (e >> 2) + 4 * kg + (e & 3);
-          if (kk < nk_lim) dst[(int64_t)kk * sr + 32 * nt + (lane & 31)] = (T)(R[kb2 * NT + nt][e] * sc);
+          float val = R[kb2 * NT + nt][e] * sc;
+          if constexpr (turn) {  // rotary positions: G_K = R^T G_K~, key at position kk
+            float c = 1.f, sn = 0.f;
+            if (kk < Lk) {
+              const float* t = p.rope_cs + (int64_t)kk * DH + ((32 * nt + (lane & 31)) & ~1);
+              c = t[0];
+              sn = t[1];
+            }
+            val = rope_back_lanes(val, c, sn, odd);
+          }
+          if (kk < nk_lim) dst[(int64_t)kk * sr + 32 * nt + (lane & 31)] = (T)val;
         }
   };
   if (!is_x) {
-    if (is_s) store(IC<DV / 32>(), dVb, p.v_sr, 1.f);
-    else store(IC<DH / 32>(), dKb, p.k_sr, p.scale);
+    if (is_s) store(IC<DV / 32>(), IC<0>(), dVb, p.v_sr, 1.f);
+    else if (p.rope & kRopeDK) store(IC<DH / 32>(), IC<1>(), dKb, p.dk_sr, p.scale);
+    else store(IC<DH / 32>(), IC<0>(), dKb, p.dk_sr, p.scale);
   }
 }
 

@@ -264,6 +264,16 @@ template <> __device__ __forceinline__ void st4<float>(float* p, float a, float 
   *reinterpret_cast<f32x4*>(p) = v;
 }
 
+// 8 consecutive elements (16-byte aligned) from an operand register.
+template <typename T> __device__ __forceinline__ void st8(T* p, const typename Op<T>::type& x);
+template <> __device__ __forceinline__ void st8<__bf16>(__bf16* p, const bf16x8& x) {
+  *reinterpret_cast<bf16x8*>(p) = x;
+}
+template <> __device__ __forceinline__ void st8<float>(float* p, const f32x8& x) {
+  st4<float>(p, x[0], x[1], x[2], x[3]);
+  st4<float>(p + 4, x[4], x[5], x[6], x[7]);
+}
+
 // ---------------------------------------------------------------- tile staging
 // Copies ROWS rows of a row-major [n][D] global tensor (unit stride in d, row
 // stride in elements) into an LDS tile laid out as Tile<T, D>, with direct
@@ -361,6 +371,46 @@ __device__ __forceinline__ bool map_work(int wg, int groups, int per_group, int 
   item = slot - t * per_group;
   unit = xcd + 8 * t;
   return unit < groups;
+}
+
+// ---------------------------------------------------------------- rotary positions
+// Column pair (2k, 2k+1) of a row at position t turns by the angle whose
+// cosine and sine the table holds at [t][k] ("Chapter 15: matrix formulas to
+// look up", sec. 15.6): x0' = c x0 - s x1, x1' = s x0 + c x1.  Passing -s
+// turns back (the backward's transposed rotation, "Chapter 31: attention
+// backpropagation", sec. 5).  Every rotation in the library goes through
+// this one expression, so a row turned in registers equals the same row
+// turned by the standalone kernel bit for bit.
+__device__ __forceinline__ void rope_pair(float c, float s, float& x0, float& x1) {
+  const float y0 = fmaf(c, x0, -(s * x1));
+  const float y1 = fmaf(s, x0, c * x1);
+  x0 = y0;
+  x1 = y1;
+}
+
+// Eight consecutive columns (starting at an even column c0) of a row:
+// cs8 = table row + c0 holds (cos, sin) of the four pairs in order.
+template <typename T>
+__device__ __forceinline__ typename Op<T>::type rope8(const typename Op<T>::type& x, const float* cs8, bool inverse) {
+  const f32x4 t0 = *reinterpret_cast<const f32x4*>(cs8);
+  const f32x4 t1 = *reinterpret_cast<const f32x4*>(cs8 + 4);
+  const float tab[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+  float v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = (float)x[e];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) rope_pair(tab[2 * m], inverse ? -tab[2 * m + 1] : tab[2 * m + 1], v[2 * m], v[2 * m + 1]);
+  return to_op<T>(v);
+}
+
+// A value of column c whose pair partner (column c ^ 1) sits in lane ^ 1:
+// turn the pair back by the angle of cs2 = table row + (c & ~1) and keep
+// this lane's column.  Every lane of the wave must call it (lane exchange).
+__device__ __forceinline__ float rope_back_lanes(float v, float c, float s, bool odd) {
+  const float pv = __shfl_xor(v, 1);
+  float x0 = odd ? pv : v, x1 = odd ? v : pv;
+  rope_pair(c, -s, x0, x1);
+  return odd ? x1 : x0;
 }
 
 }  // namespace attn

@@ -115,6 +115,13 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(const 
 #pragma unroll
     for (int ks = 0; ks < DH / 16; ++ks)
       qreg[ks] = row_active ? ld8<T>(Qb + (int64_t)qi * p.q_sr + 16 * ks + 8 * kg) : zero_op<T>();
+    if (p.rope & kRopeQ) {
+      // rotary positions: the lane's row at position qi + rope_pos[b]
+      const float* cs = p.rope_cs + (int64_t)(qi + p.rope_pos[b]) * DH + 8 * kg;
+      if (row_active)
+#pragma unroll
+        for (int ks = 0; ks < DH / 16; ++ks) qreg[ks] = rope8<T>(qreg[ks], cs + 16 * ks, false);
+    }
 
     RowOffsets<T, DH> kro;
     TrOffsets<T, DV> vto;

@@ -31,6 +31,8 @@ struct KernelParams {
   int64_t k_sb, k_sh, k_sr;
   int64_t v_sb, v_sh, v_sr;
   int64_t o_sb, o_sh, o_sr;
+  int64_t dq_sb, dq_sh, dq_sr;  // G_Q (the strides of Q unless Q is a rotated copy)
+  int64_t dk_sb, dk_sh, dk_sr;  // G_K (likewise for K)
   int32_t B, H_q, H_kv, n_q, n_k;
   int32_t group;        // H_q / H_kv
   int32_t causal;       // 0/1
@@ -52,11 +54,39 @@ struct KernelParams {
   float* part_o;
   float* part_lse;
   int64_t part_rows;
+  // rotary positions: table [n_pos][d_h/2][2] of (cos, sin); rope flags say
+  // which operand a kernel turns (kRopeQ: Q rows as loaded, forward;
+  // kRopeDQ / kRopeDK: G_Q / G_K turned back in the stores); query row i of
+  // sequence b sits at position i + rope_pos[b], key j at j
+  const float* rope_cs;
+  int32_t rope;
   int32_t lens_q[kMaxBatchChunk];
   int32_t lens_k[kMaxBatchChunk];
   int32_t offs[kMaxBatchChunk];    // causal offsets, clamped to [0, n_k]
   int32_t row0_q[kMaxBatchChunk];  // packed layout: first row of each sequence
   int32_t row0_k[kMaxBatchChunk];
+  int32_t rope_pos[kMaxBatchChunk];
+};
+
+// kernel arguments are limited to 4 KiB
+static_assert(sizeof(KernelParams) <= 4096, "kernel arguments too large");
+
+enum : int32_t { kRopeQ = 1, kRopeDQ = 2, kRopeDK = 4 };
+
+// The standalone rotation: rows i < len[b] of sequence b (first row row0[b]
+// in the packed layout) at positions i + pos0[b], all heads; 8 columns per
+// thread.
+struct RopeParams {
+  const void* x;
+  void* y;
+  const float* cs;
+  int64_t x_sb, x_sh, x_sr;
+  int64_t y_sb, y_sh, y_sr;
+  int32_t B, H, n;   // sequences of this launch, heads, row bound
+  int32_t inverse;
+  int32_t len[kMaxBatchChunk];
+  int32_t row0[kMaxBatchChunk];
+  int32_t pos0[kMaxBatchChunk];
 };
 
 // Host-only validation; pure C++ (no HIP), shared by attn_validate/fwd/bwd.
@@ -70,6 +100,7 @@ int launch_bwd_dkdv(const KernelParams& p, int dtype, int d_h, int d_v, void* st
 // forward split over the keys (p.splits > 1): partial pass, then the merge
 int launch_fwd_split(const KernelParams& p, int dtype, int d_h, int d_v, void* stream);
 int launch_fwd_combine(const KernelParams& p, int dtype, int d_v, void* stream);
+int launch_rope(const RopeParams& p, int dtype, int d_h, void* stream);
 
 // Tile sizes the dispatcher needs to size grids.
 int fwd_block_rows(int dtype);

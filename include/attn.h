@@ -179,6 +179,61 @@ attn_status attn_bwd_dkdv(const attn_problem* prob, const attn_mask* mask,
                           const float* lse, const void* dO, void* dK, void* dV,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------- rotary positions
+ * Attention on rotated queries and keys ("Chapter 15: matrix formulas to look
+ * up", math.zhuph.uk, sec. 15.6): q~_i = R_i q_i, k~_j = R_j k_j, where R_t
+ * turns every adjacent column pair (2k, 2k+1) of a row at position t by the
+ * angle theta(t, k):
+ *   x~_2k = cos x_2k - sin x_2k+1,   x~_2k+1 = sin x_2k + cos x_2k+1,
+ * so q~_i . k~_j depends on the positions only through j - i when theta is
+ * position times a fixed frequency.  V is not rotated.  The backward turns the
+ * gradients of q~ and k~ back by -theta ("Chapter 31: attention
+ * backpropagation" (eonloom handbook), sec. 5): G_Q = R^T G_Q~, G_K = R^T G_K~.
+ *
+ * Positions: key j of sequence b sits at position j; query row i at
+ * i + offset_b, with offset_b the sequence's causal offset (causal_offsets[b]
+ * or causal_offset), used for the positions even when causal == 0.  Every
+ * sequence needs L_k[b] <= n_pos and, when it has active rows,
+ * 0 <= offset_b and offset_b + L_q[b] <= n_pos (else ATTN_ERR_INVALID_ARG).
+ * Rows past L_q[b] and keys past L_k[b] are not rotated. */
+typedef struct {
+  const float* cos_sin; /* DEVICE float32 [n_pos][d_h / 2][2]: (cos theta, sin
+                           theta) of position t, pair k; 16-byte aligned       */
+  int32_t n_pos;        /* positions in the table, >= 1                        */
+  int32_t reserved;     /* must be 0                                           */
+} attn_rope;
+
+/* Rotate the rows of a Q-shaped (operand == 0: H_q heads, n_q rows, strides
+ * q_stride, positions i + offset_b, rows i < L_q[b]) or K-shaped (operand ==
+ * 1: H_kv heads, n_k rows, k_stride, positions j, rows j < L_k[b]) tensor by
+ * R (inverse == 0) or R^T (inverse == 1).  Y has the strides of X and may be
+ * X itself (in place); rows past the active ones are not written.  The
+ * rotation is computed in float32 and rounded once to the payload type. */
+attn_status attn_rope_apply(const attn_problem* prob, const attn_mask* mask, const attn_rope* rope,
+                            int32_t operand, int32_t inverse, const void* X, void* Y, void* stream);
+
+/* Forward with rotary positions: O and lse of attention on q~ and k~.  The
+ * queries are rotated in registers as they are loaded; the keys are rotated
+ * once into the workspace (attn_fwd_rope_workspace_size(prob) bytes, 256-byte
+ * aligned, contents on entry ignored).  Other arguments as attn_fwd. */
+size_t attn_fwd_rope_workspace_size(const attn_problem* prob);
+attn_status attn_fwd_rope(const attn_problem* prob, const attn_mask* mask, const attn_rope* rope,
+                          const void* Q, const void* K, const void* V, void* O, float* lse,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward with rotary positions: from the unrotated Q and K, the forward's O
+ * and lse, and G_O, writes G_Q = R^T G_Q~, G_K = R^T G_K~ and G_V.  q~ and k~
+ * are rotated into the workspace (attn_bwd_rope_workspace_size(prob) bytes,
+ * 256-byte aligned: D, then q~, then k~, in contiguous layouts), and the
+ * turn back of G_Q~ and G_K~ happens in the two passes' stores (no rounding
+ * of the rotated gradients in between).  Other arguments as attn_bwd. */
+size_t attn_bwd_rope_workspace_size(const attn_problem* prob);
+attn_status attn_bwd_rope(const attn_problem* prob, const attn_mask* mask, const attn_rope* rope,
+                          const void* Q, const void* K, const void* V,
+                          const void* O, const float* lse, const void* dO,
+                          void* dQ, void* dK, void* dV,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* attn_status_string(attn_status status);
 

@@ -183,3 +183,55 @@ def test_splitkv_workspace_and_errors():
     st = L.attn_fwd_splitkv(ctypes.byref(p), ctypes.byref(m2), fake, fake, fake, fake, fake, 4, fake,
                             ctypes.c_size_t(1 << 30), null)
     assert st == A.EMPTY_ROW
+
+
+def test_rope_struct_and_workspace():
+    lib_or_skip()
+    assert ctypes.sizeof(A.Rope) == 16 and A.Rope.n_pos.offset == 8
+    p = prob(B=2, H_q=4, H_kv=2, n_q=100, n_k=130, d_h=128, d_v=64)
+    kt = 2 * 2 * 130 * 128 * 2  # rotated keys, bf16, contiguous
+    qt = 2 * 4 * 100 * 128 * 2
+    al = lambda x: (x + 255) // 256 * 256
+    assert A.rope_workspace_size(p, backward=False) == al(kt)
+    assert A.rope_workspace_size(p, backward=True) == A.workspace_size(p) + al(qt) + al(kt)
+    pk = packed([0, 10, 30], [0, 20, 40])
+    assert A.rope_workspace_size(pk, backward=False) == al(40 * 2 * 128 * 2)
+    assert A.rope_workspace_size(pk, backward=True) == A.workspace_size(pk) + al(30 * 4 * 128 * 2) + al(40 * 2 * 128 * 2)
+
+
+def test_rope_argument_errors():
+    """Rotary-position calls reject a bad table, positions past it and bad
+    operands before anything is enqueued (no device here)."""
+    L = lib_or_skip()
+    p = prob(B=2, n_q=100, n_k=130)
+    null = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(0x10000)
+    big = ctypes.c_size_t(1 << 40)
+
+    def fwd(rope, **mk):
+        m, keep = A.make_mask(**mk)
+        return L.attn_fwd_rope(ctypes.byref(p), ctypes.byref(m), ctypes.byref(rope), fake, fake, fake, fake, fake,
+                               fake, big, null)
+
+    def apply(rope, operand=0, inverse=0, **mk):
+        m, keep = A.make_mask(**mk)
+        return L.attn_rope_apply(ctypes.byref(p), ctypes.byref(m), ctypes.byref(rope), operand, inverse, fake,
+                                 fake, null)
+
+    assert fwd(A.make_rope(0, 200)) == A.INVALID_ARG                  # no table
+    assert fwd(A.make_rope(0x10004, 200)) == A.INVALID_ARG            # misaligned table
+    assert fwd(A.Rope(fake, 200, 1)) == A.INVALID_ARG                 # reserved != 0
+    assert fwd(A.make_rope(0x10000, 129)) == A.INVALID_ARG            # keys past the table
+    # query positions i + offset_b must fit: 100 rows at offset 30 need 130
+    assert fwd(A.make_rope(0x10000, 130), causal=True, offset=31) == A.INVALID_ARG
+    assert fwd(A.make_rope(0x10000, 130), causal=False, offset=[0, -1]) == A.INVALID_ARG
+    # ...except for sequences without active rows
+    assert apply(A.make_rope(0x10000, 130), 0, 2, offset=[0, 500], seqlens_q=[100, 0]) == A.INVALID_ARG  # bad flag
+    assert apply(A.make_rope(0x10000, 130), 2, 0) == A.INVALID_ARG   # bad operand
+    # the attention checks still come first
+    assert fwd(A.make_rope(0x10000, 10), causal=True, offset=-1) == A.EMPTY_ROW
+    # backward: too small a workspace
+    m, keep = A.make_mask()
+    st = L.attn_bwd_rope(ctypes.byref(p), ctypes.byref(m), ctypes.byref(A.make_rope(0x10000, 200)), fake, fake,
+                         fake, fake, fake, fake, fake, fake, fake, fake, ctypes.c_size_t(A.workspace_size(p)), null)
+    assert st == A.WORKSPACE
