@@ -225,6 +225,65 @@ def measure_forward_split(torch, attn, W, wl, steps, warmup):
     return out, work
 
 
+def measure_rope(torch, attn, W, wl, steps, warmup):
+    """Rotary positions on the same workload: forward and backward with the
+    rotation (attn_fwd_rope, attn_bwd_rope) against without (attn_fwd,
+    attn_bwd), and the standalone rotation of Q; ms per call, inputs resident."""
+    import numpy as np
+
+    inp = W.make_inputs(wl)
+    kw = inp.mask_kwargs()
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+    q, k, v, do = dev(inp.Q), dev(inp.K), dev(inp.V), dev(inp.GO)
+    cs = torch.from_numpy(W.rotary_table(max(wl.n_q, wl.n_k) + max(wl.offset, 0), wl.d_h)).cuda()
+    # each backward reads the O and lse of its own forward
+    o, o_r = (torch.empty(wl.B, wl.H_q, wl.n_q, wl.d_v, dtype=q.dtype, device=q.device) for _ in range(2))
+    lse, lse_r = (torch.empty(wl.B, wl.H_q, wl.n_q, dtype=torch.float32, device=q.device) for _ in range(2))
+    dq, dk, dv, qt = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(q)
+    prob = attn._problem_from(q, k, v, attn._strides(o))
+    ws = torch.empty(max(attn.rope_workspace_size(prob, backward=True), 1), dtype=torch.uint8, device=q.device)
+    stream = torch.cuda.current_stream()
+    calls = {
+        "fwd": lambda: attn.fwd(q, k, v, out=o, lse=lse, stream=stream, **kw),
+        "bwd": lambda: attn.bwd(q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws, stream=stream, **kw),
+        "fwd_rope": lambda: attn.fwd_rope(q, k, v, cs, out=o_r, lse=lse_r, workspace=ws, stream=stream, **kw),
+        "bwd_rope": lambda: attn.bwd_rope(q, k, v, o_r, lse_r, do, cs, dq=dq, dk=dk, dv=dv, workspace=ws,
+                                          stream=stream, **kw),
+        "rotate_q": lambda: attn.rope_apply(q, k, v, cs, operand="q", out=qt, stream=stream, **kw),
+    }
+    # the calls interleaved, one event pair each, medians over the steps (so
+    # clock and cache state drift affects every variant alike)
+    for _ in range(warmup):
+        for fn in calls.values():
+            fn()
+    evs = {n: [] for n in calls}
+    for _ in range(steps):
+        for name, fn in calls.items():
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            evs[name].append((e0, e1))
+    torch.cuda.synchronize()
+    out = {n: float(np.median([a.elapsed_time(b) for a, b in ev])) for n, ev in evs.items()}
+    rows_q = sum(inp.seqlens_q) if inp.seqlens_q else wl.B * wl.n_q
+    es = 2 if wl.dtype == W.BF16 else 4
+    rot_bytes = 2 * rows_q * wl.H_q * wl.d_h * es  # each active Q element read and written once
+    del q, k, v, do, o, lse, o_r, lse_r, dq, dk, dv, qt, ws, cs
+    return {"workload": wl.name,
+            "fwd_ms": round(out["fwd"], 4), "fwd_rope_ms": round(out["fwd_rope"], 4),
+            "bwd_ms": round(out["bwd"], 4), "bwd_rope_ms": round(out["bwd_rope"], 4),
+            "step_overhead_pct": round(100 * (out["fwd_rope"] + out["bwd_rope"] - out["fwd"] - out["bwd"])
+                                       / (out["fwd"] + out["bwd"]), 2),
+            "rotate_q_ms": round(out["rotate_q"], 4),
+            "rotate_q_GB/s_algorithmic": round(rot_bytes / (out["rotate_q"] * 1e-3) / 1e9, 1),
+            "steps": steps, "warmup": warmup}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -350,6 +409,8 @@ def main(argv=None):
                    "unsplit_TFLOP/s": round(fw["fwd_flop"] / (t["unsplit"] * 1e-3) / 1e12, 2)}
             fsplit.append(ent)
         result["forward_splitkv"] = fsplit
+        # rotary positions on the headline workload
+        result["rotary"] = measure_rope(torch, attn, W, wl, 10, 3)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)

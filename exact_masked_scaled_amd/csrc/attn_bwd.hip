@@ -203,9 +203,23 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(con
 
   if (row_exists) {
     const float sc = row_active ? p.scale : 0.f;
-    // rotary positions: G_Q = R^T G_Q~ (the lane's four columns are two pairs)
-    const bool turn = (p.rope & kRopeDQ) && row_active;
-    const float* cs = p.rope_cs + (int64_t)(qi + p.rope_pos[b]) * DH;
+    // rotary positions: G_Q = R^T G_Q~ (the lane's four columns are two
+    // pairs); inactive rows (zeros) read an active row's table entries
+    const bool turn = (p.rope & kRopeDQ) != 0;
+    f32x4 tab[DH / 32][4];
+    if (turn) {
+      // all of the row's table entries in flight at once (pinned so the
+      // compiler keeps the loads together)
+      const float* cs = p.rope_cs + (int64_t)(max(min(qi, Lq - 1), 0) + p.rope_pos[b]) * DH;
+#pragma unroll
+      for (int dt = 0; dt < DH / 32; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) tab[dt][j] = *reinterpret_cast<const f32x4*>(cs + 32 * dt + 8 * j + 4 * kg);
+#pragma unroll
+      for (int dt = 0; dt < DH / 32; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(tab[dt][j]));
+    }
 #pragma unroll
     for (int dt = 0; dt < DH / 32; ++dt)
 #pragma unroll
@@ -215,9 +229,10 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(con
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = acc[dt][4 * j + e] * sc;
         if (turn) {
-          const f32x4 t = *reinterpret_cast<const f32x4*>(cs + d);
+          const f32x4 t = tab[dt][j];
           rope_pair(t[0], -t[1], v[0], v[1]);
           rope_pair(t[2], -t[3], v[2], v[3]);
+          if (!row_active) v[0] = v[1] = v[2] = v[3] = 0.f;
         }
         st4<T>(dQb + (int64_t)qi * p.dq_sr + d, v[0], v[1], v[2], v[3]);
       }
@@ -501,13 +516,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const KernelParams p) 
         const int key = kbase + 8 * (e >> 2) + 4 * kg + (e & 3);
         float val = dk[kt][nt][e] * p.scale;
         if (turn) {  // rotary positions: G_K = R^T G_K~, key at position key
-          float c = 1.f, sn = 0.f;
-          if (key < Lk) {
-            const float* t = p.rope_cs + (int64_t)key * DH + ((32 * nt + (lane & 31)) & ~1);
-            c = t[0];
-            sn = t[1];
-          }
-          val = rope_back_lanes(val, c, sn, odd);
+          const int kc = max(min(key, Lk - 1), 0);
+          float2 t = *reinterpret_cast<const float2*>(p.rope_cs + (int64_t)kc * DH +
+                                                      ((32 * nt + (lane & 31)) & ~1));
+          asm volatile("" : "+v"(t.x), "+v"(t.y));
+          const float turned = rope_back_lanes(val, t.x, t.y, odd);
+          val = key < Lk ? turned : val;
         }
         if (key < nk_lim) dKb[(int64_t)key * p.dk_sr + 32 * nt + (lane & 31)] = (T)val;
       }
@@ -956,22 +970,34 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
+      for (int nt = 0; nt < NT; ++nt) {
+        float2 t[16];
+        if constexpr (turn) {
+          // rotary positions: G_K = R^T G_K~, key kk at position kk.  The
+          // 16 table entries are read up front, clamped into the valid keys
+          // (whose rows exist), and pinned by an empty asm so the compiler
+          // cannot sink each load into its guarded store and wait for them
+          // one at a time; keys past L_k keep their exact zeros.
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int kk = kh0 + 32 * kb2 + 8 * (e >> 2) + 4 * kg + (e & 3);
+            const int kc = max(min(kk, Lk - 1), 0);
+            t[e] = *reinterpret_cast<const float2*>(p.rope_cs + (int64_t)kc * DH + ((32 * nt + (lane & 31)) & ~1));
+          }
+#pragma unroll
+          for (int e = 0; e < 16; ++e) asm volatile("" : "+v"(t[e].x), "+v"(t[e].y));
+        }
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int kk = kh0 + 32 * kb2 + 8 * (e >> 2) + 4 * kg + (e & 3);
           float val = R[kb2 * NT + nt][e] * sc;
-          if constexpr (turn) {  // rotary positions: G_K = R^T G_K~, key at position kk
-            float c = 1.f, sn = 0.f;
-            if (kk < Lk) {
-              const float* t = p.rope_cs + (int64_t)kk * DH + ((32 * nt + (lane & 31)) & ~1);
-              c = t[0];
-              sn = t[1];
-            }
-            val = rope_back_lanes(val, c, sn, odd);
+          if constexpr (turn) {
+            const float turned = rope_back_lanes(val, t[e].x, t[e].y, odd);
+            val = kk < Lk ? turned : val;
           }
           if (kk < nk_lim) dst[(int64_t)kk * sr + 32 * nt + (lane & 31)] = (T)val;
         }
+      }
   };
   if (!is_x) {
     if (is_s) store(IC<DV / 32>(), IC<0>(), dVb, p.v_sr, 1.f);

@@ -115,13 +115,6 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(const 
 #pragma unroll
     for (int ks = 0; ks < DH / 16; ++ks)
       qreg[ks] = row_active ? ld8<T>(Qb + (int64_t)qi * p.q_sr + 16 * ks + 8 * kg) : zero_op<T>();
-    if (p.rope & kRopeQ) {
-      // rotary positions: the lane's row at position qi + rope_pos[b]
-      const float* cs = p.rope_cs + (int64_t)(qi + p.rope_pos[b]) * DH + 8 * kg;
-      if (row_active)
-#pragma unroll
-        for (int ks = 0; ks < DH / 16; ++ks) qreg[ks] = rope8<T>(qreg[ks], cs + 16 * ks, false);
-    }
 
     RowOffsets<T, DH> kro;
     TrOffsets<T, DV> vto;
@@ -133,6 +126,14 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(const 
     using VL = TileLoad<T, C::BN, DV, 64 * C::NW>;
     KL::issue(Kb, p.k_sr, t_lo * C::BN, Lk, k_lds0, tid);
     VL::issue(Vb, p.v_sr, t_lo * C::BN, Lk, v_lds0, tid);
+    if (p.rope & kRopeQ) {
+      // rotary positions: the lane's row at position qi + rope_pos[b], turned
+      // while the first tiles are in flight
+      // (inactive rows hold zeros and read an active row's entries)
+      const float* cs = p.rope_cs + (int64_t)(max(min(qi, Lq - 1), 0) + p.rope_pos[b]) * DH + 8 * kg;
+#pragma unroll
+      for (int ks = 0; ks < DH / 16; ++ks) qreg[ks] = rope8<T>(qreg[ks], cs + 16 * ks, false);
+    }
     wait_tile_loads();
     __syncthreads();
 

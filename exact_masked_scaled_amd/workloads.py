@@ -171,6 +171,16 @@ def make_inputs(wl, seed: Optional[int] = None, with_grad: bool = True,
     return Inputs(wl, seed, lq, lk, Q, K, V, GO)
 
 
+def rotary_table(n_pos: int, d_h: int, base: float = 10000.0) -> np.ndarray:
+    """The cos/sin table a caller hands to the rotary-position calls, an input
+    like Q or K: [n_pos, d_h/2, 2] float32 of (cos, sin) of the angle
+    t * base^(-2k/d_h) for position t and column pair k (geometric
+    frequencies, one common choice of the fixed per-pair frequency)."""
+    k = np.arange(d_h // 2)
+    theta = np.arange(n_pos)[:, None] * (base ** (-2.0 * k / d_h))[None, :]
+    return np.stack([np.cos(theta), np.sin(theta)], axis=-1).astype(np.float32)
+
+
 def custom_workload(dtype=BF16, B=1, H_q=1, H_kv=1, n_q=64, n_k=64, d_h=128, d_v=128,
                     causal=False, offset=0, name="custom") -> Workload:
     return Workload(0, name, dtype, B, H_q, H_kv, n_q, n_k, d_h, d_v, causal, offset)
