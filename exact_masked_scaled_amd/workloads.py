@@ -171,6 +171,40 @@ def make_inputs(wl, seed: Optional[int] = None, with_grad: bool = True,
     return Inputs(wl, seed, lq, lk, Q, K, V, GO)
 
 
+@dataclasses.dataclass
+class ProjectionInputs:
+    wl: Workload
+    seed: int
+    d_model: int
+    seqlens: Optional[list]
+    X: np.ndarray       # [B, n, d_model] payload
+    W: np.ndarray       # [d_model, H_q d_h + H_kv d_h + H_kv d_v] payload, [W_Q | W_K | W_V]
+    GO: np.ndarray      # [B, H_q, n, d_v] payload
+
+
+def make_projection_inputs(wl: Workload, d_model: int, seed: int, seqlens=None) -> ProjectionInputs:
+    """Inputs of self-attention with its projections (n_q == n_k): X ~ N(0, 1),
+    W ~ N(0, 1/d_model) so the projected Q, K, V have unit-variance entries
+    (the variance model of [A.10, eq. A.10.4] again), G_O ~ N(0, 1); each
+    rounded once to the I/O dtype.  Draw order: X, W, G_O."""
+    if wl.n_q != wl.n_k:
+        raise ValueError("self-attention needs n_q == n_k")
+    rng = np.random.default_rng(seed)
+    C = wl.H_q * wl.d_h + wl.H_kv * wl.d_h + wl.H_kv * wl.d_v
+    X = _draw_rounded(rng, (wl.B, wl.n_q, d_model), wl.dtype)
+    W = _draw_rounded_scaled(rng, (d_model, C), wl.dtype, 1.0 / np.sqrt(d_model))
+    GO = _draw_rounded(rng, (wl.B, wl.H_q, wl.n_q, wl.d_v), wl.dtype)
+    return ProjectionInputs(wl, seed, d_model, seqlens, X, W, GO)
+
+
+def _draw_rounded_scaled(rng: np.random.Generator, shape, dtype: str, scale: float):
+    """N(0, scale^2) drawn in float64, rounded once to the I/O dtype."""
+    x = rng.standard_normal(shape) * scale
+    if dtype == BF16:
+        return bf16_bits(round_to_bf16(x))
+    return x.astype(np.float32)
+
+
 def rotary_table(n_pos: int, d_h: int, base: float = 10000.0) -> np.ndarray:
     """The cos/sin table a caller hands to the rotary-position calls, an input
     like Q or K: [n_pos, d_h/2, 2] float32 of (cos, sin) of the angle

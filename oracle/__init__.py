@@ -11,6 +11,9 @@ attention : numpy float64 definition of the forward and backward, materialising
             S, A, G_A, c and G_S for every (batch, query head).
 tiny      : an independent pure-Python (lists, no numpy) re-derivation of the
             same quantities for tiny shapes, used to cross-check ``attention``.
+projection: the projections around the core (Q/K/V = X W, G_W = X^T G, G_X
+            summed over the branches that share an input), self- and
+            cross-attention.
 
 Parity status: every function here is pinned by tests/test_oracle_*.py against
 values printed on the pages, closed forms, invariants, central finite
@@ -37,4 +40,11 @@ from .attention import (  # noqa: F401
     scores,
     masked_softmax,
     score_grad,
+)
+from .projection import (  # noqa: F401
+    self_attention_backward,
+    cross_attention_backward,
+    split_qkv_weight,
+    to_heads,
+    from_heads,
 )
