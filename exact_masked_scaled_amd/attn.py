@@ -37,7 +37,9 @@ BF16 = 1
 EXPORTS = ("attn_validate", "attn_bwd_workspace_size", "attn_fwd", "attn_bwd",
            "attn_bwd_dq", "attn_bwd_dkdv", "attn_fwd_splitkv_workspace_size", "attn_fwd_splitkv",
            "attn_rope_apply", "attn_fwd_rope_workspace_size", "attn_fwd_rope",
-           "attn_bwd_rope_workspace_size", "attn_bwd_rope", "attn_status_string", "attn_version")
+           "attn_bwd_rope_workspace_size", "attn_bwd_rope", "attn_linear_fwd", "attn_linear_bwd",
+           "attn_self_attention_fwd", "attn_self_attention_bwd_workspace_size", "attn_self_attention_bwd",
+           "attn_status_string", "attn_version")
 
 
 class AttnError(RuntimeError):
@@ -63,6 +65,12 @@ class Problem(ctypes.Structure):
                 ("v_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3),
                 ("cu_seqlens_q", ctypes.POINTER(ctypes.c_int32)),
                 ("cu_seqlens_k", ctypes.POINTER(ctypes.c_int32))]
+
+
+class Linear(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int32), ("d_in", ctypes.c_int32), ("d_out", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("ld_x", ctypes.c_int64), ("ld_w", ctypes.c_int64),
+                ("ld_y", ctypes.c_int64)]
 
 
 class Rope(ctypes.Structure):
@@ -114,6 +122,18 @@ def lib():
     L.attn_bwd_rope_workspace_size.restype = ctypes.c_size_t
     L.attn_bwd_rope.argtypes = [P, M, R, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.attn_bwd_rope.restype = ctypes.c_int
+    LP = ctypes.POINTER(Linear)
+    L.attn_linear_fwd.argtypes = [LP, vp, vp, vp, vp]
+    L.attn_linear_fwd.restype = ctypes.c_int
+    L.attn_linear_bwd.argtypes = [LP, vp, vp, vp, vp, vp, ctypes.c_int32, vp]
+    L.attn_linear_bwd.restype = ctypes.c_int
+    L.attn_self_attention_fwd.argtypes = [P, M, ctypes.c_int32, vp, vp, vp, vp, vp, vp]
+    L.attn_self_attention_fwd.restype = ctypes.c_int
+    L.attn_self_attention_bwd_workspace_size.argtypes = [P]
+    L.attn_self_attention_bwd_workspace_size.restype = ctypes.c_size_t
+    L.attn_self_attention_bwd.argtypes = [P, M, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                          vp]
+    L.attn_self_attention_bwd.restype = ctypes.c_int
     L.attn_status_string.argtypes = [ctypes.c_int]
     L.attn_status_string.restype = ctypes.c_char_p
     L.attn_version.argtypes = []
@@ -532,3 +552,125 @@ def bwd_rope(q, k, v, o, lse, do, cos_sin, *, causal=False, offset=0, seqlens_q=
     if st != OK:
         raise AttnError(st, "attn_bwd_rope")
     return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# projections
+# ---------------------------------------------------------------------------
+def _check2(name, t, dtype):
+    if t.dim() != 2 or t.dtype != dtype or not t.is_cuda or (t.shape[1] > 0 and t.stride(1) != 1):
+        raise ValueError(f"{name} must be a 2-D GPU tensor of {dtype} with unit column stride")
+
+
+def make_linear(rows, d_in, d_out, dtype, ld_x=None, ld_w=None, ld_y=None) -> Linear:
+    return Linear(int(rows), int(d_in), int(d_out), int(dtype), int(ld_x if ld_x is not None else d_in),
+                  int(ld_w if ld_w is not None else d_out), int(ld_y if ld_y is not None else d_out))
+
+
+def _linear_of(x, w, y_stride0=None) -> Linear:
+    return make_linear(x.shape[0], x.shape[1], w.shape[1], _dtype_code(x), x.stride(0), w.stride(0),
+                       y_stride0 if y_stride0 is not None else w.shape[1])
+
+
+def linear_fwd(x, w, *, out=None, stream=None):
+    """attn_linear_fwd: Y = X W for 2-D x [rows, d_in], w [d_in, d_out]."""
+    torch = _torch()
+    _check2("x", x, x.dtype)
+    _check2("w", w, x.dtype)
+    if out is None:
+        out = torch.empty(x.shape[0], w.shape[1], dtype=x.dtype, device=x.device)
+    _check2("out", out, x.dtype)
+    lin = _linear_of(x, w, out.stride(0))
+    st = lib().attn_linear_fwd(ctypes.byref(lin), _ptr(x), _ptr(w), _ptr(out), _stream(stream))
+    if st != OK:
+        raise AttnError(st, "attn_linear_fwd")
+    return out
+
+
+def linear_bwd(x, w, gy, *, gx=None, gw=None, accumulate=False, want_gx=True, want_gw=True, stream=None):
+    """attn_linear_bwd: G_X = G_Y W^T and G_W = X^T G_Y (accumulate: added)."""
+    torch = _torch()
+    for n_, t in (("x", x), ("w", w), ("gy", gy)):
+        _check2(n_, t, x.dtype)
+    if want_gx and gx is None:
+        gx = torch.empty_like(x)
+    if want_gw and gw is None:
+        gw = torch.empty_like(w)
+    if gx is not None and gx.stride() != x.stride():
+        raise ValueError("gx must have the strides of x")
+    if gw is not None and gw.stride() != w.stride():
+        raise ValueError("gw must have the strides of w")
+    lin = _linear_of(x, w, gy.stride(0))
+    st = lib().attn_linear_bwd(ctypes.byref(lin), _ptr(x), _ptr(w), _ptr(gy), _ptr(gx) if gx is not None else None,
+                               _ptr(gw) if gw is not None else None, 1 if accumulate else 0, _stream(stream))
+    if st != OK:
+        raise AttnError(st, "attn_linear_bwd")
+    return gx, gw
+
+
+def _self_problem(x, w, H_q, H_kv, d_h, d_v, o_stride, cu_seqlens, max_seqlen):
+    if cu_seqlens is None:
+        B, n, _ = x.shape
+        return make_problem(B, H_q, H_kv, n, n, d_h, d_v, _dtype_code(x), o_stride=o_stride)
+    cu, lens = _packed_lengths(cu_seqlens)
+    n = int(max_seqlen) if max_seqlen is not None else max(lens, default=0)
+    # the q/k/v strides are the column blocks of qkv, set by the library
+    return make_problem(len(cu) - 1, H_q, H_kv, n, n, d_h, d_v, _dtype_code(x), None, None, None, o_stride, cu, cu)
+
+
+def self_attention_fwd(x, w_qkv, *, H_q, H_kv, d_h, d_v, causal=False, offset=0, seqlens_q=None, seqlens_k=None,
+                       qkv=None, out=None, lse=None, stream=None, cu_seqlens=None, max_seqlen=None):
+    """attn_self_attention_fwd: x [B, n, d_model] (or packed [rows, d_model]
+    with cu_seqlens), w_qkv [d_model, H_q d_h + H_kv d_h + H_kv d_v].
+    Returns qkv [rows, C], O and lse (shapes as fwd())."""
+    torch = _torch()
+    packed = cu_seqlens is not None
+    if x.dim() != (2 if packed else 3) or not x.is_contiguous() or not w_qkv.is_contiguous():
+        raise ValueError("x ([B, n, d_model] or packed [rows, d_model]) and w_qkv must be contiguous")
+    rows = x.shape[0] if packed else x.shape[0] * x.shape[1]
+    C = H_q * d_h + H_kv * d_h + H_kv * d_v
+    if qkv is None:
+        qkv = torch.empty(rows, C, dtype=x.dtype, device=x.device)
+    if packed:
+        o_shape, lse_shape = (rows, H_q, d_v), (H_q, rows)
+    else:
+        o_shape, lse_shape = (x.shape[0], H_q, x.shape[1], d_v), (x.shape[0], H_q, x.shape[1])
+    if out is None:
+        out = torch.empty(*o_shape, dtype=x.dtype, device=x.device)
+    if lse is None:
+        lse = torch.empty(*lse_shape, dtype=torch.float32, device=x.device)
+    prob = _self_problem(x, w_qkv, H_q, H_kv, d_h, d_v, _strides(out), cu_seqlens, max_seqlen)
+    mask, keep = make_mask(causal, offset, seqlens_q, seqlens_k)
+    st = lib().attn_self_attention_fwd(ctypes.byref(prob), ctypes.byref(mask), int(x.shape[-1]), _ptr(x),
+                                       _ptr(w_qkv), _ptr(qkv), _ptr(out), _ptr(lse), _stream(stream))
+    del keep
+    if st != OK:
+        raise AttnError(st, "attn_self_attention_fwd")
+    return qkv, out, lse
+
+
+def self_attention_bwd(x, w_qkv, qkv, o, lse, do, *, H_q, H_kv, d_h, d_v, causal=False, offset=0, seqlens_q=None,
+                       seqlens_k=None, gx=None, gw=None, workspace=None, stream=None, cu_seqlens=None,
+                       max_seqlen=None):
+    """attn_self_attention_bwd: G_X (shape of x) and G_W (shape of w_qkv)."""
+    torch = _torch()
+    if do.stride() != o.stride():
+        raise ValueError("do must have the strides of o")
+    gx = torch.empty_like(x) if gx is None else gx
+    gw = torch.empty_like(w_qkv) if gw is None else gw
+    prob = _self_problem(x, w_qkv, H_q, H_kv, d_h, d_v, _strides(o), cu_seqlens, max_seqlen)
+    need = int(lib().attn_self_attention_bwd_workspace_size(ctypes.byref(prob)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    mask, keep = make_mask(causal, offset, seqlens_q, seqlens_k)
+    st = lib().attn_self_attention_bwd(ctypes.byref(prob), ctypes.byref(mask), int(x.shape[-1]), _ptr(x),
+                                       _ptr(w_qkv), _ptr(qkv), _ptr(o), _ptr(lse), _ptr(do), _ptr(gx), _ptr(gw),
+                                       _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(stream))
+    del keep
+    if st != OK:
+        raise AttnError(st, "attn_self_attention_bwd")
+    return gx, gw
+
+
+def self_attention_workspace_size(prob: Problem) -> int:
+    return int(lib().attn_self_attention_bwd_workspace_size(ctypes.byref(prob)))

@@ -34,6 +34,8 @@ HIP_FLAGS = [
     "-I", INCLUDE, "-I", CSRC,
 ]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
+ROCM_LIB = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "lib")
+LINK_LIBS = ["-L", ROCM_LIB, "-lrocblas", f"-Wl,-rpath,{ROCM_LIB}"]
 
 
 def _run(cmd, verbose):
@@ -76,7 +78,8 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = LIB_PATH + ".tmp"
-    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs], verbose)
+    # the projections' products link the vendor GEMM
+    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs, *LINK_LIBS], verbose)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

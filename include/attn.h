@@ -234,6 +234,64 @@ attn_status attn_bwd_rope(const attn_problem* prob, const attn_mask* mask, const
                           void* dQ, void* dK, void* dV,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------- projections
+ * The products on either side of the core ("Appendix A.10", eqs. A.10.10 and
+ * A.10.11), with row-major weights W [d_in][d_out]:
+ *   forward   Y = X W                       (Q = X W_Q, K = X W_K, V = X W_V)
+ *   backward  G_W = X^T G_Y,  G_X = G_Y W^T
+ * A shared input feeds several projections; its gradient is the SUM of their
+ * branches, G_X = G_Q W_Q^T + G_K W_K^T + G_V W_V^T (and for cross-attention
+ * only the branches that really share an input are summed, the same
+ * section).  Storing the weights side by side, W = [W_Q | W_K | W_V], makes
+ * both one product: Y = X W holds [Q | K | V] in each row, and G_Y W^T over
+ * the concatenated columns is the branch sum.  Separate weights sum through
+ * `accumulate`.
+ *
+ * Products run on the vendor GEMM (rocBLAS: bf16 or float32 operands,
+ * float32 accumulation, one rounding of each result to the payload type);
+ * the library keeps one rocBLAS handle per host thread and device, created on
+ * first use.  Errors as elsewhere: checked before anything is enqueued. */
+typedef struct {
+  int32_t rows;              /* rows of X, Y, G_X and G_Y                      */
+  int32_t d_in, d_out;       /* columns of X (rows of W) and of Y (of W)       */
+  int32_t dtype;             /* attn_dtype of every operand                    */
+  int64_t ld_x, ld_w, ld_y;  /* row strides in elements (G_X, G_W, G_Y share
+                                those of X, W, Y); >= the row widths         */
+} attn_linear;
+
+/* Y = X W.  Device pointers, 16-byte aligned. */
+attn_status attn_linear_fwd(const attn_linear* lin, const void* X, const void* W, void* Y, void* stream);
+
+/* G_X = G_Y W^T and G_W = X^T G_Y (either output may be NULL: not formed).
+ * accumulate == 1 adds into G_X / G_W instead of overwriting them (summing
+ * the branches of a shared input held in separate weights). */
+attn_status attn_linear_bwd(const attn_linear* lin, const void* X, const void* W, const void* G_Y,
+                            void* G_X, void* G_W, int32_t accumulate, void* stream);
+
+/* Self-attention with its projections: [Q | K | V] = X W_qkv with X
+ * [rows][d_model] and W_qkv [d_model][C], C = H_q d_h + H_kv d_h + H_kv d_v,
+ * both contiguous; rows = B n_q (padded) or cu_seqlens_q[B] (packed).  QKV
+ * [rows][C] (contiguous) receives the projections; the attention then reads
+ * Q, K, V as its column blocks (head h of Q at columns h d_h .., of K at
+ * H_q d_h + h d_h .., of V at H_q d_h + H_kv d_h + h d_v ..), so prob's
+ * q/k/v strides are ignored; O and lse as attn_fwd (o_stride from prob).
+ * Requires n_k == n_q and, packed, cu_seqlens_k equal to cu_seqlens_q. */
+attn_status attn_self_attention_fwd(const attn_problem* prob, const attn_mask* mask, int32_t d_model,
+                                    const void* X, const void* W_qkv, void* QKV, void* O, float* lse,
+                                    void* stream);
+
+/* Its backward: from X, W_qkv, the forward's QKV, O and lse, and G_O, writes
+ * G_X [rows][d_model] = G_Q W_Q^T + G_K W_K^T + G_V W_V^T and G_W [d_model][C]
+ * = X^T [G_Q | G_K | G_V] (either may be NULL).  The workspace
+ * (attn_self_attention_bwd_workspace_size bytes, 256-byte aligned) holds D
+ * and [G_Q | G_K | G_V] [rows][C]. */
+size_t attn_self_attention_bwd_workspace_size(const attn_problem* prob);
+attn_status attn_self_attention_bwd(const attn_problem* prob, const attn_mask* mask, int32_t d_model,
+                                    const void* X, const void* W_qkv, const void* QKV,
+                                    const void* O, const float* lse, const void* dO,
+                                    void* G_X, void* G_W,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* attn_status_string(attn_status status);
 

@@ -235,3 +235,52 @@ def test_rope_argument_errors():
     st = L.attn_bwd_rope(ctypes.byref(p), ctypes.byref(m), ctypes.byref(A.make_rope(0x10000, 200)), fake, fake,
                          fake, fake, fake, fake, fake, fake, fake, fake, ctypes.c_size_t(A.workspace_size(p)), null)
     assert st == A.WORKSPACE
+
+
+def test_linear_struct_and_errors():
+    L = lib_or_skip()
+    assert ctypes.sizeof(A.Linear) == 40 and A.Linear.ld_x.offset == 16
+    null = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(0x10000)
+
+    def fwd(lin, x=fake, w=fake, y=fake):
+        return L.attn_linear_fwd(ctypes.byref(lin), x, w, y, null)
+
+    assert fwd(A.make_linear(10, 64, 96, A.BF16, ld_x=32)) == A.INVALID_ARG          # row stride < width
+    assert fwd(A.make_linear(10, 64, 96, 7)) == A.UNSUPPORTED
+    assert fwd(A.make_linear(-1, 64, 96, A.BF16)) == A.INVALID_ARG
+    assert fwd(A.make_linear(10, 64, 96, A.BF16), x=null) == A.INVALID_ARG
+    assert fwd(A.make_linear(10, 64, 96, A.BF16), y=ctypes.c_void_p(0x10002)) == A.INVALID_ARG
+    assert fwd(A.make_linear(0, 64, 96, A.BF16), x=null, w=null, y=null) == A.OK     # nothing to do
+    lin = A.make_linear(10, 64, 96, A.BF16)
+    assert L.attn_linear_bwd(ctypes.byref(lin), fake, fake, fake, fake, fake, 2, null) == A.INVALID_ARG
+    assert L.attn_linear_bwd(ctypes.byref(lin), fake, fake, null, fake, null, 0, null) == A.INVALID_ARG
+    # nothing requested: nothing to check or do
+    assert L.attn_linear_bwd(ctypes.byref(lin), null, null, null, null, null, 0, null) == A.OK
+
+
+def test_self_attention_workspace_and_errors():
+    L = lib_or_skip()
+    p = A.make_problem(2, 4, 2, 100, 100, 128, 64, A.BF16)
+    C = 4 * 128 + 2 * 128 + 2 * 64
+    assert A.self_attention_workspace_size(p) == A.workspace_size(p) + (2 * 100 * C * 2 + 255) // 256 * 256
+    null = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(0x10000)
+    m, keep = A.make_mask(causal=True)
+    # self-attention needs n_k == n_q
+    p2 = A.make_problem(2, 4, 2, 100, 120, 128, 64, A.BF16)
+    assert L.attn_self_attention_fwd(ctypes.byref(p2), ctypes.byref(m), 256, fake, fake, fake, fake, fake,
+                                     null) == A.INVALID_ARG
+    assert L.attn_self_attention_fwd(ctypes.byref(p), ctypes.byref(m), 0, fake, fake, fake, fake, fake,
+                                     null) == A.INVALID_ARG
+    # packed: the same rows for queries and keys
+    pk = A.make_problem(2, 4, 2, 20, 20, 128, 64, A.BF16, cu_seqlens_q=[0, 10, 30], cu_seqlens_k=[0, 20, 30])
+    assert L.attn_self_attention_fwd(ctypes.byref(pk), ctypes.byref(m), 256, fake, fake, fake, fake, fake,
+                                     null) == A.INVALID_ARG
+    # attention checks still apply
+    m2, keep2 = A.make_mask(causal=True, offset=-1)
+    assert L.attn_self_attention_fwd(ctypes.byref(p), ctypes.byref(m2), 256, fake, fake, fake, fake, fake,
+                                     null) == A.EMPTY_ROW
+    st = L.attn_self_attention_bwd(ctypes.byref(p), ctypes.byref(m), 256, fake, fake, fake, fake, fake, fake, fake,
+                                   fake, fake, ctypes.c_size_t(16), null)
+    assert st == A.WORKSPACE
