@@ -284,6 +284,75 @@ def measure_rope(torch, attn, W, wl, steps, warmup):
             "steps": steps, "warmup": warmup}
 
 
+def measure_projected(torch, attn, W, wl, d_model, steps, warmup):
+    """Self-attention with its projections on the same sequences, packed (no
+    padding rows enter the products): forward = [Q|K|V] = X W_qkv then the
+    core; backward = the core's backward into [G_Q|G_K|G_V], then G_W and G_X
+    (the three branches summed by one product).  Interleaved per-call medians,
+    inputs resident; the products alone are timed too."""
+    import numpy as np
+
+    rng = np.random.default_rng(W.default_seed(wl.wid))
+    lq, lk = W.draw_lengths(wl, rng)
+    lens = lq or [wl.n_q] * wl.B
+    inp = W.make_projection_inputs(wl, d_model, seed=W.default_seed(wl.wid) + 500, seqlens=lens)
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+    cu = [0] + np.cumsum(lens).astype(int).tolist()
+    rows = cu[-1]
+    x = dev(np.ascontiguousarray(np.concatenate([inp.X[b, :L] for b, L in enumerate(lens)], axis=0)))
+    do = dev(np.ascontiguousarray(np.concatenate([inp.GO[b, :, :L].transpose(1, 0, 2)
+                                                  for b, L in enumerate(lens)], axis=0)))
+    w = dev(inp.W)
+    del inp
+    C = w.shape[1]
+    kw = dict(H_q=wl.H_q, H_kv=wl.H_kv, d_h=wl.d_h, d_v=wl.d_v, causal=wl.causal, offset=wl.offset, cu_seqlens=cu,
+              max_seqlen=wl.n_q)
+    qkv = torch.empty(rows, C, dtype=x.dtype, device=x.device)
+    o = torch.empty(rows, wl.H_q, wl.d_v, dtype=x.dtype, device=x.device)
+    lse = torch.empty(wl.H_q, rows, dtype=torch.float32, device=x.device)
+    gx, gw = torch.empty_like(x), torch.empty_like(w)
+    prob = attn._self_problem(x, w, wl.H_q, wl.H_kv, wl.d_h, wl.d_v, attn._strides(o), cu, wl.n_q)
+    ws = torch.empty(attn.self_attention_workspace_size(prob), dtype=torch.uint8, device=x.device)
+    gqkv = torch.empty_like(qkv)
+    stream = torch.cuda.current_stream()
+    calls = {
+        "fwd": lambda: attn.self_attention_fwd(x, w, qkv=qkv, out=o, lse=lse, stream=stream, **kw),
+        "bwd": lambda: attn.self_attention_bwd(x, w, qkv, o, lse, do, gx=gx, gw=gw, workspace=ws, stream=stream,
+                                               **kw),
+        "gemm_qkv": lambda: attn.linear_fwd(x, w, out=qkv, stream=stream),
+        "gemm_grads": lambda: attn.linear_bwd(x, w, gqkv, gx=gx, gw=gw, stream=stream),
+    }
+    for _ in range(warmup):
+        for fn in calls.values():
+            fn()
+    evs = {n: [] for n in calls}
+    for _ in range(steps):
+        for name, fn in calls.items():
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            evs[name].append((e0, e1))
+    torch.cuda.synchronize()
+    t = {n: float(np.median([a.elapsed_time(b) for a, b in ev])) for n, ev in evs.items()}
+    work = W.work(wl, lq, lk)
+    gemm_fwd = 2.0 * rows * d_model * C
+    total = 3 * gemm_fwd + work["fwd_flop"] + work["bwd_flop"]
+    del x, do, w, qkv, o, lse, gx, gw, ws, gqkv
+    return {"workload": wl.name + f"_packed_dmodel{d_model}", "rows": rows, "d_model": d_model, "qkv_width": C,
+            "fwd_ms": round(t["fwd"], 4), "bwd_ms": round(t["bwd"], 4),
+            "step_TFLOP/s": round(total / ((t["fwd"] + t["bwd"]) * 1e-3) / 1e12, 2),
+            "gemm_qkv_ms": round(t["gemm_qkv"], 4),
+            "gemm_qkv_TFLOP/s": round(gemm_fwd / (t["gemm_qkv"] * 1e-3) / 1e12, 2),
+            "gemm_grads_ms": round(t["gemm_grads"], 4),
+            "gemm_grads_TFLOP/s": round(2 * gemm_fwd / (t["gemm_grads"] * 1e-3) / 1e12, 2),
+            "steps": steps, "warmup": warmup}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -411,6 +480,8 @@ def main(argv=None):
         result["forward_splitkv"] = fsplit
         # rotary positions on the headline workload
         result["rotary"] = measure_rope(torch, attn, W, wl, 10, 3)
+        # with the Q/K/V projections (model width = the query heads' width)
+        result["projected"] = measure_projected(torch, attn, W, wl, wl.H_q * wl.d_h, 10, 3)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)
