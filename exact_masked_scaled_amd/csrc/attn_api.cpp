@@ -97,6 +97,18 @@ T* off(T* base, int64_t elems, size_t es) {
   return base ? (T*)((char*)base + elems * (int64_t)es) : nullptr;
 }
 
+// Forward work items per (sequence, KV head) unit.  With packed heads a
+// workgroup's rows are the unit's (position, head) pairs, group * n_q rows in
+// blocks; otherwise each query head has its own blocks of n_q rows.
+bool fwd_pack(const attn_problem& p) {
+  const int64_t group = p.H_q / p.H_kv;
+  return group > 1 && group * p.n_q <= INT32_MAX;
+}
+int64_t fwd_items(const attn_problem& p, bool pack) {
+  const int64_t bm = fwd_block_rows(p.dtype), group = p.H_q / p.H_kv;
+  return pack ? (group * p.n_q + bm - 1) / bm : group * ((p.n_q + bm - 1) / bm);
+}
+
 int chunk_size(const KernelParams& kp, int B) {
   return (kp.has_lens || kp.has_offs || kp.rope) ? kMaxBatchChunk : std::max(B, 1);
 }
@@ -127,12 +139,12 @@ attn_status attn_fwd(const attn_problem* prob, const attn_mask* mask, const void
   const size_t es = esize(p.dtype);
   KernelParams kp;
   fill_common(kp, p, m);
-  const int nqblk = (p.n_q + fwd_block_rows(p.dtype) - 1) / fwd_block_rows(p.dtype);
+  kp.pack = fwd_pack(p) ? 1 : 0;
   const int cs = chunk_size(kp, p.B);
   for (int b0 = 0; b0 < p.B; b0 += cs) {
     const int nb = std::min(cs, p.B - b0);
     fill_chunk(kp, p, m, b0, nb);
-    kp.per_group = kp.group * nqblk;
+    kp.per_group = (int32_t)fwd_items(p, kp.pack != 0);
     kp.q = off(Q, b0 * p.q_stride[0], es);
     kp.k = off(K, b0 * p.k_stride[0], es);
     kp.v = off(V, b0 * p.v_stride[0], es);
@@ -156,8 +168,8 @@ int64_t lse_rows(const attn_problem& p) {
 // Parts per row block: enough workgroups to give every CU two (the forward
 // runs two per CU), at most one part per key tile and at most 64.
 int32_t auto_splits(const attn_problem& p) {
-  const int64_t nqblk = (p.n_q + fwd_block_rows(p.dtype) - 1) / fwd_block_rows(p.dtype);
-  const int64_t base = std::max<int64_t>(1, (int64_t)std::min(p.B, kMaxBatchChunk) * p.H_q * nqblk);
+  const int64_t base =
+      std::max<int64_t>(1, (int64_t)std::min(p.B, kMaxBatchChunk) * p.H_kv * fwd_items(p, fwd_pack(p)));
   const int64_t want = (512 + base - 1) / base;
   const int64_t tiles = std::max<int64_t>(1, (p.n_k + 63) / 64);
   return (int32_t)std::max<int64_t>(1, std::min<int64_t>({want, tiles, 64}));
@@ -203,12 +215,12 @@ attn_status attn_fwd_splitkv(const attn_problem* prob, const attn_mask* mask, co
   fill_common(kp, p, m);
   kp.splits = splits;
   kp.part_rows = rows;
-  const int nqblk = (p.n_q + fwd_block_rows(p.dtype) - 1) / fwd_block_rows(p.dtype);
+  kp.pack = fwd_pack(p) ? 1 : 0;
   const int cs = chunk_size(kp, p.B);
   for (int b0 = 0; b0 < p.B; b0 += cs) {
     const int nb = std::min(cs, p.B - b0);
     fill_chunk(kp, p, m, b0, nb);
-    kp.per_group = kp.group * nqblk * splits;
+    kp.per_group = (int32_t)(fwd_items(p, kp.pack != 0) * splits);
     kp.q = off(Q, b0 * p.q_stride[0], es);
     kp.k = off(K, b0 * p.k_stride[0], es);
     kp.v = off(V, b0 * p.v_stride[0], es);
@@ -476,12 +488,12 @@ attn_status attn_fwd_rope(const attn_problem* prob, const attn_mask* mask, const
   kp.rope = kRopeQ;
   kp.rope_cs = rope->cos_sin;
   kp.k_sb = kt.s[0]; kp.k_sh = kt.s[1]; kp.k_sr = kt.s[2];
-  const int nqblk = (p.n_q + fwd_block_rows(p.dtype) - 1) / fwd_block_rows(p.dtype);
+  kp.pack = fwd_pack(p) ? 1 : 0;
   const int cs = chunk_size(kp, p.B);
   for (int b0 = 0; b0 < p.B; b0 += cs) {
     const int nb = std::min(cs, p.B - b0);
     fill_chunk(kp, p, m, b0, nb);
-    kp.per_group = kp.group * nqblk;
+    kp.per_group = (int32_t)fwd_items(p, kp.pack != 0);
     kp.q = off(Q, b0 * p.q_stride[0], es);
     kp.k = off((const void*)workspace, b0 * kt.s[0], es);
     kp.v = off(V, b0 * p.v_stride[0], es);

@@ -50,7 +50,6 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(const 
   __shared__ __attribute__((aligned(16))) T v_lds0[C::BN * C::VS];
   __shared__ __attribute__((aligned(16))) T v_lds1[C::BN * C::VS];
 
-  const int nqblk = (p.n_q + C::BM - 1) / C::BM;
   int unit, item;
   if (!map_work(blockIdx.x, p.groups, p.per_group, p.xcd_map, unit, item)) return;
   const int b = unit / p.H_kv, g = unit - (unit / p.H_kv) * p.H_kv;
@@ -59,14 +58,30 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(const 
     sidx = item % p.splits;
     item /= p.splits;
   }
-  // heavy (late) row blocks first; all query heads of the unit interleaved
-  const int qb = nqblk - 1 - item / p.group;
-  const int r = g * p.group + item % p.group;
+  // The rows of a workgroup: 128 query rows of one head (the unit's heads
+  // interleaved), or with p.pack 128 consecutive rows rho of the unit's
+  // (position, head) pairs, rho -> position rho / group, head g group +
+  // rho % group: the heads that share the K/V tiles share the workgroup, so
+  // a few positions per head (decoding) still fill it.  Heavy (late) blocks
+  // first.
+  const bool pack = p.pack != 0;
+  int qb, r;
+  if (pack) {
+    qb = (p.group * p.n_q + C::BM - 1) / C::BM - 1 - item;
+    r = 0;  // per lane below
+  } else {
+    qb = (p.n_q + C::BM - 1) / C::BM - 1 - item / p.group;
+    r = g * p.group + item % p.group;
+  }
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const SeqView sv = seq_view(p, b);
   const int Lq = sv.Lq, Lk = sv.Lk, off = sv.off;
-  const int q_lo = qb * C::BM;
+  const int q_lo = qb * C::BM;                          // first row of the block
+  const int rho = q_lo + 32 * w + (lane & 31);          // this lane's row
+  if (pack) r = g * p.group + rho % p.group;
+  auto pos_of = [&](int row) { return pack ? row / p.group : row; };
+  const int rows_active = pack ? p.group * Lq : Lq;     // rows before it are active
 
   const T* Qb = (const T*)p.q + b * p.q_sb + sv.q_row0 * p.q_sr + r * p.q_sh;
   const T* Kb = (const T*)p.k + b * p.k_sb + sv.k_row0 * p.k_sr + g * p.k_sh;
@@ -74,25 +89,25 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(const 
   T* Ob = (T*)p.o_out + b * p.o_sb + sv.q_row0 * p.o_sr + r * p.o_sh;
   float* lse_b = p.lse + b * p.lse_sb + r * p.lse_sh + sv.q_row0;
 
-  const int qi = q_lo + 32 * w + (lane & 31);          // this lane's query row
-  const int kg = lane >> 5;                            // k-group of the lane
+  const int qi = pos_of(rho);                           // this lane's query position
+  const int kg = lane >> 5;                             // k-group of the lane
   const bool row_exists = qi < sv.nq_lim;
   const bool row_active = qi < Lq;
 
-  // rows of the block that are active
-  const int act_hi = min(q_lo + C::BM, Lq);            // exclusive
+  // rows of the block that are active, and their positions
+  const int act_hi = min(q_lo + C::BM, rows_active);    // exclusive
   int ntiles = 0, nfull = 0;
   if (act_hi > q_lo) {
-    const int kend = key_limit(act_hi - 1, Lk, p.causal, off);
-    const int kfull = key_limit(q_lo, Lk, p.causal, off);
+    const int kend = key_limit(pos_of(act_hi - 1), Lk, p.causal, off);
+    const int kfull = key_limit(pos_of(q_lo), Lk, p.causal, off);
     ntiles = (kend + C::BN - 1) / C::BN;
     nfull = kfull / C::BN;
   }
   // this wave's rows
   const int w_lo = q_lo + 32 * w;
-  const int w_hi = min(w_lo + 32, Lq);
+  const int w_hi = min(w_lo + 32, rows_active);
   int wtiles = 0;
-  if (w_hi > w_lo) wtiles = (key_limit(w_hi - 1, Lk, p.causal, off) + C::BN - 1) / C::BN;
+  if (w_hi > w_lo) wtiles = (key_limit(pos_of(w_hi - 1), Lk, p.causal, off) + C::BN - 1) / C::BN;
   const int kmax_lane = key_limit(qi, Lk, p.causal, off);
   // key tiles [t_lo, t_hi) of this workgroup: all of them, or part sidx of
   // `splits` nearly equal parts

@@ -45,6 +45,7 @@ struct KernelParams {
   int32_t groups;       // (b, kv-head) units of work
   int32_t per_group;    // work items per unit
   int32_t xcd_map;      // 1: unit u runs on XCD u % 8 (groups % 8 == 0)
+  int32_t pack;         // forward: a workgroup's rows are (position, head) pairs of the unit's heads
   int64_t lse_sb, lse_sh;  // element strides of lse and D: sequence, head (rows: 1)
   // forward split over the keys: `splits` parts per row block, each writing
   // its normalised float32 partial output and partial lse at split s of
