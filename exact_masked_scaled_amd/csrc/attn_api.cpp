@@ -44,10 +44,15 @@ void fill_common(KernelParams& kp, const attn_problem& p, const attn_mask& m) {
   if (kp.varlen) {  // lse / D: [H_q][total rows]; the row offsets carry the sequence
     kp.lse_sb = 0;
     kp.lse_sh = p.cu_seqlens_q[p.B];
+    kp.krow_sb = 0;
+    kp.krow_sh = p.cu_seqlens_k[p.B];
   } else {
     kp.lse_sb = (int64_t)p.H_q * p.n_q;
     kp.lse_sh = p.n_q;
+    kp.krow_sb = (int64_t)p.H_kv * p.n_k;
+    kp.krow_sh = p.n_k;
   }
+  kp.hsplits = 1;
 }
 
 int32_t clamp_offset(int64_t off, int32_t n_k) {
@@ -113,6 +118,39 @@ int chunk_size(const KernelParams& kp, int B) {
   return (kp.has_lens || kp.has_offs || kp.rope) ? kMaxBatchChunk : std::max(B, 1);
 }
 
+// How the backward passes are divided when their grids alone would leave
+// most of the GPU idle (few sequences and heads, short query blocks): the
+// dQ pass over parts of the keys (float32 partial G_Q summed by a combine
+// kernel), the bf16 dK/dV pass over parts of each group's query heads
+// (partial G_K / G_V likewise).  Fixed by the sizes alone, so the workspace
+// size and the call agree; not used with rotary positions.
+struct BwdPlan {
+  int32_t dq_splits = 1, hsplits = 1;
+  int64_t q_rows = 0, k_rows = 0;      // rows of lse / D, and of the key partials
+  size_t d_bytes = 0, dq_bytes = 0, kv_bytes = 0;
+};
+BwdPlan bwd_plan(const attn_problem& p, bool rope) {
+  BwdPlan pl;
+  const bool packed = p.cu_seqlens_q != nullptr;
+  pl.q_rows = packed ? (int64_t)p.H_q * std::max(p.cu_seqlens_q[p.B], 0) : (int64_t)p.B * p.H_q * p.n_q;
+  pl.k_rows = packed ? (int64_t)p.H_kv * std::max(p.cu_seqlens_k[p.B], 0) : (int64_t)p.B * p.H_kv * p.n_k;
+  pl.d_bytes = align_up((size_t)p.B * (size_t)p.H_q * (size_t)p.n_q * sizeof(float), kWsAlign);
+  if (p.B <= 0 || p.H_kv <= 0 || rope) return pl;
+  const int64_t nb = std::min(p.B, kMaxBatchChunk);
+  const int64_t group = p.H_q / p.H_kv;
+  const int64_t dq_wgs = nb * p.H_q * ((p.n_q + bwd_dq_block_rows(p.dtype) - 1) / bwd_dq_block_rows(p.dtype));
+  const int64_t key_tiles = (p.n_k + 63) / 64;
+  if (dq_wgs > 0 && dq_wgs < 384 && key_tiles >= 8)  // two workgroups per CU want 512
+    pl.dq_splits = (int32_t)std::min<int64_t>({(512 + dq_wgs - 1) / dq_wgs, key_tiles / 4, 16});
+  const int64_t kv_wgs = nb * p.H_kv * ((p.n_k + bwd_dkdv_block_keys(p.dtype) - 1) / bwd_dkdv_block_keys(p.dtype));
+  if (p.dtype == ATTN_BF16 && kv_wgs > 0 && kv_wgs < 192 && group > 1)  // one per CU wants 256
+    pl.hsplits = (int32_t)std::min<int64_t>({(256 + kv_wgs - 1) / kv_wgs, group, 8});
+  if (pl.dq_splits > 1) pl.dq_bytes = align_up((size_t)pl.dq_splits * pl.q_rows * p.d_h * sizeof(float), kWsAlign);
+  if (pl.hsplits > 1)
+    pl.kv_bytes = align_up((size_t)pl.hsplits * pl.k_rows * (p.d_h + p.d_v) * sizeof(float), kWsAlign);
+  return pl;
+}
+
 }  // namespace
 
 extern "C" {
@@ -122,9 +160,12 @@ attn_status attn_validate(const attn_problem* prob, const attn_mask* mask) {
 }
 
 size_t attn_bwd_workspace_size(const attn_problem* prob) {
-  if (prob == nullptr || prob->B < 0 || prob->H_q < 0 || prob->n_q < 0 || prob->d_h < 0) return 0;
-  const size_t rows = (size_t)prob->B * (size_t)prob->H_q * (size_t)prob->n_q;
-  return align_up(rows * sizeof(float), kWsAlign);
+  if (prob == nullptr || prob->B < 0 || prob->H_q < 0 || prob->H_kv < 0 || prob->n_q < 0 || prob->n_k < 0 ||
+      prob->d_h < 0 || prob->d_v < 0)
+    return 0;
+  if ((prob->cu_seqlens_q == nullptr) != (prob->cu_seqlens_k == nullptr)) return 0;
+  const BwdPlan pl = bwd_plan(*prob, false);
+  return pl.d_bytes + pl.dq_bytes + pl.kv_bytes;
 }
 
 attn_status attn_fwd(const attn_problem* prob, const attn_mask* mask, const void* Q, const void* K,
@@ -301,6 +342,14 @@ attn_status bwd_enqueue(const attn_problem& p, const attn_mask& m, const BwdPtrs
   }
   const int nqblk = (p.n_q + bwd_dq_block_rows(p.dtype) - 1) / bwd_dq_block_rows(p.dtype);
   const int nkblk = (p.n_k + bwd_dkdv_block_keys(p.dtype) - 1) / bwd_dkdv_block_keys(p.dtype);
+  // workspace: D, then the partials of divided passes
+  const BwdPlan pl = bwd_plan(p, rc != nullptr);
+  float* part_q = delta ? (float*)((char*)delta + pl.d_bytes) : nullptr;
+  float* part_kv = delta ? (float*)((char*)delta + pl.d_bytes + pl.dq_bytes) : nullptr;
+  kp.splits = pl.dq_splits;
+  kp.part_rows = pl.q_rows;
+  kp.hsplits = pl.hsplits;
+  kp.part_krows = pl.k_rows;
   const int cs = chunk_size(kp, p.B);
   for (int b0 = 0; b0 < p.B; b0 += cs) {
     const int nb = std::min(cs, p.B - b0);
@@ -316,13 +365,19 @@ attn_status bwd_enqueue(const attn_problem& p, const attn_mask& m, const BwdPtrs
     kp.dq = off(t.dQ, b0 * p.q_stride[0], es);
     kp.dk = off(t.dK, b0 * p.k_stride[0], es);
     kp.dv = off(t.dV, b0 * p.v_stride[0], es);
+    if (pl.dq_splits > 1) kp.part_o = part_q + b0 * kp.lse_sb * p.d_h;
+    if (pl.hsplits > 1) {
+      kp.part_dk = part_kv + b0 * kp.krow_sb * p.d_h;
+      kp.part_dv = part_kv + (int64_t)pl.hsplits * pl.k_rows * p.d_h + b0 * kp.krow_sb * p.d_v;
+    }
     if ((passes & kDq) && has_q) {
-      kp.per_group = kp.group * nqblk;
+      kp.per_group = kp.group * nqblk * pl.dq_splits;
       if (launch_bwd_dq(kp, p.dtype, p.d_h, p.d_v, stream) != 0) return ATTN_ERR_HIP;
     }
     if ((passes & kDkdv) && has_k) {
-      kp.per_group = nkblk;
+      kp.per_group = nkblk * pl.hsplits;
       if (launch_bwd_dkdv(kp, p.dtype, p.d_h, p.d_v, stream) != 0) return ATTN_ERR_HIP;
+      if (pl.hsplits > 1 && launch_dkdv_combine(kp, p.dtype, p.d_h, p.d_v, stream) != 0) return ATTN_ERR_HIP;
     }
   }
   return ATTN_OK;

@@ -49,7 +49,9 @@ struct DqCfg {
   static constexpr int VS = Tile<T, DV>::STRIDE;
 };
 
-template <typename T, int DH, int DV>
+// SPLIT: the workgroup covers part s of its row block's key tiles and writes
+// its float32 partial G_Q (dq_combine_kernel sums the parts in order).
+template <typename T, int DH, int DV, bool SPLIT>
 __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(const KernelParams p) {
   using C = DqCfg<T, DH, DV>;
   using op_t = typename Op<T>::type;
@@ -64,6 +66,11 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(con
   int unit, item;
   if (!map_work(blockIdx.x, p.groups, p.per_group, p.xcd_map, unit, item)) return;
   const int b = unit / p.H_kv, g = unit - (unit / p.H_kv) * p.H_kv;
+  int sidx = 0;  // key part of this workgroup (SPLIT)
+  if constexpr (SPLIT) {
+    sidx = item % p.splits;
+    item /= p.splits;
+  }
   const int qb = nqblk - 1 - item / p.group;
   const int r = g * p.group + item % p.group;
 
@@ -98,7 +105,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(con
     }
   }
   const float Di = row_active ? dpart + partner32(dpart) : 0.f;
-  if (row_exists && kg == 0) p.delta[rowbase + qi] = Di;
+  if (row_exists && kg == 0 && sidx == 0) p.delta[rowbase + qi] = Di;
   const float lse2 = row_active ? p.lse[rowbase + qi] * 1.4426950408889634f : 0.f;
 
   const int act_hi = min(q_lo + C::BM, Lq);
@@ -110,6 +117,12 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(con
   const int w_lo = q_lo + 32 * w, w_hi = min(w_lo + 32, Lq);
   const int wtiles = w_hi > w_lo ? (key_limit_b(w_hi - 1, Lk, p.causal, off) + C::BN - 1) / C::BN : 0;
   const int kmax_lane = key_limit_b(qi, Lk, p.causal, off);
+  // key tiles [t_lo, t_hi) of this workgroup: all, or part sidx of `splits`
+  int t_lo = 0, t_hi = ntiles;
+  if constexpr (SPLIT) {
+    t_lo = (int)((int64_t)sidx * ntiles / p.splits);
+    t_hi = (int)((int64_t)(sidx + 1) * ntiles / p.splits);
+  }
 
   f32x16 acc[DH / 32];
 #pragma unroll
@@ -117,7 +130,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(con
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
 
-  if (ntiles > 0) {
+  if (t_hi > t_lo) {
     op_t qreg[DH / 16];
 #pragma unroll
     for (int ks = 0; ks < DH / 16; ++ks)
@@ -177,21 +190,21 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(con
 
     using KL = TileLoad<T, C::BN, DH, 64 * C::NW>;
     using VL = TileLoad<T, C::BN, DV, 64 * C::NW>;
-    KL::issue(Kb, p.k_sr, 0, Lk, k_lds0, tid);
-    VL::issue(Vb, p.v_sr, 0, Lk, v_lds0, tid);
+    KL::issue(Kb, p.k_sr, t_lo * C::BN, Lk, k_lds0, tid);
+    VL::issue(Vb, p.v_sr, t_lo * C::BN, Lk, v_lds0, tid);
     wait_tile_loads();
     __syncthreads();
     // two tiles per trip so each LDS buffer address is a compile-time constant
-    for (int t = 0; t < ntiles; t += 2) {
-      if (t + 1 < ntiles) {
+    for (int t = t_lo; t < t_hi; t += 2) {
+      if (t + 1 < t_hi) {
         KL::issue(Kb, p.k_sr, (t + 1) * C::BN, Lk, k_lds1, tid);
         VL::issue(Vb, p.v_sr, (t + 1) * C::BN, Lk, v_lds1, tid);
       }
       if (t < wtiles) tile(t, k_lds0, v_lds0);
       wait_tile_loads();
       __syncthreads();
-      if (t + 1 >= ntiles) break;
-      if (t + 2 < ntiles) {
+      if (t + 1 >= t_hi) break;
+      if (t + 2 < t_hi) {
         KL::issue(Kb, p.k_sr, (t + 2) * C::BN, Lk, k_lds0, tid);
         VL::issue(Vb, p.v_sr, (t + 2) * C::BN, Lk, v_lds0, tid);
       }
@@ -201,6 +214,25 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(con
     }
   }
 
+  if constexpr (SPLIT) {
+    // float32 partial of part sidx (inactive rows: zeros); no rotation (the
+    // split is not combined with rotary positions)
+    if (row_exists) {
+      const float sc = row_active ? p.scale : 0.f;
+      float* pq = p.part_o + ((int64_t)sidx * p.part_rows + rowbase + qi) * DH;
+#pragma unroll
+      for (int dt = 0; dt < DH / 32; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int d = 32 * dt + 8 * j + 4 * kg;
+          f32x4 v4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v4[e] = acc[dt][4 * j + e] * sc;
+          *reinterpret_cast<f32x4*>(pq + d) = v4;
+        }
+    }
+    return;
+  }
   if (row_exists) {
     const float sc = row_active ? p.scale : 0.f;
     // rotary positions: G_Q = R^T G_Q~ (the lane's four columns are two
@@ -610,6 +642,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
   int unit, kb;
   if (!map_work(blockIdx.x, p.groups, p.per_group, p.xcd_map, unit, kb)) return;
   const int b = unit / p.H_kv, g = unit - (unit / p.H_kv) * p.H_kv;
+  // split over the query heads: part hs covers heads [rr_lo, rr_hi) of the group
+  const int hs = kb % p.hsplits;
+  kb /= p.hsplits;
+  const int rr_lo = (int)((int64_t)hs * p.group / p.hsplits);
+  const int rr_hi = (int)((int64_t)(hs + 1) * p.group / p.hsplits);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, kg = lane >> 5;
   const int h = w & 1;                                   // key half
   const bool is_x = w < 4, is_s = (w & 2) == 0;          // XS / YV use P, XD / YK use G_S
@@ -639,7 +676,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
   const int qb_first = q_first / C::BM;
   const int qb_end = (Lq + C::BM - 1) / C::BM;
   const int nq = k_lo < Lk && qb_first < qb_end ? qb_end - qb_first : 0;
-  const int nsteps = nq * p.group;
+  const int nsteps = nq * (rr_hi - rr_lo);
 
   if (nsteps > 0) {
     if (is_x) {
@@ -896,7 +933,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
       }
     };
 
-    int i_rr = 0, i_qb = qb_first;   // next step to copy
+    int i_rr = rr_lo, i_qb = qb_first;   // next step to copy
     int xs_qb = qb_first;            // query block of the step XS exponentiates next
     auto next = [&](int& rr, int& qb) __attribute__((always_inline)) {
       if (++qb == qb_end) { qb = qb_first; ++rr; }
@@ -999,10 +1036,97 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
         }
       }
   };
+  if (p.hsplits > 1) {
+    // float32 partials of this part of the heads (no rotation: the split is
+    // not combined with rotary positions)
+    if (!is_x) {
+      const int64_t krow = b * p.krow_sb + g * p.krow_sh + sv.k_row0;
+      auto store_part = [&](auto NTC, float* base, int D, float sc) __attribute__((always_inline)) {
+        constexpr int NT = decltype(NTC)::value;
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int kk = kh0 + 32 * kb2 + 8 * (e >> 2) + 4 * kg + (e & 3);
+              if (kk < nk_lim)
+                base[((int64_t)hs * p.part_krows + krow + kk) * D + 32 * nt + (lane & 31)] = R[kb2 * NT + nt][e] * sc;
+            }
+      };
+      if (is_s) store_part(IC<DV / 32>(), p.part_dv, DV, 1.f);
+      else store_part(IC<DH / 32>(), p.part_dk, DH, p.scale);
+    }
+    return;
+  }
   if (!is_x) {
     if (is_s) store(IC<DV / 32>(), IC<0>(), dVb, p.v_sr, 1.f);
     else if (p.rope & kRopeDK) store(IC<DH / 32>(), IC<1>(), dKb, p.dk_sr, p.scale);
     else store(IC<DH / 32>(), IC<0>(), dKb, p.dk_sr, p.scale);
+  }
+}
+
+// ============================================================== split sums
+// G_Q of a dQ pass split over the keys: the float32 parts summed in order
+// (G_Q is a plain sum over the keys, eq. A.10.8), one wave per row.
+template <typename T, int DH>
+__global__ __launch_bounds__(256) void dq_combine_kernel(const KernelParams p) {
+  constexpr int CPL = DH / 64;  // columns per lane
+  const int b = blockIdx.z, r = blockIdx.y, lane = threadIdx.x & 63;
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const SeqView sv = seq_view(p, b);
+  if (i >= sv.nq_lim) return;
+  const int64_t row = b * p.lse_sb + r * p.lse_sh + sv.q_row0 + i;
+  float acc[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+  for (int s = 0; s < p.splits; ++s) {
+    const float* pq = p.part_o + (s * p.part_rows + row) * DH + CPL * lane;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) acc[c] += pq[c];
+  }
+  T* q = (T*)p.dq + b * p.dq_sb + (sv.q_row0 + i) * p.dq_sr + r * p.dq_sh + CPL * lane;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) q[c] = (T)acc[c];
+}
+
+// G_K and G_V of a dK/dV pass split over the query heads: the float32 parts
+// summed in order (the sums over the group's heads of [A.10 sec. A.10.5]),
+// one wave per key row.
+template <typename T, int DH, int DV>
+__global__ __launch_bounds__(256) void dkdv_combine_kernel(const KernelParams p) {
+  const int b = blockIdx.z, g = blockIdx.y, lane = threadIdx.x & 63;
+  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const SeqView sv = seq_view(p, b);
+  if (j >= sv.nk_lim) return;
+  const int64_t krow = b * p.krow_sb + g * p.krow_sh + sv.k_row0 + j;
+  {
+    constexpr int CPL = DH / 64;
+    float acc[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+    for (int s = 0; s < p.hsplits; ++s) {
+      const float* pk = p.part_dk + (s * p.part_krows + krow) * DH + CPL * lane;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) acc[c] += pk[c];
+    }
+    T* dk = (T*)p.dk + b * p.dk_sb + (sv.k_row0 + j) * p.dk_sr + g * p.dk_sh + CPL * lane;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) dk[c] = (T)acc[c];
+  }
+  {
+    constexpr int CPL = DV / 64;
+    float acc[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+    for (int s = 0; s < p.hsplits; ++s) {
+      const float* pv = p.part_dv + (s * p.part_krows + krow) * DV + CPL * lane;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) acc[c] += pv[c];
+    }
+    T* dv = (T*)p.dv + b * p.v_sb + (sv.k_row0 + j) * p.v_sr + g * p.v_sh + CPL * lane;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) dv[c] = (T)acc[c];
   }
 }
 
@@ -1012,7 +1136,16 @@ static int launch_dq_t(const KernelParams& p, void* stream) {
   const int64_t units = p.xcd_map ? ((p.groups + 7) / 8) * 8 : p.groups;
   const int64_t grid = units * p.per_group;
   if (grid <= 0) return (int)hipSuccess;
-  hipLaunchKernelGGL((bwd_dq_kernel<T, DH, DV>), dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, p);
+  if (p.splits > 1) {
+    hipLaunchKernelGGL((bwd_dq_kernel<T, DH, DV, true>), dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream,
+                       p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return (int)e;
+    hipLaunchKernelGGL((dq_combine_kernel<T, DH>), dim3((unsigned)((p.n_q + 3) / 4), (unsigned)p.H_q, (unsigned)p.B),
+                       dim3(256), 0, (hipStream_t)stream, p);
+    return (int)hipGetLastError();
+  }
+  hipLaunchKernelGGL((bwd_dq_kernel<T, DH, DV, false>), dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, p);
   return (int)hipGetLastError();
 }
 
@@ -1053,6 +1186,18 @@ int launch_bwd_dq(const KernelParams& p, int dtype, int d_h, int d_v, void* stre
 
 int launch_bwd_dkdv(const KernelParams& p, int dtype, int d_h, int d_v, void* stream) {
   ATTN_DISPATCH(launch_dkdv_t)
+}
+
+template <typename T, int DH, int DV>
+static int launch_dkdv_combine_t(const KernelParams& p, void* stream) {
+  if (p.B <= 0 || p.n_k <= 0) return (int)hipSuccess;
+  hipLaunchKernelGGL((dkdv_combine_kernel<T, DH, DV>), dim3((unsigned)((p.n_k + 3) / 4), (unsigned)p.H_kv, (unsigned)p.B),
+                     dim3(256), 0, (hipStream_t)stream, p);
+  return (int)hipGetLastError();
+}
+
+int launch_dkdv_combine(const KernelParams& p, int dtype, int d_h, int d_v, void* stream) {
+  ATTN_DISPATCH(launch_dkdv_combine_t)
 }
 
 }  // namespace attn

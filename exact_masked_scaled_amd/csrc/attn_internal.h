@@ -55,6 +55,14 @@ struct KernelParams {
   float* part_o;
   float* part_lse;
   int64_t part_rows;
+  // dK/dV pass split over the query heads of a group (hsplits > 1): part h
+  // of the heads writes float32 partial G_K / G_V of its keys at
+  // part_dk [h][krows][d_h] / part_dv [h][krows][d_v], key row index
+  // b * krow_sb + g * krow_sh + (first row of the sequence) + j
+  int32_t hsplits;
+  float* part_dk;
+  float* part_dv;
+  int64_t krow_sb, krow_sh, part_krows;
   // rotary positions: table [n_pos][d_h/2][2] of (cos, sin); rope flags say
   // which operand a kernel turns (kRopeQ: Q rows as loaded, forward;
   // kRopeDQ / kRopeDK: G_Q / G_K turned back in the stores); query row i of
@@ -104,6 +112,7 @@ attn_status linear_bwd(const attn_linear& L, const void* X, const void* W, const
 int launch_fwd(const KernelParams& p, int dtype, int d_h, int d_v, void* stream);
 int launch_bwd_dq(const KernelParams& p, int dtype, int d_h, int d_v, void* stream);
 int launch_bwd_dkdv(const KernelParams& p, int dtype, int d_h, int d_v, void* stream);
+int launch_dkdv_combine(const KernelParams& p, int dtype, int d_h, int d_v, void* stream);
 // forward split over the keys (p.splits > 1): partial pass, then the merge
 int launch_fwd_split(const KernelParams& p, int dtype, int d_h, int d_v, void* stream);
 int launch_fwd_combine(const KernelParams& p, int dtype, int d_v, void* stream);

@@ -121,8 +121,16 @@ attn_status attn_validate(const attn_problem* prob, const attn_mask* mask);
 
 /* Bytes of device workspace attn_bwd needs for `prob` (256-byte aligned
  * base): per-row float32 D_i = rowsum(G_O o O), B * H_q * n_q floats (an
- * upper bound of H_q * cu_seqlens_q[B] in the packed layout).  Its contents
- * on entry are ignored. */
+ * upper bound of H_q * cu_seqlens_q[B] in the packed layout), and, when the
+ * problem's grids are too small for the GPU, float32 partials of divided
+ * passes: the dQ pass over parts of the keys (when it has fewer than 384
+ * workgroups of 128 rows and the keys span at least 8 tiles of 64: parts =
+ * min(ceil(512 / workgroups), tiles / 4, 16), each holding G_Q of every row)
+ * and the bf16 dK/dV pass over parts of each group's query heads (fewer than
+ * 192 workgroups of 128 keys: parts = min(ceil(256 / workgroups), H_q / H_kv,
+ * 8), each holding G_K and G_V of every key row); the parts are summed in a
+ * fixed order, so results stay reproducible.  Contents on entry are
+ * ignored. */
 size_t attn_bwd_workspace_size(const attn_problem* prob);
 
 /* Forward.  Q [B,H_q,n_q,d_h], K [B,H_kv,n_k,d_h], V [B,H_kv,n_k,d_v] in;

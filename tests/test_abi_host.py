@@ -108,12 +108,45 @@ def test_calls_reject_before_any_launch():
     assert A.status_string(A.EMPTY_ROW).startswith("an active query row")
 
 
+def _al(x):
+    return (x + 255) // 256 * 256
+
+
 def test_workspace_size():
     lib_or_skip()
-    p = prob(B=3, H_q=4, n_q=100, d_h=128)
-    rows = 3 * 4 * 100
-    assert A.workspace_size(p) == (rows * 4 + 255) // 256 * 256
+    # a grid that fills the GPU: D only
+    p = prob(B=8, H_q=32, H_kv=8, n_q=4096, n_k=4096, d_h=128, d_v=128)
+    assert A.workspace_size(p) == _al(8 * 32 * 4096 * 4)
     assert A.workspace_size(prob(B=0)) == 0
+    # float32 (no head split) with few keys (no key split): D only
+    assert A.workspace_size(prob(B=3, H_q=4, n_q=100, d_h=128, dtype=A.F32)) == _al(3 * 4 * 100 * 4)
+
+
+def test_workspace_size_divided_passes():
+    """Small grids divide the backward passes; the workspace then also holds
+    their float32 partials: the dQ pass over parts of the keys when fewer than
+    384 of its workgroups exist and the keys span at least 8 tiles of 64
+    (parts = min(ceil(512 / workgroups), tiles / 4, 16)); the bf16 dK/dV pass
+    over parts of each group's query heads when fewer than 192 of its
+    workgroups exist (parts = min(ceil(256 / workgroups), group, 8))."""
+    lib_or_skip()
+    # chunked MQA: B=2, H_q=32, H_kv=1, n_q=256, n_k=8192, d=128
+    p = prob(B=2, H_q=32, H_kv=1, n_q=256, n_k=8192, d_h=128, d_v=128)
+    rows, krows = 2 * 32 * 256, 2 * 1 * 8192
+    dq_wgs, kv_wgs = 2 * 32 * 2, 2 * 1 * 64
+    s = min(-(-512 // dq_wgs), 128 // 4, 16)
+    hs = min(-(-256 // kv_wgs), 32, 8)
+    assert (s, hs) == (4, 2)
+    want = _al(rows * 4) + _al(s * rows * 128 * 4) + _al(hs * krows * 256 * 4)
+    assert A.workspace_size(p) == want
+    # packed rows: partial rows follow the packed totals
+    pk = packed([0, 100, 300], [0, 600, 1200], H_q=4, H_kv=2)
+    rows_p, krows_p = 4 * 300, 2 * 1200
+    dq_wgs, kv_wgs = 2 * 4 * 2, 2 * 2 * 5
+    s = min(-(-512 // dq_wgs), 10 // 4, 16)
+    hs = min(-(-256 // kv_wgs), 2, 8)
+    assert A.workspace_size(pk) == (_al(2 * 4 * 200 * 4) + _al(s * rows_p * 128 * 4)
+                                    + _al(hs * krows_p * (128 + 64) * 4))
 
 
 def test_validation_per_sequence_offsets():

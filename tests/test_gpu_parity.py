@@ -213,3 +213,28 @@ def test_staged_backward_equals_bwd():
     torch.cuda.synchronize()
     assert bool((dk == ref["GK"]).all()) and bool((dv == ref["GV"]).all())
     assert bool((dq == ref["GQ"]).all())
+
+
+DIVIDED_CASES = [
+    # (name, dtype, B, H_q, H_kv, n_q, n_k, d_h, d_v, causal, offset, lens_q, lens_k)
+    ("bf16_chunked_gqa_divided", W.BF16, 1, 8, 2, 96, 1024, 128, 128, True, 928, None, None),
+    ("bf16_cross_mqa_divided_ragged", W.BF16, 2, 8, 1, 70, 700, 128, 64, False, 0, [70, 33], [700, 517]),
+    ("f32_chunked_divided", W.F32, 1, 2, 1, 64, 640, 64, 64, True, 576, None, None),
+]
+
+
+@pytest.mark.parametrize("case", DIVIDED_CASES, ids=lambda c: c[0])
+def test_divided_backward_parity(case):
+    """Grids too small for the GPU divide the backward passes (dQ over key
+    parts, bf16 dK/dV over parts of each group's heads, float32 partials
+    summed by combine kernels): the whole result against the oracle."""
+    name, dtype, B, H_q, H_kv, n_q, n_k, d_h, d_v, causal, off, lq, lk = case
+    P.say(f"[parity] {name}")
+    prob = A.make_problem(B, H_q, H_kv, n_q, n_k, d_h, d_v, A.BF16 if dtype == W.BF16 else A.F32)
+    d_only = (B * H_q * n_q * 4 + 255) // 256 * 256
+    assert A.workspace_size(prob) > d_only  # partials present: the passes are divided
+    wl = W.custom_workload(dtype, B, H_q, H_kv, n_q, n_k, d_h, d_v, causal, off, name)
+    inp = W.make_custom_inputs(wl, seed=zlib.crc32(name.encode()) % 10000, seqlens_q=lq, seqlens_k=lk)
+    gpu = P.run_gpu(inp)
+    errs, ref = P.compare_full(inp, gpu)
+    P.assert_within(errs, dtype, name)

@@ -7,9 +7,9 @@ Tolerance: max|gpu - ref| / max|ref| <= 1e-5 (float32 I/O) or 2e-2 (bf16 I/O)
 per tensor, as for the unrotated path.  Besides the oracle, the fused forms
 are checked against the unfused ones: the forward turns Q in registers through
 the same rotation as the standalone kernel, so attn_fwd_rope equals attn_fwd
-on explicitly rotated inputs bit for bit; in the backward G_V is bitwise that
-of attn_bwd on rotated inputs and G_Q / G_K differ from turning back a
-rounded G_Q~ / G_K~ only by that rounding."""
+on explicitly rotated inputs bit for bit; in the backward G_Q / G_K differ
+from turning back a rounded G_Q~ / G_K~ only by that rounding, and G_V from
+attn_bwd on rotated inputs only by float32 summation order."""
 
 import zlib
 
@@ -116,9 +116,10 @@ def test_rope_fused_equals_unfused(case):
     dq_u = A.rope_apply(dqt, k, v, cs, operand="q", inverse=True, **kw)
     dk_u = A.rope_apply(q, dkt, v, cs, operand="k", inverse=True, **kw)
     torch.cuda.synchronize()
-    assert torch.equal(dv_f, dv_u)
+    # G_V: the same sums, but the unrotated backward may divide a small grid's
+    # passes (float32 partials summed in another order), so to rounding
     tol = 1e-2 if dtype == W.BF16 else 1e-6  # one bf16 rounding of G_Q~ / G_K~
-    for got, want, lens in ((dq_f, dq_u, lq), (dk_f, dk_u, lk)):
+    for got, want, lens in ((dq_f, dq_u, lq), (dk_f, dk_u, lk), (dv_f, dv_u, lk)):
         g, w = P.to_f64(got), P.to_f64(want)
         for b in range(q.shape[0]):
             n = got.shape[2] if lens is None else lens[b]
