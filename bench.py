@@ -4,7 +4,8 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3] [--uniform-len N]
 
 One step = the whole hot path over one batch of synthetic input: the forward
-(O and lse) and the backward's two passes (the query-stationary pass: D and
+(O and lse; split over the keys where the library's automatic part count
+divides it) and the backward's two passes (the query-stationary pass: D and
 G_Q; the key-stationary pass: G_K and G_V), all through the C ABI on one HIP
 stream, inputs resident in HBM.  Default workload: bf16 causal GQA with key and
 row padding, B=8, H_q=32, H_kv=8, n=4096, d=128 (lengths drawn in [2048, 4096]).
@@ -155,11 +156,24 @@ def measure(torch, attn, W, wl, uniform_len, steps, warmup, packed=False):
     staged = attn.StagedBackward(q, k, v, o, lse, do, dq, dk, dv, ws, **kw)
     stream = torch.cuda.current_stream()
     names = ("fwd", "bwd_dq", "bwd_dkdv")
+    # the forward split over the keys where the library's automatic part
+    # count divides it (few query rows per KV head against long key ranges)
+    pf = attn._problem_from(q, k, v, attn._strides(o), kw.get("cu_seqlens_q"), kw.get("cu_seqlens_k"),
+                            kw.get("max_seqlen_q"), kw.get("max_seqlen_k"))
+    split_fwd = attn.splitkv_workspace_size(pf, 0) > attn.splitkv_workspace_size(pf, 1)
+    ws_f = torch.empty(max(attn.splitkv_workspace_size(pf, 0), 1), dtype=torch.uint8, device=q.device) \
+        if split_fwd else None
+
+    def forward():
+        if split_fwd:
+            attn.fwd_splitkv(q, k, v, num_splits=0, out=o, lse=lse, workspace=ws_f, stream=stream, **kw)
+        else:
+            attn.fwd(q, k, v, out=o, lse=lse, stream=stream, **kw)
 
     def step(events=None):
         if events is not None:
             events[0].record(stream)
-        attn.fwd(q, k, v, out=o, lse=lse, stream=stream, **kw)
+        forward()
         if events is not None:
             events[1].record(stream)
         staged.dq(stream)
@@ -182,9 +196,9 @@ def measure(torch, attn, W, wl, uniform_len, steps, warmup, packed=False):
     ms_per_step = (t1 - t0) * 1e3 / steps
     kern_ms = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps for j, n in enumerate(names)}
     device = q.device
-    del q, k, v, do, o, lse, dq, dk, dv, ws, staged
+    del q, k, v, do, o, lse, dq, dk, dv, ws, staged, ws_f
     torch.cuda.synchronize()
-    return inp, work, ms_per_step, kern_ms, device
+    return inp, work, ms_per_step, kern_ms, device, split_fwd
 
 
 def measure_forward_split(torch, attn, W, wl, steps, warmup):
@@ -386,7 +400,8 @@ def main(argv=None):
         return 2
     attn.lib()  # fail loudly without the library
     wl = W.WORKLOADS[args.workload]
-    inp, work, ms_per_step, kern_ms, dev_of = measure(torch, attn, W, wl, args.uniform_len, args.steps, args.warmup)
+    inp, work, ms_per_step, kern_ms, dev_of, split_fwd = measure(torch, attn, W, wl, args.uniform_len, args.steps,
+                                                                 args.warmup)
     names = ("fwd", "bwd_dq", "bwd_dkdv")
 
     flop = work["fwd_flop"] + work["bwd_flop"]
@@ -434,6 +449,7 @@ def main(argv=None):
             "literal_formula_fwd_gflop": round(work["literal_fwd_flop"] / 1e9, 3),
         },
         "kernels": kernels,
+        "forward": "split over keys" if split_fwd else "unsplit",
         "roofline": roof,
         "cpu_baseline": None,
     }
@@ -453,7 +469,7 @@ def main(argv=None):
             if wid == args.workload and ulen == args.uniform_len and not pk:
                 continue
             owl = W.WORKLOADS[wid]
-            _, ow, oms, okern, _ = measure(torch, attn, W, owl, ulen, 10, 3, packed=pk)
+            _, ow, oms, okern, _, osplit = measure(torch, attn, W, owl, ulen, 10, 3, packed=pk)
             oflop = ow["fwd_flop"] + ow["bwd_flop"]
             ov = oflop / (oms * 1e-3) / 1e12
             label = owl.name + (f"_uniform{ulen}" if ulen else "") + ("_packed" if pk else "")
@@ -461,6 +477,7 @@ def main(argv=None):
                            "value": round(ov, 2), "unit": "TFLOP/s", "ms_per_step": round(oms, 4),
                            "pct_of_peak": round(100 * ov / PEAK_TFLOPS[owl.dtype], 2),
                            "visible_pairs": ow["pairs"], "kernels_ms": {n: round(t, 4) for n, t in okern.items()},
+                           "forward": "split over keys" if osplit else "unsplit",
                            "steps": 10, "warmup": 3})
         result["other_workloads"] = others
         # forward only, split over the keys, where few query rows meet a long key range
