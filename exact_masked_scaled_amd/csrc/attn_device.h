@@ -305,6 +305,37 @@ struct TileLoad {
       __builtin_amdgcn_global_load_lds((const void*)src, (ATTN_LDS void*)(lds + first * L::EPC), 16, 0, 0);
     }
   }
+
+  // The same copy for a tile whose rows all lie below the limit, with the
+  // per-lane parts of the addresses computed once per kernel: each lane's
+  // byte offset from the tile's first row (lane_offsets) is fixed, so a copy
+  // is a wave-uniform base plus that 32-bit offset (the scalar-base form of
+  // the load) and costs no vector arithmetic.  Requires
+  // ROWS * row_stride * sizeof(T) < 2^31 (fits()).
+  static __device__ __forceinline__ bool fits(int64_t row_stride) {
+    return row_stride >= 0 && row_stride <= (int64_t)(0x7fffffff / ((int64_t)ROWS * (int64_t)sizeof(T))) - D;
+  }
+  static __device__ __forceinline__ void lane_offsets(int64_t row_stride, int tid, uint32_t (&off)[N]) {
+    const int wave_base = (tid >> 6) * 64, lane = tid & 63;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int pc = wave_base + NT * i + lane;
+      const int row = pc / L::CH;
+      const int chunk = (pc % L::CH) ^ L::f(row);
+      off[i] = (uint32_t)(((int64_t)row * row_stride + chunk * L::EPC) * (int64_t)sizeof(T));
+    }
+  }
+  static __device__ __forceinline__ void issue_full(const T* base, int64_t row_stride, int row0,
+                                                    const uint32_t (&off)[N], T* lds, int tid) {
+    const int wave_base = __builtin_amdgcn_readfirstlane((tid >> 6) * 64);
+    const char* tile = reinterpret_cast<const char*>(base + (int64_t)row0 * row_stride);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int first = wave_base + NT * i;
+      __builtin_amdgcn_global_load_lds((const void*)(tile + off[i]), (ATTN_LDS void*)(lds + first * L::EPC), 16,
+                                       0, 0);
+    }
+  }
 };
 
 // Wait until every global-to-LDS copy issued by this wave has landed.

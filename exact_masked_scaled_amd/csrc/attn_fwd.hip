@@ -139,8 +139,22 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(const 
     // K/V tiles stream through two LDS buffers with direct global-to-LDS loads
     using KL = TileLoad<T, C::BN, DH, 64 * C::NW>;
     using VL = TileLoad<T, C::BN, DV, 64 * C::NW>;
-    KL::issue(Kb, p.k_sr, t_lo * C::BN, Lk, k_lds0, tid);
-    VL::issue(Vb, p.v_sr, t_lo * C::BN, Lk, v_lds0, tid);
+    // per-lane copy offsets, fixed for the loop (tiles wholly below L_k take
+    // the scalar-base copy; the last, partial tile clamps its rows)
+    uint32_t k_off[KL::N], v_off[VL::N];
+    const bool fast = KL::fits(p.k_sr) && VL::fits(p.v_sr);
+    KL::lane_offsets(p.k_sr, tid, k_off);
+    VL::lane_offsets(p.v_sr, tid, v_off);
+    auto copy_tile = [&](int t, T* kl, T* vl) __attribute__((always_inline)) {
+      if (fast && (t + 1) * C::BN <= Lk) {
+        KL::issue_full(Kb, p.k_sr, t * C::BN, k_off, kl, tid);
+        VL::issue_full(Vb, p.v_sr, t * C::BN, v_off, vl, tid);
+      } else {
+        KL::issue(Kb, p.k_sr, t * C::BN, Lk, kl, tid);
+        VL::issue(Vb, p.v_sr, t * C::BN, Lk, vl, tid);
+      }
+    };
+    copy_tile(t_lo, k_lds0, v_lds0);
     if (p.rope & kRopeQ) {
       // rotary positions: the lane's row at position qi + rope_pos[b], turned
       // while the first tiles are in flight
@@ -219,18 +233,12 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(const 
 
     // two tiles per trip so each LDS buffer address is a compile-time constant
     for (int t = t_lo; t < t_hi; t += 2) {
-      if (t + 1 < t_hi) {
-        KL::issue(Kb, p.k_sr, (t + 1) * C::BN, Lk, k_lds1, tid);
-        VL::issue(Vb, p.v_sr, (t + 1) * C::BN, Lk, v_lds1, tid);
-      }
+      if (t + 1 < t_hi) copy_tile(t + 1, k_lds1, v_lds1);
       if (t < wtiles) tile(t, k_lds0, v_lds0);
       wait_tile_loads();
       __syncthreads();
       if (t + 1 >= t_hi) break;
-      if (t + 2 < t_hi) {
-        KL::issue(Kb, p.k_sr, (t + 2) * C::BN, Lk, k_lds0, tid);
-        VL::issue(Vb, p.v_sr, (t + 2) * C::BN, Lk, v_lds0, tid);
-      }
+      if (t + 2 < t_hi) copy_tile(t + 2, k_lds0, v_lds0);
       if (t + 1 < wtiles) tile(t + 1, k_lds1, v_lds1);
       wait_tile_loads();
       __syncthreads();
