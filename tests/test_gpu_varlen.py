@@ -213,3 +213,45 @@ def test_padding_rows_never_read(case):
         assert (P.to_f64(o[b, :, lq[b]:]) == 0).all() and (P.to_f64(dq[b, :, lq[b]:]) == 0).all()
         assert (P.to_f64(o_s[b, :, lq[b]:]) == 0).all()
         assert (P.to_f64(dk[b, :, lk[b]:]) == 0).all() and (P.to_f64(dv[b, :, lk[b]:]) == 0).all()
+
+
+# --------------------------------------------------------------------- more sequences than one launch takes
+def test_many_sequences_chunked_launches():
+    """300 sequences with their own lengths and offsets (more than one
+    launch's 128): the padded forward, the split forward, the backward (its
+    dK/dV pass divided over heads for this small grid), and the packed
+    layout, against the oracle."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(2024)
+    B, H_q, H_kv, n_q, n_k, d = 300, 2, 1, 48, 80, 128
+    lq = rng.integers(0, n_q + 1, size=B).tolist()
+    lk = [int(x) for x in rng.integers(1, n_k + 1, size=B)]
+    offs = [int(rng.integers(0, k_ + 1)) for k_ in lk]  # row 0 sees keys 0..off
+    wl = W.custom_workload(W.BF16, B, H_q, H_kv, n_q, n_k, d, d, True, 0, "many_seqs")
+    inp = W.make_custom_inputs(wl, seed=77, seqlens_q=lq, seqlens_k=lk)
+    kw = dict(causal=True, offset=offs, seqlens_q=lq, seqlens_k=lk)
+    inp.mask_kwargs = lambda: kw
+    P.say("[varlen] 300 sequences, padded")
+    gpu = P.run_gpu(inp)
+    errs, ref = P.compare_full(inp, gpu)
+    P.assert_within(errs, W.BF16, "many sequences padded")
+    q, k, v = P.to_device(inp.Q), P.to_device(inp.K), P.to_device(inp.V)
+    o_s, lse_s = A.fwd_splitkv(q, k, v, num_splits=2, **kw)
+    torch.cuda.synchronize()
+    es = {"O": P.rel_err(P.to_f64(o_s), ref["O"]), "lse": P.rel_err(P.to_f64(lse_s), ref["lse"])}
+    P.assert_within(es, W.BF16, "many sequences split forward")
+    # packed: the same sequences without padding rows
+    P.say("[varlen] 300 sequences, packed")
+    cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(int).tolist()
+    cu_k = np.concatenate([[0], np.cumsum(lk)]).astype(int).tolist()
+    qp, kp, vp, dop = (P.to_device(_pack(inp.Q, lq)), P.to_device(_pack(inp.K, lk)), P.to_device(_pack(inp.V, lk)),
+                       P.to_device(_pack(inp.GO, lq)))
+    pk = dict(causal=True, offset=offs, cu_seqlens_q=cu_q, cu_seqlens_k=cu_k, max_seqlen_q=n_q, max_seqlen_k=n_k)
+    op, lsep = A.fwd(qp, kp, vp, **pk)
+    dqp, dkp, dvp = A.bwd(qp, kp, vp, op, lsep, dop, **pk)
+    torch.cuda.synchronize()
+    for b in range(B):
+        rq, rk = slice(cu_q[b], cu_q[b + 1]), slice(cu_k[b], cu_k[b + 1])
+        for got, want in ((op[rq].transpose(0, 1), gpu["O"][b, :, :lq[b]]), (dqp[rq].transpose(0, 1), gpu["GQ"][b, :, :lq[b]]),
+                          (dkp[rk].transpose(0, 1), gpu["GK"][b, :, :lk[b]]), (dvp[rk].transpose(0, 1), gpu["GV"][b, :, :lk[b]])):
+            assert torch.equal(got, want), b
