@@ -74,7 +74,9 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(con
   const int qb = nqblk - 1 - item / p.group;
   const int r = g * p.group + item % p.group;
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, kg = lane >> 5;
+  // the wave index is the same in every lane: held in a scalar register, so
+  // row-range branches are scalar branches
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, kg = lane >> 5;
   const SeqView sv = seq_view(p, b);
   const int Lq = sv.Lq, Lk = sv.Lk, off = sv.off;
   const int q_lo = qb * C::BM;
@@ -607,7 +609,11 @@ struct DkvQuadCfg {
   static_assert(NS % 2 == 0, "exchange parity follows the stage");
 };
 
-template <typename T, int DH, int DV>
+// HSPLIT: the workgroup covers part of the group's query heads and writes
+// float32 partial G_K / G_V (dkdv_combine_kernel sums the parts in order).
+// ROPE: G_K is turned back in the stores (rotary positions).  Separate
+// instances keep the other paths' registers out of the plain kernel.
+template <typename T, int DH, int DV, bool HSPLIT, bool ROPE>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParams p) {
   static_assert(sizeof(T) == 2, "four-role dK/dV pass is the bf16 path");
   using C = DkvQuadCfg<T, DH, DV>;
@@ -643,10 +649,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
   if (!map_work(blockIdx.x, p.groups, p.per_group, p.xcd_map, unit, kb)) return;
   const int b = unit / p.H_kv, g = unit - (unit / p.H_kv) * p.H_kv;
   // split over the query heads: part hs covers heads [rr_lo, rr_hi) of the group
-  const int hs = kb % p.hsplits;
-  kb /= p.hsplits;
-  const int rr_lo = (int)((int64_t)hs * p.group / p.hsplits);
-  const int rr_hi = (int)((int64_t)(hs + 1) * p.group / p.hsplits);
+  int hs = 0, rr_lo = 0, rr_hi = p.group;
+  if constexpr (HSPLIT) {
+    hs = kb % p.hsplits;
+    kb /= p.hsplits;
+    rr_lo = (int)((int64_t)hs * p.group / p.hsplits);
+    rr_hi = (int)((int64_t)(hs + 1) * p.group / p.hsplits);
+  }
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, kg = lane >> 5;
   const int h = w & 1;                                   // key half
   const bool is_x = w < 4, is_s = (w & 2) == 0;          // XS / YV use P, XD / YK use G_S
@@ -1007,36 +1016,38 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        float2 t[16];
-        if constexpr (turn) {
-          // rotary positions: G_K = R^T G_K~, key kk at position kk.  The
-          // 16 table entries are read up front, clamped into the valid keys
-          // (whose rows exist), and pinned by an empty asm so the compiler
-          // cannot sink each load into its guarded store and wait for them
-          // one at a time; keys past L_k keep their exact zeros.
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int kk = kh0 + 32 * kb2 + 8 * (e >> 2) + 4 * kg + (e & 3);
-            const int kc = max(min(kk, Lk - 1), 0);
-            t[e] = *reinterpret_cast<const float2*>(p.rope_cs + (int64_t)kc * DH + ((32 * nt + (lane & 31)) & ~1));
-          }
-#pragma unroll
-          for (int e = 0; e < 16; ++e) asm volatile("" : "+v"(t[e].x), "+v"(t[e].y));
-        }
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int kk = kh0 + 32 * kb2 + 8 * (e >> 2) + 4 * kg + (e & 3);
-          float val = R[kb2 * NT + nt][e] * sc;
+        for (int eh = 0; eh < 16; eh += 8) {
+          float2 t[8];
           if constexpr (turn) {
-            const float turned = rope_back_lanes(val, t[e].x, t[e].y, odd);
-            val = kk < Lk ? turned : val;
+            // rotary positions: G_K = R^T G_K~, key kk at position kk.  Eight
+            // table entries are read up front, clamped into the valid keys
+            // (whose rows exist), and pinned by an empty asm so the compiler
+            // cannot sink each load into its guarded store and wait for them
+            // one at a time; keys past L_k keep their exact zeros.
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int kk = kh0 + 32 * kb2 + 8 * ((eh + e) >> 2) + 4 * kg + ((eh + e) & 3);
+              const int kc = max(min(kk, Lk - 1), 0);
+              t[e] = *reinterpret_cast<const float2*>(p.rope_cs + (int64_t)kc * DH + ((32 * nt + (lane & 31)) & ~1));
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(t[e].x), "+v"(t[e].y));
           }
-          if (kk < nk_lim) dst[(int64_t)kk * sr + 32 * nt + (lane & 31)] = (T)val;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int kk = kh0 + 32 * kb2 + 8 * ((eh + e) >> 2) + 4 * kg + ((eh + e) & 3);
+            float val = R[kb2 * NT + nt][eh + e] * sc;
+            if constexpr (turn) {
+              const float turned = rope_back_lanes(val, t[e].x, t[e].y, odd);
+              val = kk < Lk ? turned : val;
+            }
+            if (kk < nk_lim) dst[(int64_t)kk * sr + 32 * nt + (lane & 31)] = (T)val;
+          }
         }
-      }
   };
-  if (p.hsplits > 1) {
+  if constexpr (HSPLIT) {
     // float32 partials of this part of the heads (no rotation: the split is
     // not combined with rotary positions)
     if (!is_x) {
@@ -1061,7 +1072,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
   }
   if (!is_x) {
     if (is_s) store(IC<DV / 32>(), IC<0>(), dVb, p.v_sr, 1.f);
-    else if (p.rope & kRopeDK) store(IC<DH / 32>(), IC<1>(), dKb, p.dk_sr, p.scale);
+    else if constexpr (ROPE) store(IC<DH / 32>(), IC<1>(), dKb, p.dk_sr, p.scale);
     else store(IC<DH / 32>(), IC<0>(), dKb, p.dk_sr, p.scale);
   }
 }
@@ -1155,8 +1166,15 @@ static int launch_dkdv_t(const KernelParams& p, void* stream) {
   const int64_t grid = units * p.per_group;
   if (grid <= 0) return (int)hipSuccess;
   if constexpr (sizeof(T) == 2) {
-    hipLaunchKernelGGL((bwd_dkdv_quad_kernel<T, DH, DV>), dim3((unsigned)grid), dim3(512), 0, (hipStream_t)stream,
-                       p);
+    if (p.hsplits > 1)
+      hipLaunchKernelGGL((bwd_dkdv_quad_kernel<T, DH, DV, true, false>), dim3((unsigned)grid), dim3(512), 0,
+                         (hipStream_t)stream, p);
+    else if (p.rope & kRopeDK)
+      hipLaunchKernelGGL((bwd_dkdv_quad_kernel<T, DH, DV, false, true>), dim3((unsigned)grid), dim3(512), 0,
+                         (hipStream_t)stream, p);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_quad_kernel<T, DH, DV, false, false>), dim3((unsigned)grid), dim3(512), 0,
+                         (hipStream_t)stream, p);
   } else {
     hipLaunchKernelGGL((bwd_dkdv_kernel<T, DH, DV>), dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, p);
   }

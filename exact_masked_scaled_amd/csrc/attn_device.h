@@ -293,7 +293,7 @@ struct TileLoad {
 
   static __device__ __forceinline__ void issue(const T* base, int64_t row_stride, int row0, int limit, T* lds,
                                                int tid) {
-    const int wave_base = (tid >> 6) * 64, lane = tid & 63;
+    const int wave_base = __builtin_amdgcn_readfirstlane((tid >> 6) * 64), lane = tid & 63;
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int first = wave_base + NT * i;  // first chunk written by this wave instruction
@@ -316,7 +316,7 @@ struct TileLoad {
     return row_stride >= 0 && row_stride <= (int64_t)(0x7fffffff / ((int64_t)ROWS * (int64_t)sizeof(T))) - D;
   }
   static __device__ __forceinline__ void lane_offsets(int64_t row_stride, int tid, uint32_t (&off)[N]) {
-    const int wave_base = (tid >> 6) * 64, lane = tid & 63;
+    const int wave_base = __builtin_amdgcn_readfirstlane((tid >> 6) * 64), lane = tid & 63;
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int pc = wave_base + NT * i + lane;

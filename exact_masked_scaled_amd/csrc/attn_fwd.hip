@@ -74,7 +74,9 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(const 
     r = g * p.group + item % p.group;
   }
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  // the wave index is the same in every lane: held in a scalar register, so
+  // row-range branches are scalar branches
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const SeqView sv = seq_view(p, b);
   const int Lq = sv.Lq, Lk = sv.Lk, off = sv.off;
   const int q_lo = qb * C::BM;                          // first row of the block
