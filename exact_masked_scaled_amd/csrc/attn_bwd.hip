@@ -51,7 +51,8 @@ struct DqCfg {
 
 // SPLIT: the workgroup covers part s of its row block's key tiles and writes
 // its float32 partial G_Q (dq_combine_kernel sums the parts in order).
-template <typename T, int DH, int DV, bool SPLIT>
+// ROPE: G_Q is turned back in the stores (rotary positions); its own instance.
+template <typename T, int DH, int DV, bool SPLIT, bool ROPE>
 __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(const KernelParams p) {
   using C = DqCfg<T, DH, DV>;
   using op_t = typename Op<T>::type;
@@ -239,7 +240,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(con
     const float sc = row_active ? p.scale : 0.f;
     // rotary positions: G_Q = R^T G_Q~ (the lane's four columns are two
     // pairs); inactive rows (zeros) read an active row's table entries
-    const bool turn = (p.rope & kRopeDQ) != 0;
+    constexpr bool turn = ROPE;
     f32x4 tab[DH / 32][4];
     if (turn) {
       // all of the row's table entries in flight at once (pinned so the
@@ -1148,15 +1149,20 @@ static int launch_dq_t(const KernelParams& p, void* stream) {
   const int64_t grid = units * p.per_group;
   if (grid <= 0) return (int)hipSuccess;
   if (p.splits > 1) {
-    hipLaunchKernelGGL((bwd_dq_kernel<T, DH, DV, true>), dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream,
-                       p);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, DH, DV, true, false>), dim3((unsigned)grid), dim3(256), 0,
+                       (hipStream_t)stream, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
     hipLaunchKernelGGL((dq_combine_kernel<T, DH>), dim3((unsigned)((p.n_q + 3) / 4), (unsigned)p.H_q, (unsigned)p.B),
                        dim3(256), 0, (hipStream_t)stream, p);
     return (int)hipGetLastError();
   }
-  hipLaunchKernelGGL((bwd_dq_kernel<T, DH, DV, false>), dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, p);
+  if (p.rope & kRopeDQ)
+    hipLaunchKernelGGL((bwd_dq_kernel<T, DH, DV, false, true>), dim3((unsigned)grid), dim3(256), 0,
+                       (hipStream_t)stream, p);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<T, DH, DV, false, false>), dim3((unsigned)grid), dim3(256), 0,
+                       (hipStream_t)stream, p);
   return (int)hipGetLastError();
 }
 

@@ -39,7 +39,9 @@ __device__ __forceinline__ int key_limit(int i, int Lk, int causal, int off) {
 // SPLIT: the workgroup covers only part s of its row block's key tiles and
 // writes a normalised float32 partial output and partial lse (merged by
 // fwd_combine_kernel); otherwise it covers all of them and writes O and lse.
-template <typename T, int DH, int DV, bool SPLIT>
+// ROPE: the query rows are turned as they are loaded (rotary positions); its
+// own instance.
+template <typename T, int DH, int DV, bool SPLIT, bool ROPE>
 __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(const KernelParams p) {
   using C = FwdCfg<T, DH, DV>;
   using op_t = typename Op<T>::type;
@@ -157,7 +159,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(const 
       }
     };
     copy_tile(t_lo, k_lds0, v_lds0);
-    if (p.rope & kRopeQ) {
+    if constexpr (ROPE) {
       // rotary positions: the lane's row at position qi + rope_pos[b], turned
       // while the first tiles are in flight
       // (inactive rows hold zeros and read an active row's entries)
@@ -334,7 +336,14 @@ static int launch_fwd_t(const KernelParams& p, void* stream) {
   const int64_t units = p.xcd_map ? ((p.groups + 7) / 8) * 8 : p.groups;
   const int64_t grid = units * p.per_group;
   if (grid <= 0) return (int)hipSuccess;
-  hipLaunchKernelGGL((fwd_kernel<T, DH, DV, SPLIT>), dim3((unsigned)grid), dim3(64 * C::NW), 0,
+  if constexpr (!SPLIT) {
+    if (p.rope & kRopeQ) {
+      hipLaunchKernelGGL((fwd_kernel<T, DH, DV, false, true>), dim3((unsigned)grid), dim3(64 * C::NW), 0,
+                         (hipStream_t)stream, p);
+      return (int)hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((fwd_kernel<T, DH, DV, SPLIT, false>), dim3((unsigned)grid), dim3(64 * C::NW), 0,
                      (hipStream_t)stream, p);
   return (int)hipGetLastError();
 }
