@@ -16,9 +16,10 @@ once per pass and writes three short summaries into ``--out``:
 
 Each pass is a child process (``timeout -s KILL`` around ``rocprofv3 ... --
 python3 bench.py``) started from /tmp; this process never touches the GPU.
-Raw CSV output goes to ``--raw`` (default gpurun_out/rocprof).  Counter passes
-stay within one rocprofv3 pass's hardware limits (at most 8 SQ and 2 GRBM
-counters; FETCH_SIZE and WRITE_SIZE in runs of their own).
+Raw CSV output goes to ``--raw`` (default /tmp/attn_rocprof; the summaries
+write it as $RAW).  Counter passes stay within one rocprofv3 pass's hardware
+limits (at most 8 SQ and 2 GRBM counters; FETCH_SIZE and WRITE_SIZE in runs of
+their own).
 """
 
 from __future__ import annotations
@@ -59,7 +60,7 @@ def short_name(mangled: str):
     return m.group(1) if m else None
 
 
-def command(name: str, repo: str = "$REPO", raw: str = "$REPO/gpurun_out/rocprof") -> str:
+def command(name: str, repo: str = "$REPO", raw: str = "$RAW") -> str:
     flags, args = PASSES[name]
     lim = "timeout -s KILL 300 " if name == "trace" else "timeout -s KILL 120 "
     return (f"cd /tmp && export TMPDIR=/tmp && {lim}rocprofv3 {' '.join(flags)} -d {raw}/{name} -o run "
@@ -110,8 +111,8 @@ def mean(v):
 def write_trace(raw: str, out: str, bench: dict):
     rows = list(csv.DictReader(open(os.path.join(raw, "trace", "run_kernel_stats.csv"))))
     o = [f"# Kernel time: {WORKLOAD}\n",
-         "Made by `python -m exact_masked_scaled_amd.rocprof_evidence` (pass `trace`); the command, from the repository",
-         "root (`REPO=$PWD`, one MI355X):\n", "```", command("trace"), "```\n",
+         "Made by `python -m exact_masked_scaled_amd.rocprof_evidence --raw $RAW` (pass `trace`); the command, from the",
+         "repository root (`REPO=$PWD`, one MI355X; `RAW` the raw-output directory):\n", "```", command("trace"), "```\n",
          "| kernel | calls | avg (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
     for r in rows:
         n = short_name(r["Name"])
@@ -143,8 +144,8 @@ def write_traffic(raw: str, out: str):
     fs = copy_bytes / (mean(cf) * 1024)
     ws = copy_bytes / (mean(cw) * 1024)
     o = [f"# HBM traffic per launch: {WORKLOAD}\n",
-         "Made by `python -m exact_masked_scaled_amd.rocprof_evidence` (passes `fetch`, `write`); the commands, from the",
-         "repository root (`REPO=$PWD`, one MI355X), one counter per run:\n", "```", command("fetch"), command("write"),
+         "Made by `python -m exact_masked_scaled_amd.rocprof_evidence --raw $RAW` (passes `fetch`, `write`); the commands,",
+         "from the repository root (`REPO=$PWD`, one MI355X; `RAW` the raw-output directory), one counter per run:\n", "```", command("fetch"), command("write"),
          "```\n",
          f"Counters are KiB per dispatch. Calibration: a plain elementwise copy of {COPY_MIB} MiB (reads and writes "
          f"{copy_bytes / 1e6:.1f} MB) reads FETCH_SIZE = {mean(cf) * 1024 / 1e6:.1f} MB and WRITE_SIZE = "
@@ -178,8 +179,8 @@ def write_mfma(raw: str, out: str, bench: dict):
     dh, dv = bench["config"]["d_h"], bench["config"]["d_v"]
     executed = {"fwd": 2 * P * (dh + dv), "bwd_dq": 2 * P * (2 * dh + dv), "bwd_dkdv": 2 * P * (2 * dh + 2 * dv)}
     o = [f"# MFMA utilisation and wave-time breakdown: {WORKLOAD}\n",
-         "Made by `python -m exact_masked_scaled_amd.rocprof_evidence` (passes `mfma`, `wait`); the commands, from the",
-         "repository root (`REPO=$PWD`, one MI355X):\n", "```", command("mfma"), command("wait"), "```\n",
+         "Made by `python -m exact_masked_scaled_amd.rocprof_evidence --raw $RAW` (passes `mfma`, `wait`); the commands,",
+         "from the repository root (`REPO=$PWD`, one MI355X; `RAW` the raw-output directory):\n", "```", command("mfma"), command("wait"), "```\n",
          "rocprofv3 sums each counter over the chip (GRBM_GUI_ACTIVE over the 8 XCDs, so one XCD's active cycles are an",
          "eighth of it); figures are means over the launches of a pass. MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES /",
          "(GRBM_GUI_ACTIVE / 8 x 1024 SIMDs). The clock is one XCD's GRBM_GUI_ACTIVE cycles over the dispatch's own",
@@ -220,7 +221,7 @@ def write_mfma(raw: str, out: str, bench: dict):
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--out", default=os.path.join(ROOT, "profiles"))
-    ap.add_argument("--raw", default=os.path.join(ROOT, "gpurun_out", "rocprof"))
+    ap.add_argument("--raw", default="/tmp/attn_rocprof")
     ap.add_argument("--only", nargs="*", choices=["trace", "traffic", "mfma"], default=None,
                     help="summaries to (re)make; default all")
     ap.add_argument("--no-run", action="store_true", help="only summarise the raw output of earlier passes")

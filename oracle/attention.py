@@ -14,7 +14,7 @@ Everything is the plain definition, written out per (batch, query head) with
 dense float64 numpy matrices.  No blocking, no online softmax, no fusion: a
 reader can check each line against the equations named beside it.
 
-Readings of points the pages leave open (each is also listed in the design doc):
+Readings of points the pages leave open:
   * visible set of row i of sequence b:
         V_i = { j : j < L_k[b]  and  (not causal  or  j <= i + offset_b) }
     for active rows i < L_q[b]; 0-based indices.  The causal set {j <= i} is
