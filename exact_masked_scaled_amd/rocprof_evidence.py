@@ -150,9 +150,11 @@ def write_traffic(raw: str, out: str):
          f"Counters are KiB per dispatch. Calibration: a plain elementwise copy of {COPY_MIB} MiB (reads and writes "
          f"{copy_bytes / 1e6:.1f} MB) reads FETCH_SIZE = {mean(cf) * 1024 / 1e6:.1f} MB and WRITE_SIZE = "
          f"{mean(cw) * 1024 / 1e6:.1f} MB, so FETCH_SIZE is scaled by {fs:.3f} and WRITE_SIZE by {ws:.3f}. Each figure is "
-         "the mean over the launches of the run.\n",
-         "| kernel | FETCH_SIZE raw (MB) | WRITE_SIZE raw (MB) | HBM read (MB) | HBM write (MB) | total (MB) |",
-         "|---|---|---|---|---|---|"]
+         "the mean over the launches of the run; HBM GB/s divides the calibrated bytes by the mean duration of the "
+         "same dispatches (their start and end timestamps in the counter records), against the 8 TB/s peak.\n",
+         "| kernel | FETCH_SIZE raw (MB) | WRITE_SIZE raw (MB) | HBM read (MB) | HBM write (MB) | total (MB) | "
+         "dispatch (ms) | HBM GB/s |",
+         "|---|---|---|---|---|---|---|---|"]
     dom = None
     for k in KERNELS:
         if k not in fe or k not in wr:
@@ -160,7 +162,9 @@ def write_traffic(raw: str, out: str):
         f_ = mean(fe[k]["FETCH_SIZE"]) * 1024
         w_ = mean(wr[k]["WRITE_SIZE"]) * 1024
         tot = f_ * fs + w_ * ws
-        o.append(f"| `{k}` | {f_ / 1e6:.1f} | {w_ / 1e6:.1f} | {f_ * fs / 1e6:.1f} | {w_ * ws / 1e6:.1f} | {tot / 1e6:.1f} |")
+        dur = mean(fe[k]["_dur"] + wr[k]["_dur"])  # the dispatches of both passes
+        o.append(f"| `{k}` | {f_ / 1e6:.1f} | {w_ / 1e6:.1f} | {f_ * fs / 1e6:.1f} | {w_ * ws / 1e6:.1f} | {tot / 1e6:.1f} | "
+                 f"{dur * 1e3:.3f} | {tot / dur / 1e9:.0f} |")
         if KERNELS[k] == B.DOMINANT:
             dom = tot
     if dom is None:

@@ -58,6 +58,9 @@ def test_traffic_is_scaled_by_the_calibration_copy_and_read_back_by_bench(tmp_pa
     expect = (2000.0 * 1024) * 2.0 + 500.0 * 1024 * 1.0  # mean FETCH x 2 + WRITE x 1, KiB -> bytes
     assert f"hbm_bytes_per_launch: {expect:.0f}" in text
     assert "fetch_scale: 2.0000" in text and "write_scale: 1.0000" in text
+    row = [l for l in text.splitlines() if l.startswith("| `bwd_dkdv_quad_kernel`")][0]
+    cells = [c.strip() for c in row.split("|")[2:-1]]
+    assert cells[-2] == "0.000" and cells[-1] == f"{expect / 10e-9 / 1e9:.0f}"  # 10 ns dispatches
     monkeypatch.setattr(bench, "TRAFFIC_FILE", path)
     assert bench.load_traffic(None) == expect
 
