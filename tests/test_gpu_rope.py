@@ -195,3 +195,43 @@ def test_rope_packed_equals_padded():
         assert torch.equal(dqp[rq].transpose(0, 1), dq[b, :, :lq[b]])
         assert torch.equal(dkp[rk].transpose(0, 1), dk[b, :, :lk[b]])
         assert torch.equal(dvp[rk].transpose(0, 1), dv[b, :, :lk[b]])
+
+
+SPLIT_CASES = [
+    # decoding: one new row per sequence at position L_k[b] - 1, GQA, a long ragged cache
+    ("bf16_decode_gqa", W.BF16, 3, 8, 2, 1, 700, 128, 128, True, [699, 411, 522], [1, 1, 1], [700, 412, 523], 700),
+    # a chunk of new rows against its history, per-sequence offsets
+    ("bf16_chunk_mqa", W.BF16, 2, 8, 1, 48, 640, 128, 128, True, [592, 300], [48, 20], [640, 320], 640),
+    ("f32_decode_d64", W.F32, 2, 4, 4, 1, 300, 64, 64, True, [299, 99], [1, 1], [300, 100], 300),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: c[0])
+@pytest.mark.parametrize("parts", [0, 5])
+def test_rope_decoding_through_the_split_forward(case, parts):
+    """Rotary positions with the forward split over the keys, as a decoding
+    step composes them: Q and K turned by attn_rope_apply (in practice new K
+    rows are turned once as they enter the cache), then attn_fwd_splitkv on
+    the turned tensors (automatic part count, or 5 parts); O and lse against
+    the oracle's attention on rotated q, k."""
+    torch = pytest.importorskip("torch")
+    name, dtype, n_pos, d_h = case[0], case[1], case[-1], case[7]
+    P.say(f"[rope] split forward {name} parts={parts}")
+    inp, kw = _inputs(case)
+    cs_host, cs = _table(n_pos, d_h)
+    q, k, v = P.to_device(inp.Q), P.to_device(inp.K), P.to_device(inp.V)
+    qt = A.rope_apply(q, k, v, cs, operand="q", **kw)
+    kt = A.rope_apply(q, k, v, cs, operand="k", **kw)
+    lq, lk = kw["seqlens_q"], kw["seqlens_k"]
+    for b in range(q.shape[0]):  # rows past the active ones are not written by the rotation
+        qt[b, :, lq[b]:] = 0
+        kt[b, :, lk[b]:] = 0
+    o, lse = A.fwd_splitkv(qt, kt, v, num_splits=parts, **kw)
+    torch.cuda.synchronize()
+    f64 = W.payload_to_f64
+    go = np.zeros(inp.Q.shape[:3] + (inp.V.shape[-1],))
+    ref = oracle.attention_backward_rope(f64(inp.Q), f64(inp.K), f64(inp.V), go, cs_host, **kw)
+    errs = {"O": P.rel_err(P.to_f64(o), ref["O"]), "lse": P.rel_err(P.to_f64(lse), ref["lse"])}
+    P.assert_within(errs, dtype, f"{name} parts={parts}")
+    for b in range(q.shape[0]):
+        assert (P.to_f64(o[b, :, lq[b]:]) == 0).all() and (P.to_f64(lse[b, :, lq[b]:]) == 0).all()
