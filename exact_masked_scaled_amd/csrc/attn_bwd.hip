@@ -999,13 +999,52 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
       next(i_rr, i_qb);
       if (1 < nsteps) { issue(i_rr, i_qb, IC<1>()); next(i_rr, i_qb); }
     }
-    for (int s0 = 0; s0 <= nsteps + 2; s0 += NS) {
-      if (!body(s0, IC<0>())) break;
-      if (!body(s0 + 1, IC<1>())) break;
-      if (!body(s0 + 2, IC<2>())) break;
-      if (!body(s0 + 3, IC<3>())) break;
-      if (!body(s0 + 4, IC<4>())) break;
-      if (!body(s0 + 5, IC<5>())) break;
+    // Steps 3 .. nsteps - 1 do the whole of every role's work; only the
+    // ramp-up (0 .. 2) and ramp-down (the last steps) skip parts.  The ramps
+    // run through `body`, the steady range through `steady`, which has no
+    // ramp branches, so the steady loop keeps every role's register blocks
+    // in place (ramp branches inside the loop made the register allocator
+    // copy whole S / dP blocks at their joins every step).  Every wave runs
+    // the same sequence of steps, one barrier each.
+    auto steady = [&](int s, auto U) __attribute__((always_inline)) {
+      constexpr int u = decltype(U)::value;
+      const int ahead = min(PD - 1, nsteps - 1 - s);
+      if (is_x || ahead <= 0) stage_barrier<0>();
+      else stage_barrier<C::CPS>();
+      if (!is_x && s + PD < nsteps) { issue(i_rr, i_qb, IC<u + PD>()); next(i_rr, i_qb); }
+      constexpr int jn = u & 1;
+      if (is_x && is_s) {
+        op_t* xw = jn ? xp0 : xp1;
+        const float* rows = r_st(IC<u + NS - 1>());
+        const int q0 = xs_qb * C::BM;
+        if (full_tile(q0)) xs_iter(TR(), TR(), TR(), IC<jn>(), q_st(U), q0, rows, xw);
+        else xs_iter(TR(), TR(), F(), IC<jn>(), q_st(U), q0, rows, xw);
+        if (++xs_qb == qb_end) xs_qb = qb_first;
+      } else if (is_x) {
+        constexpr int jd = (u + 1) & 1;
+        xd_iter(TR(), TR(), IC<jd>(), o_st(IC<u + NS - 1>()), r_st(IC<u + NS - 2>()), jn ? xp1 : xp0,
+                jn ? xd1 : xd0);
+      } else if (is_s) {
+        y_iter(o_st(IC<u + NS - 2>()), jn ? xp1 : xp0);
+      } else {
+        y_iter(q_st(IC<u + NS - 3>()), jn ? xd0 : xd1);
+      }
+    };
+    static_assert(NS == 6, "the steady loop below is written for six ring stages");
+    if (body(0, IC<0>()) && body(1, IC<1>()) && body(2, IC<2>())) {
+      int s = 3;
+      for (; s + NS <= nsteps; s += NS) {
+        steady(s, IC<3>());
+        steady(s + 1, IC<4>());
+        steady(s + 2, IC<5>());
+        steady(s + 3, IC<0>());
+        steady(s + 4, IC<1>());
+        steady(s + 5, IC<2>());
+      }
+      // the remaining steps s .. nsteps + 2 (at most 8; s % NS == 3)
+      if (body(s, IC<3>()) && body(s + 1, IC<4>()) && body(s + 2, IC<5>()) && body(s + 3, IC<0>()) &&
+          body(s + 4, IC<1>()) && body(s + 5, IC<2>()) && body(s + 6, IC<3>()))
+        body(s + 7, IC<4>());
     }
   }
 
