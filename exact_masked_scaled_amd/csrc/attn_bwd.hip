@@ -1024,6 +1024,25 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
         constexpr int jd = (u + 1) & 1;
         xd_iter(TR(), TR(), IC<jd>(), o_st(IC<u + NS - 1>()), r_st(IC<u + NS - 2>()), jn ? xp1 : xp0,
                 jn ? xd1 : xd0);
+      } else if constexpr (DH == DV) {
+        // YV and YK run the same products on different tiles: one path, so
+        // their accumulators share one register assignment
+        const T* tile = is_s ? o_st(IC<u + NS - 2>()) : q_st(IC<u + NS - 3>());
+        const op_t* in = (is_s ? (jn ? xp1 : xp0) : (jn ? xd0 : xd1)) + (h * 2) * 2 * 64;
+        op_t a[2][2];
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int st = 0; st < 2; ++st) a[kb2][st] = in[(kb2 * 2 + st) * 64 + lane];
+        constexpr int NT = DV / 32;
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            const op_t bt = TrOffsets<T, DV>::read_at(tile, 16 * st, ofs[nt], ofs[NOFS / 2 + nt]);
+            mma(R[nt], a[0][st], bt);
+            mma(R[NT + nt], a[1][st], bt);
+          }
       } else if (is_s) {
         y_iter(o_st(IC<u + NS - 2>()), jn ? xp1 : xp0);
       } else {
