@@ -47,16 +47,29 @@ rocblas_handle handle_for(void* stream) {
 
 bool fits_i32(int64_t x) { return x >= 0 && x <= INT32_MAX; }
 
+// D(m x n, column-major, leading dimension ld) = 0 with plain stores, so a
+// caller may capture it in a graph (no memset node).
+template <typename E>
+__global__ void zero_columns(E* D, int64_t ld, int64_t m, int64_t n) {
+  const int64_t total = m * n, step = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += step) {
+    const int64_t c = i / m;
+    D[c * ld + (i - c * m)] = E(0);
+  }
+}
+
 // Column-major D(m x n) = op(A) op(B) (+ D if accumulate), on the stream.
 attn_status gemm(void* stream, int dtype, rocblas_operation ta, rocblas_operation tb, int64_t m, int64_t n, int64_t k,
                  const void* A, int64_t lda, const void* B, int64_t ldb, void* D, int64_t ldd, bool accumulate) {
   if (m == 0 || n == 0) return ATTN_OK;
   if (k == 0) {  // an empty sum: D = 0, or D unchanged when accumulating
     if (accumulate) return ATTN_OK;
-    const size_t es = dtype == ATTN_BF16 ? 2 : 4;
-    return hipMemset2DAsync(D, (size_t)ldd * es, 0, (size_t)m * es, (size_t)n, (hipStream_t)stream) == hipSuccess
-               ? ATTN_OK
-               : ATTN_ERR_HIP;
+    const int64_t blocks = std::min<int64_t>((m * n + 255) / 256, 2048);
+    if (dtype == ATTN_BF16)
+      zero_columns<uint16_t><<<dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream>>>((uint16_t*)D, ldd, m, n);
+    else
+      zero_columns<uint32_t><<<dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream>>>((uint32_t*)D, ldd, m, n);
+    return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
   }
   rocblas_handle h = handle_for(stream);
   if (h == nullptr) return ATTN_ERR_HIP;

@@ -38,7 +38,11 @@
  * arrays read during the call (copied by value into the kernel arguments).
  * Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the null
  * stream); nothing synchronises the host.  The library allocates no device
- * memory and keeps no global mutable state: calls are re-entrant.
+ * memory and keeps no global mutable state: calls are re-entrant.  The
+ * attention calls enqueue kernels only (no memset or copy), so a caller may
+ * capture them in a HIP graph; the host arrays are read when the call is
+ * made, so every replay of a captured call uses the lengths and offsets it
+ * was captured with.
  *
  * The per-sequence arrays (seqlens, causal_offsets, cu_seqlens) are HOST
  * arrays read during the call.
