@@ -41,8 +41,17 @@ def poison(t):
     return t
 
 
-def run_gpu(inp: W.Inputs, backward=True, poison_outputs=True):
-    """Forward (+ backward) on the GPU; returns device tensors."""
+def bench_forward_splits(prob) -> int:
+    """The forward the benchmark times: split over the keys (automatic part
+    count, 0) when the library's automatic count divides the problem,
+    otherwise unsplit (1)."""
+    return 0 if A.splitkv_workspace_size(prob, 0) > A.splitkv_workspace_size(prob, 1) else 1
+
+
+def run_gpu(inp: W.Inputs, backward=True, poison_outputs=True, num_splits=1):
+    """Forward (+ backward) on the GPU; returns device tensors.  num_splits 1
+    runs attn_fwd; any other value runs attn_fwd_splitkv with that part count
+    (0: automatic, the benchmark's choice)."""
     import torch
     wl = inp.wl
     q, k, v = to_device(inp.Q), to_device(inp.K), to_device(inp.V)
@@ -51,7 +60,13 @@ def run_gpu(inp: W.Inputs, backward=True, poison_outputs=True):
     lse = torch.empty(wl.B, wl.H_q, wl.n_q, dtype=torch.float32, device=q.device)
     if poison_outputs:
         poison(out), poison(lse)
-    o, lse = A.fwd(q, k, v, out=out, lse=lse, **kw)
+    if num_splits == 1:
+        o, lse = A.fwd(q, k, v, out=out, lse=lse, **kw)
+    else:
+        prob = A._problem_from(q, k, v, A._strides(out))
+        wsf = torch.full((max(A.splitkv_workspace_size(prob, num_splits), 1),), 0xFF, dtype=torch.uint8,
+                         device=q.device)
+        o, lse = A.fwd_splitkv(q, k, v, num_splits=num_splits, out=out, lse=lse, workspace=wsf, **kw)
     res = {"O": o, "lse": lse}
     if backward:
         do = to_device(inp.GO)
@@ -91,28 +106,68 @@ def compare_full(inp: W.Inputs, gpu: dict, backward=True) -> dict:
     return errs, ref
 
 
-def compare_groups(inp: W.Inputs, gpu: dict, groups) -> dict:
-    """Comparison on sampled (sequence, KV head) groups: every output of the
-    query heads of the group and G_K/G_V of its KV head."""
-    f64 = W.payload_to_f64
+def compare_groups(inp: W.Inputs, gpu: dict, groups=None, progress=None, workers=4) -> dict:
+    """Comparison per (sequence, KV head) group: every output of the query
+    heads of the group and G_K/G_V of its KV head, against the oracle
+    restricted to that group.  groups=None compares every group of the
+    problem, i.e. every element of every output.  The error of a tensor is
+    max|gpu - ref| / max|ref| over all compared elements."""
     wl = inp.wl
     kw = inp.mask_kwargs()
-    got = {n: [] for n in TENSORS}
-    ref = {n: [] for n in TENSORS}
-    Qf = _Lazy(inp.Q)
-    Kf = _Lazy(inp.K)
-    Vf = _Lazy(inp.V)
-    GOf = _Lazy(inp.GO)
-    for (b, g) in groups:
+    if groups is None:
+        groups = [(b, g) for b in range(wl.B) for g in range(wl.H_kv)]
+    diff = {n: 0.0 for n in TENSORS}
+    top = {n: 0.0 for n in TENSORS}
+    finite = {n: True for n in TENSORS}
+    Qf, Kf, Vf, GOf = _Lazy(inp.Q), _Lazy(inp.K), _Lazy(inp.V), _Lazy(inp.GO)
+    host = {n: t.detach().float().cpu().numpy() for n, t in gpu.items()}
+
+    def one(bg):
+        b, g = bg
         o = oracle.attention_group(Qf, Kf, Vf, GOf, b, g, **kw)
         heads = o["heads"]
-        for name in ("O", "lse", "GQ"):
-            ref[name].append(o[name].ravel())
-            got[name].append(to_f64(gpu[name][b, heads[0]:heads[-1] + 1]).ravel())
-        for name in ("GK", "GV"):
-            ref[name].append(o[name].ravel())
-            got[name].append(to_f64(gpu[name][b, g]).ravel())
-    return {n: rel_err(np.concatenate(got[n]), np.concatenate(ref[n])) for n in TENSORS}
+        res = {}
+        for name in TENSORS:
+            if name in ("GK", "GV"):
+                got = host[name][b, g].astype(np.float64)
+            else:
+                got = host[name][b, heads[0]:heads[-1] + 1].astype(np.float64)
+            ref = o[name]
+            res[name] = (bool(np.all(np.isfinite(got))),
+                         float(np.max(np.abs(got - ref))) if ref.size else 0.0,
+                         float(np.max(np.abs(ref))) if ref.size else 0.0)
+        return res
+
+    # groups are independent: a few host threads (numpy's products and large
+    # element-wise operations release the interpreter lock)
+    import concurrent.futures as cf
+    with cf.ThreadPoolExecutor(max_workers=min(workers, len(groups)) or 1) as ex:
+        for idx, res in enumerate(ex.map(one, groups)):
+            for name, (fin, d, t) in res.items():
+                finite[name] &= fin
+                diff[name] = max(diff[name], d)
+                top[name] = max(top[name], t)
+            if progress is not None and (idx + 1) % progress == 0:
+                say(f"  compared {idx + 1}/{len(groups)} groups")
+    out = {}
+    for n in TENSORS:
+        if not finite[n]:
+            out[n] = float("inf")
+        else:
+            out[n] = diff[n] / top[n] if top[n] > 0 else diff[n]
+    return out
+
+
+def record(label: str, errs: dict, **extra):
+    """Append one parity row (per-tensor errors) to the JSON-lines file named
+    by ATTN_PARITY_TABLE, when that variable is set."""
+    import json
+    import os
+    path = os.environ.get("ATTN_PARITY_TABLE")
+    if not path:
+        return
+    with open(path, "a") as f:
+        f.write(json.dumps({"case": label, **{k: float(v) for k, v in errs.items()}, **extra}) + "\n")
 
 
 class _Lazy:

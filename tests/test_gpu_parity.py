@@ -80,36 +80,38 @@ def test_workload1_full():
     P.assert_within(errs, W.F32, "workload 1")
 
 
-def _sample_groups(inp, n=2):
-    wl = inp.wl
-    units = [(b, g) for b in range(wl.B) for g in range(wl.H_kv)]
-    if inp.seqlens_k:  # include the longest and the shortest sequence
-        bl = int(np.argmax(inp.seqlens_k))
-        bs = int(np.argmin(inp.seqlens_k))
-        picks = [(bl, 0), (bs, wl.H_kv - 1)]
-    else:
-        picks = [units[0], units[-1]]
-    return picks[:n]
+FULL_SIZE = [(1, "bench"), (2, "bench"), (3, "bench"), (4, "bench"), (5, "bench"),
+             (1, "unsplit"), (4, "unsplit"), (5, "unsplit")]
 
 
-@pytest.mark.parametrize("wid", [2, 3, 4, 5])
+@pytest.mark.parametrize("wid,forward", FULL_SIZE, ids=lambda x: str(x))
 @pytest.mark.timeout(900)
-def test_full_size_workloads_sampled(wid):
-    """Full-size workloads in the benchmark's launch configuration; every
-    output of two sampled (sequence, KV-head) groups is compared with the
-    oracle, and every element of every output must be finite."""
+def test_full_size_every_group(wid, forward):
+    """The five workloads at full size, with the forward the benchmark runs
+    ("bench": split over the keys with the automatic part count where that
+    divides the problem, else unsplit) or the unsplit forward: every element
+    of O, lse, G_Q, G_K and G_V against the float64 oracle, one (sequence,
+    KV head) group at a time, plus the structural zeros of padded keys and
+    inactive rows."""
     inp = W.make_inputs(wid)
-    P.say(f"[parity] {inp.wl.describe()} lens_k={inp.seqlens_k}")
-    gpu = P.run_gpu(inp)
-    import torch
-    for name, t in gpu.items():
-        assert bool(torch.isfinite(t).all()), f"non-finite values in {name}"
-    groups = _sample_groups(inp)
-    errs = P.compare_groups(inp, gpu, groups)
-    P.assert_within(errs, inp.wl.dtype, f"workload {wid} groups {groups}")
+    wl = inp.wl
+    prob = A.make_problem(wl.B, wl.H_q, wl.H_kv, wl.n_q, wl.n_k, wl.d_h, wl.d_v,
+                          A.BF16 if wl.dtype == W.BF16 else A.F32)
+    ns = P.bench_forward_splits(prob) if forward == "bench" else 1
+    label = f"workload {wid} ({'split forward, automatic parts' if ns == 0 else 'unsplit forward'})"
+    P.say(f"[parity] {label}: {wl.describe()} lens_k={inp.seqlens_k}")
+    gpu = P.run_gpu(inp, num_splits=ns)
+    errs = P.compare_groups(inp, gpu, progress=8)
+    P.record(f"workload {wid}", errs, forward="split" if ns == 0 else "unsplit", dtype=wl.dtype,
+             elements={n: int(t.numel()) for n, t in gpu.items()})
+    P.assert_within(errs, wl.dtype, label)
     if inp.seqlens_k:
         for b, L in enumerate(inp.seqlens_k):
             assert not bool(gpu["GK"][b, :, L:].any()) and not bool(gpu["GV"][b, :, L:].any())
+    if inp.seqlens_q:
+        for b, L in enumerate(inp.seqlens_q):
+            for n in ("O", "lse", "GQ"):
+                assert not bool(gpu[n][b, :, L:].any()), n
 
 
 # --------------------------------------------------------------------- pinned examples on the GPU
