@@ -37,7 +37,8 @@ BF16 = 1
 EXPORTS = ("attn_validate", "attn_bwd_workspace_size", "attn_fwd", "attn_bwd",
            "attn_bwd_dq", "attn_bwd_dkdv", "attn_fwd_splitkv_workspace_size", "attn_fwd_splitkv",
            "attn_rope_apply", "attn_fwd_rope_workspace_size", "attn_fwd_rope",
-           "attn_bwd_rope_workspace_size", "attn_bwd_rope", "attn_linear_fwd", "attn_linear_bwd",
+           "attn_bwd_rope_workspace_size", "attn_bwd_rope", "attn_gemm_create", "attn_gemm_destroy",
+           "attn_linear_fwd", "attn_linear_bwd",
            "attn_self_attention_fwd", "attn_self_attention_bwd_workspace_size", "attn_self_attention_bwd",
            "attn_status_string", "attn_version")
 
@@ -123,16 +124,20 @@ def lib():
     L.attn_bwd_rope.argtypes = [P, M, R, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.attn_bwd_rope.restype = ctypes.c_int
     LP = ctypes.POINTER(Linear)
-    L.attn_linear_fwd.argtypes = [LP, vp, vp, vp, vp]
+    L.attn_gemm_create.argtypes = [ctypes.POINTER(vp)]
+    L.attn_gemm_create.restype = ctypes.c_int
+    L.attn_gemm_destroy.argtypes = [vp]
+    L.attn_gemm_destroy.restype = ctypes.c_int
+    L.attn_linear_fwd.argtypes = [LP, vp, vp, vp, vp, vp]
     L.attn_linear_fwd.restype = ctypes.c_int
-    L.attn_linear_bwd.argtypes = [LP, vp, vp, vp, vp, vp, ctypes.c_int32, vp]
+    L.attn_linear_bwd.argtypes = [LP, vp, vp, vp, vp, vp, vp, ctypes.c_int32, vp]
     L.attn_linear_bwd.restype = ctypes.c_int
-    L.attn_self_attention_fwd.argtypes = [P, M, ctypes.c_int32, vp, vp, vp, vp, vp, vp]
+    L.attn_self_attention_fwd.argtypes = [P, M, vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp]
     L.attn_self_attention_fwd.restype = ctypes.c_int
     L.attn_self_attention_bwd_workspace_size.argtypes = [P]
     L.attn_self_attention_bwd_workspace_size.restype = ctypes.c_size_t
-    L.attn_self_attention_bwd.argtypes = [P, M, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
-                                          vp]
+    L.attn_self_attention_bwd.argtypes = [P, M, vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                          ctypes.c_size_t, vp]
     L.attn_self_attention_bwd.restype = ctypes.c_int
     L.attn_status_string.argtypes = [ctypes.c_int]
     L.attn_status_string.restype = ctypes.c_char_p
@@ -557,6 +562,50 @@ def bwd_rope(q, k, v, o, lse, do, cos_sin, *, causal=False, offset=0, seqlens_q=
 # ---------------------------------------------------------------------------
 # projections
 # ---------------------------------------------------------------------------
+class GemmContext:
+    """A caller-owned GEMM context (attn_gemm_create) for the projection
+    calls, bound to the device current when it is made; destroyed by close()
+    or when collected."""
+
+    def __init__(self):
+        h = ctypes.c_void_p()
+        st = lib().attn_gemm_create(ctypes.byref(h))
+        if st != OK:
+            raise AttnError(st, "attn_gemm_create")
+        self.handle = h
+
+    def close(self):
+        if self.handle is not None and self.handle.value:
+            lib().attn_gemm_destroy(self.handle)
+        self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # interpreter shutdown
+            pass
+
+
+_DEFAULT_GEMM = {}
+
+
+def gemm_context(device=None) -> GemmContext:
+    """This process's default context for `device` (the current one when
+    None), made on first use: the caller side, not the library, keeps it."""
+    torch = _torch()
+    dev = torch.cuda.current_device() if device is None else int(device)
+    ctx = _DEFAULT_GEMM.get(dev)
+    if ctx is None:
+        with torch.cuda.device(dev):
+            ctx = GemmContext()
+        _DEFAULT_GEMM[dev] = ctx
+    return ctx
+
+
+def _gemm_of(ctx, t):
+    return (ctx if ctx is not None else gemm_context(t.device.index)).handle
+
+
 def _check2(name, t, dtype):
     if t.dim() != 2 or t.dtype != dtype or not t.is_cuda or (t.shape[1] > 0 and t.stride(1) != 1):
         raise ValueError(f"{name} must be a 2-D GPU tensor of {dtype} with unit column stride")
@@ -572,8 +621,9 @@ def _linear_of(x, w, y_stride0=None) -> Linear:
                        y_stride0 if y_stride0 is not None else w.shape[1])
 
 
-def linear_fwd(x, w, *, out=None, stream=None):
-    """attn_linear_fwd: Y = X W for 2-D x [rows, d_in], w [d_in, d_out]."""
+def linear_fwd(x, w, *, out=None, stream=None, gemm=None):
+    """attn_linear_fwd: Y = X W for 2-D x [rows, d_in], w [d_in, d_out].
+    gemm: a GemmContext (default: gemm_context() of x's device)."""
     torch = _torch()
     _check2("x", x, x.dtype)
     _check2("w", w, x.dtype)
@@ -581,13 +631,14 @@ def linear_fwd(x, w, *, out=None, stream=None):
         out = torch.empty(x.shape[0], w.shape[1], dtype=x.dtype, device=x.device)
     _check2("out", out, x.dtype)
     lin = _linear_of(x, w, out.stride(0))
-    st = lib().attn_linear_fwd(ctypes.byref(lin), _ptr(x), _ptr(w), _ptr(out), _stream(stream))
+    st = lib().attn_linear_fwd(ctypes.byref(lin), _gemm_of(gemm, x), _ptr(x), _ptr(w), _ptr(out), _stream(stream))
     if st != OK:
         raise AttnError(st, "attn_linear_fwd")
     return out
 
 
-def linear_bwd(x, w, gy, *, gx=None, gw=None, accumulate=False, want_gx=True, want_gw=True, stream=None):
+def linear_bwd(x, w, gy, *, gx=None, gw=None, accumulate=False, want_gx=True, want_gw=True, stream=None,
+               gemm=None):
     """attn_linear_bwd: G_X = G_Y W^T and G_W = X^T G_Y (accumulate: added)."""
     torch = _torch()
     for n_, t in (("x", x), ("w", w), ("gy", gy)):
@@ -601,7 +652,8 @@ def linear_bwd(x, w, gy, *, gx=None, gw=None, accumulate=False, want_gx=True, wa
     if gw is not None and gw.stride() != w.stride():
         raise ValueError("gw must have the strides of w")
     lin = _linear_of(x, w, gy.stride(0))
-    st = lib().attn_linear_bwd(ctypes.byref(lin), _ptr(x), _ptr(w), _ptr(gy), _ptr(gx) if gx is not None else None,
+    st = lib().attn_linear_bwd(ctypes.byref(lin), _gemm_of(gemm, x), _ptr(x), _ptr(w), _ptr(gy),
+                               _ptr(gx) if gx is not None else None,
                                _ptr(gw) if gw is not None else None, 1 if accumulate else 0, _stream(stream))
     if st != OK:
         raise AttnError(st, "attn_linear_bwd")
@@ -619,7 +671,7 @@ def _self_problem(x, w, H_q, H_kv, d_h, d_v, o_stride, cu_seqlens, max_seqlen):
 
 
 def self_attention_fwd(x, w_qkv, *, H_q, H_kv, d_h, d_v, causal=False, offset=0, seqlens_q=None, seqlens_k=None,
-                       qkv=None, out=None, lse=None, stream=None, cu_seqlens=None, max_seqlen=None):
+                       qkv=None, out=None, lse=None, stream=None, cu_seqlens=None, max_seqlen=None, gemm=None):
     """attn_self_attention_fwd: x [B, n, d_model] (or packed [rows, d_model]
     with cu_seqlens), w_qkv [d_model, H_q d_h + H_kv d_h + H_kv d_v].
     Returns qkv [rows, C], O and lse (shapes as fwd())."""
@@ -641,7 +693,8 @@ def self_attention_fwd(x, w_qkv, *, H_q, H_kv, d_h, d_v, causal=False, offset=0,
         lse = torch.empty(*lse_shape, dtype=torch.float32, device=x.device)
     prob = _self_problem(x, w_qkv, H_q, H_kv, d_h, d_v, _strides(out), cu_seqlens, max_seqlen)
     mask, keep = make_mask(causal, offset, seqlens_q, seqlens_k)
-    st = lib().attn_self_attention_fwd(ctypes.byref(prob), ctypes.byref(mask), int(x.shape[-1]), _ptr(x),
+    st = lib().attn_self_attention_fwd(ctypes.byref(prob), ctypes.byref(mask), _gemm_of(gemm, x), int(x.shape[-1]),
+                                       _ptr(x),
                                        _ptr(w_qkv), _ptr(qkv), _ptr(out), _ptr(lse), _stream(stream))
     del keep
     if st != OK:
@@ -651,7 +704,7 @@ def self_attention_fwd(x, w_qkv, *, H_q, H_kv, d_h, d_v, causal=False, offset=0,
 
 def self_attention_bwd(x, w_qkv, qkv, o, lse, do, *, H_q, H_kv, d_h, d_v, causal=False, offset=0, seqlens_q=None,
                        seqlens_k=None, gx=None, gw=None, workspace=None, stream=None, cu_seqlens=None,
-                       max_seqlen=None):
+                       max_seqlen=None, gemm=None):
     """attn_self_attention_bwd: G_X (shape of x) and G_W (shape of w_qkv)."""
     torch = _torch()
     if do.stride() != o.stride():
@@ -663,7 +716,8 @@ def self_attention_bwd(x, w_qkv, qkv, o, lse, do, *, H_q, H_kv, d_h, d_v, causal
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     mask, keep = make_mask(causal, offset, seqlens_q, seqlens_k)
-    st = lib().attn_self_attention_bwd(ctypes.byref(prob), ctypes.byref(mask), int(x.shape[-1]), _ptr(x),
+    st = lib().attn_self_attention_bwd(ctypes.byref(prob), ctypes.byref(mask), _gemm_of(gemm, x), int(x.shape[-1]),
+                                       _ptr(x),
                                        _ptr(w_qkv), _ptr(qkv), _ptr(o), _ptr(lse), _ptr(do), _ptr(gx), _ptr(gw),
                                        _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(stream))
     del keep

@@ -103,9 +103,9 @@ attn_status validate_problem(const attn_problem* prob, const attn_mask* mask);
 
 // Dense products of the projections (vendor GEMM); arguments checked.
 attn_status validate_linear(const attn_linear* L);
-attn_status linear_fwd(const attn_linear& L, const void* X, const void* W, void* Y, void* stream);
-attn_status linear_bwd(const attn_linear& L, const void* X, const void* W, const void* G_Y, void* G_X, void* G_W,
-                       bool accumulate, void* stream);
+attn_status linear_fwd(attn_gemm ctx, const attn_linear& L, const void* X, const void* W, void* Y, void* stream);
+attn_status linear_bwd(attn_gemm ctx, const attn_linear& L, const void* X, const void* W, const void* G_Y, void* G_X,
+                       void* G_W, bool accumulate, void* stream);
 
 // Launchers (defined in the .hip translation units).  Return hipSuccess or
 // the launch error, as an int to keep this header free of HIP types.

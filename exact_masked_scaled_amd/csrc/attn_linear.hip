@@ -13,6 +13,10 @@
 // full width), and the backward writes G_Q, G_K, G_V into the same layout:
 // no transposes or copies between the products and the attention.
 //
+// The vendor library's handle lives in a context the caller creates
+// (attn_gemm_create), passes to every projection call and destroys: the
+// library itself holds no handle and allocates nothing on these calls.
+//
 // Row-major matrices are handed to the column-major GEMM as their transposes:
 //   Y   = X W      ->  Y^T   = W^T X^T          (N, N)
 //   G_X = G_Y W^T  ->  G_X^T = W G_Y^T          (T, N)
@@ -22,27 +26,29 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <new>
 
 #include "attn_internal.h"
+
+// The caller-owned GEMM context: the vendor library's handle, bound to the
+// device that was current when it was created.  The library keeps no handle
+// of its own; every projection call names the context it runs on.
+struct attn_gemm_s {
+  rocblas_handle h;
+  int device;
+};
 
 namespace attn {
 
 namespace {
 
-// One rocBLAS handle per host thread and device (a handle holds its stream,
-// so handles are not shared between threads).
-constexpr int kMaxDevices = 64;
-thread_local rocblas_handle t_handles[kMaxDevices] = {};
-
-rocblas_handle handle_for(void* stream) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  if (t_handles[dev] == nullptr && rocblas_create_handle(&t_handles[dev]) != rocblas_status_success) {
-    t_handles[dev] = nullptr;
-    return nullptr;
-  }
-  if (rocblas_set_stream(t_handles[dev], (hipStream_t)stream) != rocblas_status_success) return nullptr;
-  return t_handles[dev];
+// The context's handle on `stream`, or nullptr when the context is missing or
+// belongs to another device than the current one.
+rocblas_handle handle_for(attn_gemm ctx, void* stream) {
+  int dev = -1;
+  if (ctx == nullptr || ctx->h == nullptr || hipGetDevice(&dev) != hipSuccess || dev != ctx->device) return nullptr;
+  if (rocblas_set_stream(ctx->h, (hipStream_t)stream) != rocblas_status_success) return nullptr;
+  return ctx->h;
 }
 
 bool fits_i32(int64_t x) { return x >= 0 && x <= INT32_MAX; }
@@ -59,7 +65,7 @@ __global__ void zero_columns(E* D, int64_t ld, int64_t m, int64_t n) {
 }
 
 // Column-major D(m x n) = op(A) op(B) (+ D if accumulate), on the stream.
-attn_status gemm(void* stream, int dtype, rocblas_operation ta, rocblas_operation tb, int64_t m, int64_t n, int64_t k,
+attn_status gemm(attn_gemm ctx, void* stream, int dtype, rocblas_operation ta, rocblas_operation tb, int64_t m, int64_t n, int64_t k,
                  const void* A, int64_t lda, const void* B, int64_t ldb, void* D, int64_t ldd, bool accumulate) {
   if (m == 0 || n == 0) return ATTN_OK;
   if (k == 0) {  // an empty sum: D = 0, or D unchanged when accumulating
@@ -71,8 +77,8 @@ attn_status gemm(void* stream, int dtype, rocblas_operation ta, rocblas_operatio
       zero_columns<uint32_t><<<dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream>>>((uint32_t*)D, ldd, m, n);
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
   }
-  rocblas_handle h = handle_for(stream);
-  if (h == nullptr) return ATTN_ERR_HIP;
+  rocblas_handle h = handle_for(ctx, stream);
+  if (h == nullptr) return ATTN_ERR_INVALID_ARG;
   const rocblas_datatype t = dtype == ATTN_BF16 ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r;
   const float alpha = 1.f, beta = accumulate ? 1.f : 0.f;
   const rocblas_status st =
@@ -96,19 +102,19 @@ attn_status validate_linear(const attn_linear* L) {
   return ATTN_OK;
 }
 
-attn_status linear_fwd(const attn_linear& L, const void* X, const void* W, void* Y, void* stream) {
-  return gemm(stream, L.dtype, rocblas_operation_none, rocblas_operation_none, L.d_out, L.rows, L.d_in, W, L.ld_w, X,
+attn_status linear_fwd(attn_gemm ctx, const attn_linear& L, const void* X, const void* W, void* Y, void* stream) {
+  return gemm(ctx, stream, L.dtype, rocblas_operation_none, rocblas_operation_none, L.d_out, L.rows, L.d_in, W, L.ld_w, X,
               L.ld_x, Y, L.ld_y, false);
 }
 
-attn_status linear_bwd(const attn_linear& L, const void* X, const void* W, const void* G_Y, void* G_X, void* G_W,
-                       bool accumulate, void* stream) {
+attn_status linear_bwd(attn_gemm ctx, const attn_linear& L, const void* X, const void* W, const void* G_Y, void* G_X,
+                       void* G_W, bool accumulate, void* stream) {
   attn_status st = ATTN_OK;
   if (G_X)
-    st = gemm(stream, L.dtype, rocblas_operation_transpose, rocblas_operation_none, L.d_in, L.rows, L.d_out, W, L.ld_w,
+    st = gemm(ctx, stream, L.dtype, rocblas_operation_transpose, rocblas_operation_none, L.d_in, L.rows, L.d_out, W, L.ld_w,
               G_Y, L.ld_y, G_X, L.ld_x, accumulate);
   if (st == ATTN_OK && G_W)
-    st = gemm(stream, L.dtype, rocblas_operation_none, rocblas_operation_transpose, L.d_out, L.d_in, L.rows, G_Y,
+    st = gemm(ctx, stream, L.dtype, rocblas_operation_none, rocblas_operation_transpose, L.d_out, L.d_in, L.rows, G_Y,
               L.ld_y, X, L.ld_x, G_W, L.ld_w, accumulate);
   return st;
 }
@@ -119,19 +125,44 @@ using namespace attn;
 
 extern "C" {
 
-attn_status attn_linear_fwd(const attn_linear* L, const void* X, const void* W, void* Y, void* stream) {
+attn_status attn_gemm_create(attn_gemm* out) {
+  if (out == nullptr) return ATTN_ERR_INVALID_ARG;
+  *out = nullptr;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return ATTN_ERR_HIP;
+  attn_gemm ctx = new (std::nothrow) attn_gemm_s{nullptr, dev};
+  if (ctx == nullptr) return ATTN_ERR_HIP;
+  if (rocblas_create_handle(&ctx->h) != rocblas_status_success) {
+    delete ctx;
+    return ATTN_ERR_HIP;
+  }
+  *out = ctx;
+  return ATTN_OK;
+}
+
+attn_status attn_gemm_destroy(attn_gemm ctx) {
+  if (ctx == nullptr) return ATTN_OK;
+  const rocblas_status st = ctx->h ? rocblas_destroy_handle(ctx->h) : rocblas_status_success;
+  delete ctx;
+  return st == rocblas_status_success ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status attn_linear_fwd(const attn_linear* L, attn_gemm ctx, const void* X, const void* W, void* Y,
+                            void* stream) {
   const attn_status st = validate_linear(L);
   if (st != ATTN_OK) return st;
+  if (ctx == nullptr) return ATTN_ERR_INVALID_ARG;
   if (L->rows == 0 || L->d_out == 0) return ATTN_OK;
   if (!Y || !aligned16(Y) || (L->d_in > 0 && (!X || !W || !aligned16(X) || !aligned16(W))))
     return ATTN_ERR_INVALID_ARG;
-  return linear_fwd(*L, X, W, Y, stream);
+  return linear_fwd(ctx, *L, X, W, Y, stream);
 }
 
-attn_status attn_linear_bwd(const attn_linear* L, const void* X, const void* W, const void* G_Y, void* G_X,
-                            void* G_W, int32_t accumulate, void* stream) {
+attn_status attn_linear_bwd(const attn_linear* L, attn_gemm ctx, const void* X, const void* W, const void* G_Y,
+                            void* G_X, void* G_W, int32_t accumulate, void* stream) {
   const attn_status st = validate_linear(L);
   if (st != ATTN_OK) return st;
+  if (ctx == nullptr) return ATTN_ERR_INVALID_ARG;
   if (accumulate != 0 && accumulate != 1) return ATTN_ERR_INVALID_ARG;
   if (G_X && !aligned16(G_X)) return ATTN_ERR_INVALID_ARG;
   if (G_W && !aligned16(G_W)) return ATTN_ERR_INVALID_ARG;
@@ -141,7 +172,7 @@ attn_status attn_linear_bwd(const attn_linear* L, const void* X, const void* W, 
   if ((sum_x || sum_w) && (!G_Y || !aligned16(G_Y))) return ATTN_ERR_INVALID_ARG;
   if (sum_x && (!W || !aligned16(W))) return ATTN_ERR_INVALID_ARG;
   if (sum_w && (!X || !aligned16(X))) return ATTN_ERR_INVALID_ARG;
-  return linear_bwd(*L, X, W, G_Y, gx ? G_X : nullptr, gw ? G_W : nullptr, accumulate != 0, stream);
+  return linear_bwd(ctx, *L, X, W, G_Y, gx ? G_X : nullptr, gw ? G_W : nullptr, accumulate != 0, stream);
 }
 
 // ---------------------------------------------------------------- self-attention with its projections
@@ -189,9 +220,9 @@ attn_linear qkv_linear(const attn_problem& p, int32_t d_model) {
 
 // Checks shared by the self-attention calls: the problem over the views,
 // the product, and that Q, K and V come from the same rows.
-attn_status prepare_self(const attn_problem* prob, const attn_mask* mask, int32_t d_model, attn_problem& p,
-                         int64_t off[3], attn_linear& L) {
-  if (prob == nullptr || mask == nullptr || d_model < 1) return ATTN_ERR_INVALID_ARG;
+attn_status prepare_self(const attn_problem* prob, const attn_mask* mask, attn_gemm ctx, int32_t d_model,
+                         attn_problem& p, int64_t off[3], attn_linear& L) {
+  if (prob == nullptr || mask == nullptr || ctx == nullptr || d_model < 1) return ATTN_ERR_INVALID_ARG;
   if (prob->B < 0 || prob->H_q < 1 || prob->H_kv < 1 || prob->d_h < 0 || prob->d_v < 0) return ATTN_ERR_INVALID_ARG;
   if (!qkv_views(*prob, p, off)) return ATTN_ERR_INVALID_ARG;
   if (p.cu_seqlens_q != nullptr)
@@ -209,17 +240,17 @@ void* mat(void* base, int64_t elems, size_t es) { return (char*)base + elems * (
 
 }  // namespace
 
-attn_status attn_self_attention_fwd(const attn_problem* prob, const attn_mask* mask, int32_t d_model, const void* X,
-                                    const void* W_qkv, void* QKV, void* O, float* lse, void* stream) {
+attn_status attn_self_attention_fwd(const attn_problem* prob, const attn_mask* mask, attn_gemm ctx, int32_t d_model,
+                                    const void* X, const void* W_qkv, void* QKV, void* O, float* lse, void* stream) {
   attn_problem p;
   int64_t off[3];
   attn_linear L;
-  attn_status st = prepare_self(prob, mask, d_model, p, off, L);
+  attn_status st = prepare_self(prob, mask, ctx, d_model, p, off, L);
   if (st != ATTN_OK) return st;
   if (L.rows == 0) return ATTN_OK;
   if (!X || !W_qkv || !QKV || !aligned16(X) || !aligned16(W_qkv) || !aligned16(QKV)) return ATTN_ERR_INVALID_ARG;
   if (!O || !lse || !aligned16(O) || !aligned16(lse)) return ATTN_ERR_INVALID_ARG;
-  st = linear_fwd(L, X, W_qkv, QKV, stream);
+  st = linear_fwd(ctx, L, X, W_qkv, QKV, stream);
   if (st != ATTN_OK) return st;
   const size_t es = es_of(p.dtype);
   return attn_fwd(&p, mask, cat(QKV, off[0], es), cat(QKV, off[1], es), cat(QKV, off[2], es), O, lse, stream);
@@ -234,18 +265,18 @@ size_t attn_self_attention_bwd_workspace_size(const attn_problem* prob) {
   return attn_bwd_workspace_size(prob) + (g + 255) / 256 * 256;
 }
 
-attn_status attn_self_attention_bwd(const attn_problem* prob, const attn_mask* mask, int32_t d_model, const void* X,
-                                    const void* W_qkv, const void* QKV, const void* O, const float* lse,
+attn_status attn_self_attention_bwd(const attn_problem* prob, const attn_mask* mask, attn_gemm ctx, int32_t d_model,
+                                    const void* X, const void* W_qkv, const void* QKV, const void* O, const float* lse,
                                     const void* dO, void* G_X, void* G_W, void* workspace, size_t workspace_bytes,
                                     void* stream) {
   attn_problem p;
   int64_t off[3];
   attn_linear L;
-  attn_status st = prepare_self(prob, mask, d_model, p, off, L);
+  attn_status st = prepare_self(prob, mask, ctx, d_model, p, off, L);
   if (st != ATTN_OK) return st;
   if (L.rows == 0) {  // no rows: G_W is an empty sum
     if (G_W && !aligned16(G_W)) return ATTN_ERR_INVALID_ARG;
-    return linear_bwd(L, X, W_qkv, nullptr, nullptr, G_W, false, stream);
+    return linear_bwd(ctx, L, X, W_qkv, nullptr, nullptr, G_W, false, stream);
   }
   if (!X || !W_qkv || !QKV || !aligned16(X) || !aligned16(W_qkv) || !aligned16(QKV)) return ATTN_ERR_INVALID_ARG;
   if (!O || !lse || !dO || !aligned16(O) || !aligned16(lse) || !aligned16(dO)) return ATTN_ERR_INVALID_ARG;
@@ -260,7 +291,7 @@ attn_status attn_self_attention_bwd(const attn_problem* prob, const attn_mask* m
                 mat(G, off[0], es), mat(G, off[1], es), mat(G, off[2], es), workspace, ws_attn, stream);
   if (st != ATTN_OK) return st;
   // G_W = X^T G_QKV; G_X = G_QKV W^T sums the Q, K and V branches
-  return linear_bwd(L, X, W_qkv, G, G_X, G_W, false, stream);
+  return linear_bwd(ctx, L, X, W_qkv, G, G_X, G_W, false, stream);
 }
 
 }  // extern "C"

@@ -38,8 +38,10 @@
  * arrays read during the call (copied by value into the kernel arguments).
  * Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the null
  * stream); nothing synchronises the host.  The library allocates no device
- * memory and keeps no global mutable state: calls are re-entrant.  The
- * attention calls enqueue kernels only (no memset or copy), so a caller may
+ * memory on any call except attn_gemm_create (which makes a caller-owned
+ * context for the projections' vendor GEMM), and keeps no global mutable
+ * state: calls are re-entrant.  The attention calls enqueue kernels only (no
+ * memset or copy), so a caller may
  * capture them in a HIP graph; the host arrays are read when the call is
  * made, so every replay of a captured call uses the lengths and offsets it
  * was captured with.
@@ -120,11 +122,20 @@ typedef struct {
 
 /* Host-only argument check (no device work, no pointers needed).  Returns the
  * status attn_fwd / attn_bwd would return for these sizes and masks, apart
- * from pointer and workspace checks. */
+ * from pointer and workspace checks.  It resolves the visible sets of
+ * "Appendix A.10" secs. A.10.1 and A.10.6 (causal rule, padded keys and rows)
+ * and rejects an active row whose visible set is empty, where the softmax of
+ * eq. A.10.2 is undefined, as "Chapter 31: attention backpropagation"
+ * (eonloom handbook) sec. 3 prescribes: ATTN_ERR_EMPTY_ROW.  The rule is
+ * O(B): row 0 of a sequence sees the fewest keys, so the sequence is valid
+ * when it has no active rows, or L_k[b] >= 1 and (not causal or
+ * offset_b >= 0). */
 attn_status attn_validate(const attn_problem* prob, const attn_mask* mask);
 
 /* Bytes of device workspace attn_bwd needs for `prob` (256-byte aligned
- * base): per-row float32 D_i = rowsum(G_O o O), B * H_q * n_q floats (an
+ * base): per-row float32 D_i = rowsum(G_O o O), the row scalar c_i of
+ * "Appendix A.10" eq. A.10.7 (c_i = sum_j A_ij sum_l G_O[i,l] V[j,l] =
+ * sum_l G_O[i,l] O[i,l]), B * H_q * n_q floats (an
  * upper bound of H_q * cu_seqlens_q[B] in the packed layout), and, when the
  * problem's grids are too small for the GPU, float32 partials of divided
  * passes: the dQ pass over parts of the keys (when it has fewer than 384
@@ -137,9 +148,16 @@ attn_status attn_validate(const attn_problem* prob, const attn_mask* mask);
  * ignored. */
 size_t attn_bwd_workspace_size(const attn_problem* prob);
 
-/* Forward.  Q [B,H_q,n_q,d_h], K [B,H_kv,n_k,d_h], V [B,H_kv,n_k,d_v] in;
- * O [B,H_q,n_q,d_v] and lse [B,H_q,n_q] (float32, contiguous) out.  Device
- * pointers, 16-byte aligned; row strides multiples of 8 elements. */
+/* Forward ("Appendix A.10" eqs. A.10.1-A.10.3 on the visible sets of
+ * secs. A.10.1 and A.10.6): S = Q K^T / sqrt(d_h), the row softmax of S
+ * restricted to each row's visible set (max-shifted), O = A V, and the
+ * natural-log logsumexp lse_i of the scaled scores over the visible set.
+ * Q [B,H_q,n_q,d_h], K [B,H_kv,n_k,d_h], V [B,H_kv,n_k,d_v] in;
+ * O [B,H_q,n_q,d_v] and lse [B,H_q,n_q] (float32, contiguous) out; query
+ * head r reads KV head r / (H_q / H_kv) (sec. A.10.5).  Device pointers,
+ * 16-byte aligned; row strides multiples of 8 elements.  Inactive rows get
+ * O = 0 and lse = 0.  Errors: INVALID_ARG, EMPTY_ROW, UNSUPPORTED (see
+ * attn_validate), HIP (launch failure); outputs untouched on any error. */
 attn_status attn_fwd(const attn_problem* prob, const attn_mask* mask,
                      const void* Q, const void* K, const void* V,
                      void* O, float* lse, void* stream);
@@ -163,10 +181,17 @@ attn_status attn_fwd_splitkv(const attn_problem* prob, const attn_mask* mask,
                              void* O, float* lse, int32_t num_splits,
                              void* workspace, size_t workspace_bytes, void* stream);
 
-/* Backward.  Takes the forward's inputs, its outputs O and lse, and G_O
- * (strides of O); writes G_Q (strides of Q), G_K (strides of K) and G_V
- * (strides of V).  `workspace` is device memory of at least
- * attn_bwd_workspace_size(prob) bytes, 256-byte aligned. */
+/* Backward ("Appendix A.10" eqs. A.10.5-A.10.9, sec. A.10.5): given G_O,
+ *   G_V = A^T G_O, G_A = G_O V^T, G_S = A o (G_A - c_i) on the visible set,
+ *   G_Q = G_S K / sqrt(d_h), G_K = G_S^T Q / sqrt(d_h),
+ * with A recomputed from Q, K and the forward's lse (no n_q x n_k matrix is
+ * stored) and G_K, G_V summed over the query heads of each KV head.  Takes
+ * the forward's inputs, its outputs O and lse, and G_O (strides of O);
+ * writes G_Q (strides of Q), G_K (strides of K) and G_V (strides of V):
+ * inactive rows get G_Q = 0, keys past L_k[b] get G_K = G_V = 0.
+ * `workspace` is device memory of at least attn_bwd_workspace_size(prob)
+ * bytes, 256-byte aligned (WORKSPACE if missing or too small); other errors
+ * as attn_fwd. */
 attn_status attn_bwd(const attn_problem* prob, const attn_mask* mask,
                      const void* Q, const void* K, const void* V,
                      const void* O, const float* lse, const void* dO,
@@ -260,9 +285,25 @@ attn_status attn_bwd_rope(const attn_problem* prob, const attn_mask* mask, const
  * `accumulate`.
  *
  * Products run on the vendor GEMM (rocBLAS: bf16 or float32 operands,
- * float32 accumulation, one rounding of each result to the payload type);
- * the library keeps one rocBLAS handle per host thread and device, created on
- * first use.  Errors as elsewhere: checked before anything is enqueued. */
+ * float32 accumulation, one rounding of each result to the payload type).
+ * Its state lives in a GEMM context that the CALLER creates, passes to every
+ * projection call and destroys (attn_gemm_create / attn_gemm_destroy): the
+ * library keeps no handle of its own.  A context belongs to the device that
+ * was current when it was created (a call on another device returns
+ * ATTN_ERR_INVALID_ARG) and holds the stream of its last call, so one
+ * context must not be used by two host threads at once.  Errors as
+ * elsewhere: checked before anything is enqueued. */
+typedef struct attn_gemm_s* attn_gemm;
+
+/* Create a GEMM context on the current device (this call allocates: the
+ * vendor handle and its device workspace).  *ctx receives it, or NULL on
+ * error (ATTN_ERR_HIP).  The caller owns it until attn_gemm_destroy. */
+attn_status attn_gemm_create(attn_gemm* ctx);
+
+/* Destroy a context made by attn_gemm_create (NULL: no-op).  No call may be
+ * using it, and work enqueued with it should have completed. */
+attn_status attn_gemm_destroy(attn_gemm ctx);
+
 typedef struct {
   int32_t rows;              /* rows of X, Y, G_X and G_Y                      */
   int32_t d_in, d_out;       /* columns of X (rows of W) and of Y (of W)       */
@@ -271,14 +312,16 @@ typedef struct {
                                 those of X, W, Y); >= the row widths         */
 } attn_linear;
 
-/* Y = X W.  Device pointers, 16-byte aligned. */
-attn_status attn_linear_fwd(const attn_linear* lin, const void* X, const void* W, void* Y, void* stream);
+/* Y = X W.  Device pointers, 16-byte aligned; `ctx` from attn_gemm_create
+ * (NULL: ATTN_ERR_INVALID_ARG). */
+attn_status attn_linear_fwd(const attn_linear* lin, attn_gemm ctx, const void* X, const void* W, void* Y,
+                            void* stream);
 
 /* G_X = G_Y W^T and G_W = X^T G_Y (either output may be NULL: not formed).
  * accumulate == 1 adds into G_X / G_W instead of overwriting them (summing
  * the branches of a shared input held in separate weights). */
-attn_status attn_linear_bwd(const attn_linear* lin, const void* X, const void* W, const void* G_Y,
-                            void* G_X, void* G_W, int32_t accumulate, void* stream);
+attn_status attn_linear_bwd(const attn_linear* lin, attn_gemm ctx, const void* X, const void* W,
+                            const void* G_Y, void* G_X, void* G_W, int32_t accumulate, void* stream);
 
 /* Self-attention with its projections: [Q | K | V] = X W_qkv with X
  * [rows][d_model] and W_qkv [d_model][C], C = H_q d_h + H_kv d_h + H_kv d_v,
@@ -288,9 +331,9 @@ attn_status attn_linear_bwd(const attn_linear* lin, const void* X, const void* W
  * H_q d_h + h d_h .., of V at H_q d_h + H_kv d_h + h d_v ..), so prob's
  * q/k/v strides are ignored; O and lse as attn_fwd (o_stride from prob).
  * Requires n_k == n_q and, packed, cu_seqlens_k equal to cu_seqlens_q. */
-attn_status attn_self_attention_fwd(const attn_problem* prob, const attn_mask* mask, int32_t d_model,
-                                    const void* X, const void* W_qkv, void* QKV, void* O, float* lse,
-                                    void* stream);
+attn_status attn_self_attention_fwd(const attn_problem* prob, const attn_mask* mask, attn_gemm ctx,
+                                    int32_t d_model, const void* X, const void* W_qkv, void* QKV, void* O,
+                                    float* lse, void* stream);
 
 /* Its backward: from X, W_qkv, the forward's QKV, O and lse, and G_O, writes
  * G_X [rows][d_model] = G_Q W_Q^T + G_K W_K^T + G_V W_V^T and G_W [d_model][C]
@@ -298,8 +341,8 @@ attn_status attn_self_attention_fwd(const attn_problem* prob, const attn_mask* m
  * (attn_self_attention_bwd_workspace_size bytes, 256-byte aligned) holds D
  * and [G_Q | G_K | G_V] [rows][C]. */
 size_t attn_self_attention_bwd_workspace_size(const attn_problem* prob);
-attn_status attn_self_attention_bwd(const attn_problem* prob, const attn_mask* mask, int32_t d_model,
-                                    const void* X, const void* W_qkv, const void* QKV,
+attn_status attn_self_attention_bwd(const attn_problem* prob, const attn_mask* mask, attn_gemm ctx,
+                                    int32_t d_model, const void* X, const void* W_qkv, const void* QKV,
                                     const void* O, const float* lse, const void* dO,
                                     void* G_X, void* G_W,
                                     void* workspace, size_t workspace_bytes, void* stream);

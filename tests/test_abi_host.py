@@ -276,8 +276,10 @@ def test_linear_struct_and_errors():
     null = ctypes.c_void_p(0)
     fake = ctypes.c_void_p(0x10000)
 
-    def fwd(lin, x=fake, w=fake, y=fake):
-        return L.attn_linear_fwd(ctypes.byref(lin), x, w, y, null)
+    ctx = fake  # a context is only used once a product is enqueued
+
+    def fwd(lin, x=fake, w=fake, y=fake, c=ctx):
+        return L.attn_linear_fwd(ctypes.byref(lin), c, x, w, y, null)
 
     assert fwd(A.make_linear(10, 64, 96, A.BF16, ld_x=32)) == A.INVALID_ARG          # row stride < width
     assert fwd(A.make_linear(10, 64, 96, 7)) == A.UNSUPPORTED
@@ -285,11 +287,18 @@ def test_linear_struct_and_errors():
     assert fwd(A.make_linear(10, 64, 96, A.BF16), x=null) == A.INVALID_ARG
     assert fwd(A.make_linear(10, 64, 96, A.BF16), y=ctypes.c_void_p(0x10002)) == A.INVALID_ARG
     assert fwd(A.make_linear(0, 64, 96, A.BF16), x=null, w=null, y=null) == A.OK     # nothing to do
+    # the GEMM context is the caller's: a call without one is an argument error
+    assert fwd(A.make_linear(10, 64, 96, A.BF16), c=null) == A.INVALID_ARG
+    assert fwd(A.make_linear(0, 64, 96, A.BF16), x=null, w=null, y=null, c=null) == A.INVALID_ARG
     lin = A.make_linear(10, 64, 96, A.BF16)
-    assert L.attn_linear_bwd(ctypes.byref(lin), fake, fake, fake, fake, fake, 2, null) == A.INVALID_ARG
-    assert L.attn_linear_bwd(ctypes.byref(lin), fake, fake, null, fake, null, 0, null) == A.INVALID_ARG
+    assert L.attn_linear_bwd(ctypes.byref(lin), ctx, fake, fake, fake, fake, fake, 2, null) == A.INVALID_ARG
+    assert L.attn_linear_bwd(ctypes.byref(lin), ctx, fake, fake, null, fake, null, 0, null) == A.INVALID_ARG
+    assert L.attn_linear_bwd(ctypes.byref(lin), null, fake, fake, fake, fake, fake, 0, null) == A.INVALID_ARG
     # nothing requested: nothing to check or do
-    assert L.attn_linear_bwd(ctypes.byref(lin), null, null, null, null, null, 0, null) == A.OK
+    assert L.attn_linear_bwd(ctypes.byref(lin), ctx, null, null, null, null, null, 0, null) == A.OK
+    # destroying no context is a no-op
+    assert L.attn_gemm_destroy(null) == A.OK
+    assert L.attn_gemm_create(None) == A.INVALID_ARG
 
 
 def test_self_attention_workspace_and_errors():
@@ -300,20 +309,27 @@ def test_self_attention_workspace_and_errors():
     null = ctypes.c_void_p(0)
     fake = ctypes.c_void_p(0x10000)
     m, keep = A.make_mask(causal=True)
+    ctx = fake
     # self-attention needs n_k == n_q
     p2 = A.make_problem(2, 4, 2, 100, 120, 128, 64, A.BF16)
-    assert L.attn_self_attention_fwd(ctypes.byref(p2), ctypes.byref(m), 256, fake, fake, fake, fake, fake,
+    assert L.attn_self_attention_fwd(ctypes.byref(p2), ctypes.byref(m), ctx, 256, fake, fake, fake, fake, fake,
                                      null) == A.INVALID_ARG
-    assert L.attn_self_attention_fwd(ctypes.byref(p), ctypes.byref(m), 0, fake, fake, fake, fake, fake,
+    assert L.attn_self_attention_fwd(ctypes.byref(p), ctypes.byref(m), ctx, 0, fake, fake, fake, fake, fake,
+                                     null) == A.INVALID_ARG
+    # no GEMM context
+    assert L.attn_self_attention_fwd(ctypes.byref(p), ctypes.byref(m), null, 256, fake, fake, fake, fake, fake,
                                      null) == A.INVALID_ARG
     # packed: the same rows for queries and keys
     pk = A.make_problem(2, 4, 2, 20, 20, 128, 64, A.BF16, cu_seqlens_q=[0, 10, 30], cu_seqlens_k=[0, 20, 30])
-    assert L.attn_self_attention_fwd(ctypes.byref(pk), ctypes.byref(m), 256, fake, fake, fake, fake, fake,
+    assert L.attn_self_attention_fwd(ctypes.byref(pk), ctypes.byref(m), ctx, 256, fake, fake, fake, fake, fake,
                                      null) == A.INVALID_ARG
     # attention checks still apply
     m2, keep2 = A.make_mask(causal=True, offset=-1)
-    assert L.attn_self_attention_fwd(ctypes.byref(p), ctypes.byref(m2), 256, fake, fake, fake, fake, fake,
+    assert L.attn_self_attention_fwd(ctypes.byref(p), ctypes.byref(m2), ctx, 256, fake, fake, fake, fake, fake,
                                      null) == A.EMPTY_ROW
-    st = L.attn_self_attention_bwd(ctypes.byref(p), ctypes.byref(m), 256, fake, fake, fake, fake, fake, fake, fake,
-                                   fake, fake, ctypes.c_size_t(16), null)
+    st = L.attn_self_attention_bwd(ctypes.byref(p), ctypes.byref(m), ctx, 256, fake, fake, fake, fake, fake, fake,
+                                   fake, fake, fake, ctypes.c_size_t(16), null)
     assert st == A.WORKSPACE
+    st = L.attn_self_attention_bwd(ctypes.byref(p), ctypes.byref(m), null, 256, fake, fake, fake, fake, fake, fake,
+                                   fake, fake, fake, ctypes.c_size_t(1 << 30), null)
+    assert st == A.INVALID_ARG

@@ -71,6 +71,26 @@ def test_linear_parity(dtype):
     P.assert_within(e2, dtype, f"linear accumulate {dtype}")
 
 
+def test_caller_owned_gemm_context():
+    """The projections run on a GEMM context the caller creates and destroys:
+    a context made explicitly gives the same products as the default one,
+    and a destroyed context's replacement works on the same stream."""
+    torch = pytest.importorskip("torch")
+    P.say("[proj] caller-owned GEMM context")
+    rng = np.random.default_rng(3)
+    x = P.to_device(_draw(rng, (130, 64), W.BF16))
+    w = P.to_device(_draw(rng, (64, 96), W.BF16, 1 / 8))
+    ref = A.linear_fwd(x, w)
+    for _ in range(2):
+        ctx = A.GemmContext()
+        y = A.linear_fwd(x, w, gemm=ctx, out=P.poison(torch.empty_like(ref)))
+        gx, gw = A.linear_bwd(x, w, y, gemm=ctx)
+        torch.cuda.synchronize()
+        ctx.close()
+        assert torch.equal(y, ref)
+        assert torch.isfinite(gx.float()).all() and torch.isfinite(gw.float()).all()
+
+
 SELF_CASES = [
     # (name, dtype, B, n, d_model, H_q, H_kv, d_h, d_v, causal, lens)
     ("bf16_gqa_causal_lens", W.BF16, 2, 200, 256, 4, 2, 128, 128, True, [200, 131]),
