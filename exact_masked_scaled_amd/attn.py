@@ -34,7 +34,7 @@ F32 = 0
 BF16 = 1
 
 # every symbol the header declares
-EXPORTS = ("attn_validate", "attn_bwd_workspace_size", "attn_fwd", "attn_bwd",
+EXPORTS = ("attn_validate", "attn_bwd_workspace_size", "attn_fwd", "attn_bwd", "attn_bwd_noalloc",
            "attn_bwd_dq", "attn_bwd_dkdv", "attn_fwd_splitkv_workspace_size", "attn_fwd_splitkv",
            "attn_rope_apply", "attn_fwd_rope_workspace_size", "attn_fwd_rope",
            "attn_bwd_rope_workspace_size", "attn_bwd_rope", "attn_gemm_create", "attn_gemm_destroy",
@@ -104,6 +104,8 @@ def lib():
     L.attn_fwd.restype = ctypes.c_int
     L.attn_bwd.argtypes = [P, M, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.attn_bwd.restype = ctypes.c_int
+    L.attn_bwd_noalloc.argtypes = [P, M, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.attn_bwd_noalloc.restype = ctypes.c_int
     L.attn_bwd_dq.argtypes = [P, M, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.attn_bwd_dq.restype = ctypes.c_int
     L.attn_bwd_dkdv.argtypes = [P, M, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
@@ -404,6 +406,30 @@ def bwd(q, k, v, o, lse, do, *, causal=False, offset=0, seqlens_q=None, seqlens_
     if st != OK:
         raise AttnError(st, "attn_bwd")
     return dq, dk, dv
+
+
+def bwd_noalloc(q, k, v, o, lse, do, *, causal=False, offset=0, seqlens_q=None, seqlens_k=None,
+                dq, dk, dv, stream=None, cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None,
+                max_seqlen_k=None):
+    """attn_bwd_noalloc: the backward with the library's fixed device
+    workspace; the caller passes every output (nothing is allocated)."""
+    nd = 3 if (cu_seqlens_q is not None or cu_seqlens_k is not None) else 4
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _check4(name, t, q.dtype, nd)
+    if do.stride() != o.stride() or dq.stride() != q.stride() or dk.stride() != k.stride() \
+            or dv.stride() != v.stride():
+        raise ValueError("do, dq, dk, dv must have the strides of o, q, k, v")
+    prob = _problem_from(q, k, v, _strides(o), cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    mask, keep = make_mask(causal, offset, seqlens_q, seqlens_k)
+    st = lib().attn_bwd_noalloc(ctypes.byref(prob), ctypes.byref(mask), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream))
+    del keep
+    if st != OK:
+        raise AttnError(st, "attn_bwd_noalloc")
+    return dq, dk, dv
+
+
+NOALLOC_MAX_WORKSPACE = 64 << 20  # ATTN_BWD_NOALLOC_MAX_WORKSPACE
 
 
 class StagedBackward:

@@ -198,6 +198,23 @@ attn_status attn_bwd(const attn_problem* prob, const attn_mask* mask,
                      void* dQ, void* dK, void* dV,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): attn_bwd with its
+ * workspace in a fixed device array of the library instead of a caller
+ * buffer.  Same arguments and results as attn_bwd, without the workspace.
+ * The array holds ATTN_BWD_NOALLOC_MAX_WORKSPACE bytes on every device the
+ * library runs on (kept until the process ends); a problem whose
+ * attn_bwd_workspace_size exceeds it returns ATTN_ERR_WORKSPACE.  The array's
+ * device address is resolved on the first call made with a device current
+ * (make one call before capturing a graph); no call allocates.  All calls on
+ * one device share its array: calls that overlap on one device (other
+ * streams, or host threads without ordering) race. */
+#define ATTN_BWD_NOALLOC_MAX_WORKSPACE ((size_t)64 << 20)
+attn_status attn_bwd_noalloc(const attn_problem* prob, const attn_mask* mask,
+                             const void* Q, const void* K, const void* V,
+                             const void* O, const float* lse, const void* dO,
+                             void* dQ, void* dK, void* dV, void* stream);
+
 /* The backward in its two passes, for callers that schedule or time them
  * separately; attn_bwd is exactly attn_bwd_dq followed by attn_bwd_dkdv on
  * one stream with one workspace.  Each validates like attn_bwd.

@@ -108,6 +108,28 @@ def test_calls_reject_before_any_launch():
     assert A.status_string(A.EMPTY_ROW).startswith("an active query row")
 
 
+def test_noalloc_backward_errors_before_any_device_work():
+    """attn_bwd_noalloc checks the problem and its fixed workspace's size on
+    the host before it touches a device (so these run without a GPU)."""
+    L = lib_or_skip()
+    fake = ctypes.c_void_p(0x10000)
+    null = ctypes.c_void_p(0)
+    m, keep = A.make_mask(causal=True, offset=-1)
+    p = A.make_problem(1, 4, 2, 64, 64, 128, 128, A.BF16)
+    args = [fake] * 9 + [null]
+    assert L.attn_bwd_noalloc(ctypes.byref(p), ctypes.byref(m), *args) == A.EMPTY_ROW
+    m2, keep2 = A.make_mask()
+    bad = A.make_problem(1, 3, 2, 64, 64, 128, 128, A.BF16)  # H_q not a multiple of H_kv
+    assert L.attn_bwd_noalloc(ctypes.byref(bad), ctypes.byref(m2), *args) == A.INVALID_ARG
+    # D alone over the fixed array: B * H_q * n_q floats > 64 MiB
+    big = A.make_problem(64, 64, 8, 8192, 64, 128, 128, A.BF16)
+    assert A.workspace_size(big) > A.NOALLOC_MAX_WORKSPACE
+    assert L.attn_bwd_noalloc(ctypes.byref(big), ctypes.byref(m2), *args) == A.WORKSPACE
+    # the limit the header states
+    text = open(HEADER).read()
+    assert re.search(r"#define ATTN_BWD_NOALLOC_MAX_WORKSPACE \(\(size_t\)64 << 20\)", text)
+
+
 def _al(x):
     return (x + 255) // 256 * 256
 
