@@ -35,6 +35,8 @@
 
 namespace attn {
 
+
+
 __device__ __forceinline__ int key_limit_b(int i, int Lk, int causal, int off) {
   return causal ? min(Lk, i + off + 1) : Lk;
 }
@@ -152,17 +154,45 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(con
 
     // one key tile, 32 keys at a time: S^T, dP^T, G_S^T, then
     // G_Q^T += K^T G_S^T (only one 32-key slice of S^T / dP^T is live at once)
-    auto tile = [&](const int t, const T* Ks, const T* Vs) {
+    auto tile = [&](const int t, const T* Ks, const T* Vs) __attribute__((always_inline)) {
       const bool masked = t >= nfull;  // tile straddles the causal diagonal or the key length
 #pragma unroll
       for (int mt = 0; mt < C::BN / 32; ++mt) {
         f32x16 s, dp;
 #pragma unroll
         for (int e = 0; e < 16; ++e) { s[e] = 0.f; dp[e] = 0.f; }
+        if constexpr (sizeof(T) == 2 && DH == DV) {
+          // the S and dP chains side by side, each operand read PF k-steps
+          // ahead of its product (the order pinned through scheduling)
+          constexpr int KS = DH / 16, PF = 2;
+          op_t ka[PF + 1], va[PF + 1];
 #pragma unroll
-        for (int ks = 0; ks < DH / 16; ++ks) mma(s, kro.read(Ks, 32 * mt, ks), qreg[ks]);
+          for (int j = 0; j < PF; ++j) {
+            ka[j] = kro.read(Ks, 32 * mt, j);
+            va[j] = vro.read(Vs, 32 * mt, j);
+          }
 #pragma unroll
-        for (int ks = 0; ks < DV / 16; ++ks) mma(dp, vro.read(Vs, 32 * mt, ks), doreg[ks]);
+          for (int ks = 0; ks < KS; ++ks) {
+            if (ks + PF < KS) {
+              ka[(ks + PF) % (PF + 1)] = kro.read(Ks, 32 * mt, ks + PF);
+              va[(ks + PF) % (PF + 1)] = vro.read(Vs, 32 * mt, ks + PF);
+            }
+            mma(s, ka[ks % (PF + 1)], qreg[ks]);
+            mma(dp, va[ks % (PF + 1)], doreg[ks]);
+          }
+#pragma unroll
+          for (int j = 0; j < PF; ++j) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            if (ks + PF < KS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          }
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < DH / 16; ++ks) mma(s, kro.read(Ks, 32 * mt, ks), qreg[ks]);
+#pragma unroll
+          for (int ks = 0; ks < DV / 16; ++ks) mma(dp, vro.read(Vs, 32 * mt, ks), doreg[ks]);
+        }
         if (masked) {
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
@@ -193,24 +223,32 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(con
 
     using KL = TileLoad<T, C::BN, DH, 64 * C::NW>;
     using VL = TileLoad<T, C::BN, DV, 64 * C::NW>;
-    KL::issue(Kb, p.k_sr, t_lo * C::BN, Lk, k_lds0, tid);
-    VL::issue(Vb, p.v_sr, t_lo * C::BN, Lk, v_lds0, tid);
+    // buffer copies with 32-bit offsets from row 0 of this (sequence, KV
+    // head) when its rows fit, else one resource per row
+    const int rows_k = max(sv.nk_lim, C::BN);
+    const bool fast = fits_u32<T>(rows_k, p.k_sr, DH) && fits_u32<T>(rows_k, p.v_sr, DV);
+    const uint32_t k_srb = (uint32_t)(p.k_sr * (int64_t)sizeof(T)), v_srb = (uint32_t)(p.v_sr * (int64_t)sizeof(T));
+    const __amdgpu_buffer_rsrc_t k_rs = buf_rsrc(Kb, 0xffffffffu), v_rs = buf_rsrc(Vb, 0xffffffffu);
+    auto copy_tile = [&](int t, T* kl, T* vl) __attribute__((always_inline)) {
+      if (fast) {
+        KL::issue_buf(k_rs, k_srb, t * C::BN, Lk, kl, tid);
+        VL::issue_buf(v_rs, v_srb, t * C::BN, Lk, vl, tid);
+      } else {
+        KL::issue_rows(Kb, p.k_sr, t * C::BN, Lk, kl, tid);
+        VL::issue_rows(Vb, p.v_sr, t * C::BN, Lk, vl, tid);
+      }
+    };
+    copy_tile(t_lo, k_lds0, v_lds0);
     wait_tile_loads();
     __syncthreads();
     // two tiles per trip so each LDS buffer address is a compile-time constant
     for (int t = t_lo; t < t_hi; t += 2) {
-      if (t + 1 < t_hi) {
-        KL::issue(Kb, p.k_sr, (t + 1) * C::BN, Lk, k_lds1, tid);
-        VL::issue(Vb, p.v_sr, (t + 1) * C::BN, Lk, v_lds1, tid);
-      }
+      if (t + 1 < t_hi) copy_tile(t + 1, k_lds1, v_lds1);
       if (t < wtiles) tile(t, k_lds0, v_lds0);
       wait_tile_loads();
       __syncthreads();
       if (t + 1 >= t_hi) break;
-      if (t + 2 < t_hi) {
-        KL::issue(Kb, p.k_sr, (t + 2) * C::BN, Lk, k_lds0, tid);
-        VL::issue(Vb, p.v_sr, (t + 2) * C::BN, Lk, v_lds0, tid);
-      }
+      if (t + 2 < t_hi) copy_tile(t + 2, k_lds0, v_lds0);
       if (t + 1 < wtiles) tile(t + 1, k_lds1, v_lds1);
       wait_tile_loads();
       __syncthreads();

@@ -274,6 +274,42 @@ template <> __device__ __forceinline__ void st8<float>(float* p, const f32x8& x)
   st4<float>(p + 4, x[4], x[5], x[6], x[7]);
 }
 
+// ---------------------------------------------------------------- buffer copies
+// Tile copies through buffer loads with the LDS flag (buffer_load_dwordx4 ...
+// lds): like global_load_lds they move data from memory into LDS without
+// registers, but they are not FLAT instructions, so the compiler's wait
+// insertion does not treat an in-flight copy as a pending FLAT access that
+// forces every later LDS-read wait to lgkmcnt(0): reads of one buffer can be
+// waited for one at a time while the next tile's copy is in flight.
+//
+// A buffer resource names a byte range starting at `base`; offsets are
+// 32-bit (per-lane voffset plus a wave-uniform soffset).  Data format word as
+// for gfx9 raw buffers (32-bit elements, no swizzle, no stride).
+// The base must be the same in every lane of the wave (a resource lives in
+// scalar registers); it is read from the first lane, so the compiler never
+// wraps the load in a per-lane loop over distinct resources.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t v = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  void* u = (void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(u, (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void buf_copy16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (ATTN_LDS void*)lds, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void buf_copy4(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (ATTN_LDS void*)lds, 4, voff, soff, 0, 0);
+}
+// Can rows [0, rows) of a tensor with this row stride (elements) and width
+// (elements) be addressed with 32-bit byte offsets from row 0?
+template <typename T>
+__device__ __forceinline__ bool fits_u32(int64_t rows, int64_t row_stride, int width) {
+  if (row_stride < 0) return false;
+  const int64_t r = rows > 1 ? rows : 1;
+  return (r - 1) * row_stride * (int64_t)sizeof(T) + (int64_t)width * (int64_t)sizeof(T) <= 0xffffffffLL;
+}
+
 // ---------------------------------------------------------------- tile staging
 // Copies ROWS rows of a row-major [n][D] global tensor (unit stride in d, row
 // stride in elements) into an LDS tile laid out as Tile<T, D>, with direct
@@ -306,15 +342,10 @@ struct TileLoad {
     }
   }
 
-  // The same copy for a tile whose rows all lie below the limit, with the
-  // per-lane parts of the addresses computed once per kernel: each lane's
-  // byte offset from the tile's first row (lane_offsets) is fixed, so a copy
-  // is a wave-uniform base plus that 32-bit offset (the scalar-base form of
-  // the load) and costs no vector arithmetic.  Requires
-  // ROWS * row_stride * sizeof(T) < 2^31 (fits()).
-  static __device__ __forceinline__ bool fits(int64_t row_stride) {
-    return row_stride >= 0 && row_stride <= (int64_t)(0x7fffffff / ((int64_t)ROWS * (int64_t)sizeof(T))) - D;
-  }
+  // Per-lane byte offsets of a tile copy from the tile's first row: fixed for
+  // the whole kernel, so the copy of a tile wholly below the limit costs no
+  // vector arithmetic (issue_buf_full).  Meaningful when 64 rows of the
+  // tensor fit 32-bit offsets (fits_u32).
   static __device__ __forceinline__ void lane_offsets(int64_t row_stride, int tid, uint32_t (&off)[N]) {
     const int wave_base = __builtin_amdgcn_readfirstlane((tid >> 6) * 64), lane = tid & 63;
 #pragma unroll
@@ -325,15 +356,49 @@ struct TileLoad {
       off[i] = (uint32_t)(((int64_t)row * row_stride + chunk * L::EPC) * (int64_t)sizeof(T));
     }
   }
-  static __device__ __forceinline__ void issue_full(const T* base, int64_t row_stride, int row0,
-                                                    const uint32_t (&off)[N], T* lds, int tid) {
+  // Buffer forms (see buf_rsrc).  Whole tile below the limit: the resource
+  // starts at row 0 of the tensor, soff = byte offset of the tile's first
+  // row, off = the lane offsets of lane_offsets().
+  static __device__ __forceinline__ void issue_buf_full(__amdgpu_buffer_rsrc_t r, uint32_t soff,
+                                                        const uint32_t (&off)[N], T* lds, int tid) {
     const int wave_base = __builtin_amdgcn_readfirstlane((tid >> 6) * 64);
-    const char* tile = reinterpret_cast<const char*>(base + (int64_t)row0 * row_stride);
+#pragma unroll
+    for (int i = 0; i < N; ++i) buf_copy16(r, lds + (wave_base + NT * i) * L::EPC, off[i], soff);
+  }
+  // Any tile, rows at or beyond `limit` repeating row limit - 1; the
+  // resource starts at row 0 and every row below the limit must be
+  // addressable with 32-bit offsets (fits_u32).
+  static __device__ __forceinline__ void issue_buf(__amdgpu_buffer_rsrc_t r, uint32_t row_stride_bytes, int row0,
+                                                   int limit, T* lds, int tid) {
+    const int wave_base = __builtin_amdgcn_readfirstlane((tid >> 6) * 64), lane = tid & 63;
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int first = wave_base + NT * i;
-      __builtin_amdgcn_global_load_lds((const void*)(tile + off[i]), (ATTN_LDS void*)(lds + first * L::EPC), 16,
-                                       0, 0);
+      const int pc = first + lane;
+      const int row = pc / L::CH;
+      const int chunk = (pc % L::CH) ^ L::f(row);
+      const uint32_t g = (uint32_t)min(row0 + row, limit - 1);
+      buf_copy16(r, lds + first * L::EPC, g * row_stride_bytes + (uint32_t)(chunk * 16), 0u);
+    }
+  }
+  // General form for row strides too large for 32-bit offsets: one resource
+  // per tile row (wave-uniform), the lanes of that row enabled.
+  static __device__ __forceinline__ void issue_rows(const T* base, int64_t row_stride, int row0, int limit, T* lds,
+                                                    int tid) {
+    static_assert(64 % L::CH == 0, "a wave instruction covers whole rows");
+    const int wave_base = __builtin_amdgcn_readfirstlane((tid >> 6) * 64), lane = tid & 63;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int first = wave_base + NT * i;
+      const int row_first = first / L::CH;
+      const int my = lane / L::CH;
+      const int chunk = ((first + lane) % L::CH) ^ L::f(row_first + my);
+#pragma unroll
+      for (int rr = 0; rr < 64 / L::CH; ++rr) {
+        const int g = min(row0 + row_first + rr, limit - 1);
+        const __amdgpu_buffer_rsrc_t r = buf_rsrc(base + (int64_t)g * row_stride, (uint32_t)(L::CH * 16));
+        if (my == rr) buf_copy16(r, lds + first * L::EPC, (uint32_t)(chunk * 16), 0u);
+      }
     }
   }
 };

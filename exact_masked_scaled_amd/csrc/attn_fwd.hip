@@ -140,22 +140,34 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(const 
     kro.init(lane);
     vto.init(lane);
     const float tau_raw = 8.f / p.scale_log2;
-    // K/V tiles stream through two LDS buffers with direct global-to-LDS loads
+    // K/V tiles stream through two LDS buffers, copied from memory into LDS
+    // by buffer loads (no staging registers)
     using KL = TileLoad<T, C::BN, DH, 64 * C::NW>;
     using VL = TileLoad<T, C::BN, DV, 64 * C::NW>;
     // per-lane copy offsets, fixed for the loop (tiles wholly below L_k take
-    // the scalar-base copy; the last, partial tile clamps its rows)
+    // them with the tile's row offset as the scalar offset; the last,
+    // partial tile clamps its rows)
     uint32_t k_off[KL::N], v_off[VL::N];
-    const bool fast = KL::fits(p.k_sr) && VL::fits(p.v_sr);
+    // buffer copies with 32-bit offsets from row 0 of this (sequence, KV
+    // head) when its rows fit, else one resource per row
+    const int rows_k = max(sv.nk_lim, C::BN);
+    const bool fast = fits_u32<T>(rows_k, p.k_sr, DH) && fits_u32<T>(rows_k, p.v_sr, DV);
+    const uint32_t k_srb = (uint32_t)(p.k_sr * (int64_t)sizeof(T)), v_srb = (uint32_t)(p.v_sr * (int64_t)sizeof(T));
+    const __amdgpu_buffer_rsrc_t k_rs = buf_rsrc(Kb, 0xffffffffu), v_rs = buf_rsrc(Vb, 0xffffffffu);
     KL::lane_offsets(p.k_sr, tid, k_off);
     VL::lane_offsets(p.v_sr, tid, v_off);
     auto copy_tile = [&](int t, T* kl, T* vl) __attribute__((always_inline)) {
-      if (fast && (t + 1) * C::BN <= Lk) {
-        KL::issue_full(Kb, p.k_sr, t * C::BN, k_off, kl, tid);
-        VL::issue_full(Vb, p.v_sr, t * C::BN, v_off, vl, tid);
+      if (fast) {
+        if ((t + 1) * C::BN <= Lk) {
+          KL::issue_buf_full(k_rs, (uint32_t)(t * C::BN) * k_srb, k_off, kl, tid);
+          VL::issue_buf_full(v_rs, (uint32_t)(t * C::BN) * v_srb, v_off, vl, tid);
+        } else {
+          KL::issue_buf(k_rs, k_srb, t * C::BN, Lk, kl, tid);
+          VL::issue_buf(v_rs, v_srb, t * C::BN, Lk, vl, tid);
+        }
       } else {
-        KL::issue(Kb, p.k_sr, t * C::BN, Lk, kl, tid);
-        VL::issue(Vb, p.v_sr, t * C::BN, Lk, vl, tid);
+        KL::issue_rows(Kb, p.k_sr, t * C::BN, Lk, kl, tid);
+        VL::issue_rows(Vb, p.v_sr, t * C::BN, Lk, vl, tid);
       }
     };
     copy_tile(t_lo, k_lds0, v_lds0);
@@ -170,15 +182,40 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(const 
     wait_tile_loads();
     __syncthreads();
 
-    auto tile = [&](const int t, const T* Ks, const T* Vs) {
+    auto tile = [&](const int t, const T* Ks, const T* Vs) __attribute__((always_inline)) {
         // S^T tile: keys (rows) x this wave's 32 queries (columns), raw scores
+        // the key blocks' product chains side by side, each K operand read
+        // PF k-steps ahead of its product
         f32x16 s[C::BN / 32];
 #pragma unroll
-        for (int mt = 0; mt < C::BN / 32; ++mt) {
+        for (int mt = 0; mt < C::BN / 32; ++mt)
 #pragma unroll
           for (int e = 0; e < 16; ++e) s[mt][e] = 0.f;
+        constexpr int KS = DH / 16, PF = 2;
+        op_t ka[PF + 1][C::BN / 32];
 #pragma unroll
-          for (int ks = 0; ks < DH / 16; ++ks) mma(s[mt], kro.read(Ks, 32 * mt, ks), qreg[ks]);
+        for (int j = 0; j < PF; ++j)
+#pragma unroll
+          for (int mt = 0; mt < C::BN / 32; ++mt) ka[j][mt] = kro.read(Ks, 32 * mt, j);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          if (ks + PF < KS) {
+#pragma unroll
+            for (int mt = 0; mt < C::BN / 32; ++mt) ka[(ks + PF) % (PF + 1)][mt] = kro.read(Ks, 32 * mt, ks + PF);
+          }
+#pragma unroll
+          for (int mt = 0; mt < C::BN / 32; ++mt) mma(s[mt], ka[ks % (PF + 1)][mt], qreg[ks]);
+        }
+        // keep that order through scheduling: PF groups of reads, then per
+        // k-step the reads PF steps ahead before that step's products
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int j = 0; j < PF; ++j) __builtin_amdgcn_sched_group_barrier(0x100, C::BN / 32, 0);
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            if (ks + PF < KS) __builtin_amdgcn_sched_group_barrier(0x100, C::BN / 32, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, C::BN / 32, 0);
+          }
         }
         if (t >= nfull) {  // tile straddles the causal diagonal or the key length
 #pragma unroll
