@@ -114,6 +114,28 @@ def cpu_baseline(inp, seconds: float):
     }
 
 
+def kernel_report(wl, work, kern_ms):
+    """Per kernel of a step: time, algorithmic and executed TFLOP/s and
+    fractions of the dtype's dense MFMA peak; the dominant (longest) kernel
+    and its algorithmic rate.  Algorithmic FLOPs are credited without double
+    counting the recomputed products: the dQ pass gets the G_Q product only,
+    the dK/dV pass the recomputed scores, dP, G_V and G_K."""
+    peak = PEAK_TFLOPS[wl.dtype]
+    P, dh, dv_ = work["pairs"], wl.d_h, wl.d_v
+    alg = {"fwd": 2 * P * (dh + dv_), "bwd_dq": 2 * P * dh, "bwd_dkdv": 2 * P * (2 * dh + 2 * dv_)}
+    executed = {"fwd": 2 * P * (dh + dv_), "bwd_dq": 2 * P * (2 * dh + dv_), "bwd_dkdv": 2 * P * (2 * dh + 2 * dv_)}
+    kernels = {}
+    for n, t in kern_ms.items():
+        sec = t * 1e-3
+        kernels[n] = {"ms": round(t, 4),
+                      "algorithmic_TFLOP/s": round(alg[n] / sec / 1e12, 2),
+                      "frac_of_peak": round(alg[n] / sec / 1e12 / peak, 4),
+                      "executed_MFMA_TFLOP/s": round(executed[n] / sec / 1e12, 2),
+                      "executed_frac_of_peak": round(executed[n] / sec / 1e12 / peak, 4)}
+    dominant = max(kern_ms, key=kern_ms.get)
+    return kernels, dominant, alg[dominant] / (kern_ms[dominant] * 1e-3) / 1e12
+
+
 def measure(torch, attn, W, wl, uniform_len, steps, warmup, packed=False):
     """Time `steps` steps (forward, dQ pass, dK/dV pass) of one workload with
     its inputs resident; returns (inputs, work, ms per step, ms per kernel, device).
@@ -407,21 +429,7 @@ def main(argv=None):
     flop = work["fwd_flop"] + work["bwd_flop"]
     value = flop / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[wl.dtype]
-    P, dh, dv_ = work["pairs"], wl.d_h, wl.d_v
-    # algorithmic FLOPs credited to each kernel, without double counting the
-    # recomputed products: dq gets the G_Q product only, dkdv the recomputed
-    # scores, dP, G_V and G_K
-    alg = {"fwd": 2 * P * (dh + dv_), "bwd_dq": 2 * P * dh, "bwd_dkdv": 2 * P * (2 * dh + 2 * dv_)}
-    executed = {"fwd": 2 * P * (dh + dv_), "bwd_dq": 2 * P * (2 * dh + dv_), "bwd_dkdv": 2 * P * (2 * dh + 2 * dv_)}
-    kernels = {}
-    for n in names:
-        sec = kern_ms[n] * 1e-3
-        kernels[n] = {"ms": round(kern_ms[n], 4),
-                      "algorithmic_TFLOP/s": round(alg[n] / sec / 1e12, 2),
-                      "executed_MFMA_TFLOP/s": round(executed[n] / sec / 1e12, 2),
-                      "executed_frac_of_peak": round(executed[n] / sec / 1e12 / peak, 4)}
-    dominant = max(kern_ms, key=kern_ms.get)
-    ach = alg[dominant] / (kern_ms[dominant] * 1e-3) / 1e12
+    kernels, dominant, ach = kernel_report(wl, work, kern_ms)
     roof = {"kernel": dominant, "bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
             "frac": round(ach / peak, 4),
             "traffic": load_traffic(None) if dominant == DOMINANT else None}
@@ -464,19 +472,27 @@ def main(argv=None):
     if not args.no_other_workloads:
         # every other configuration, shorter runs (the headline target is the one above)
         others = []
-        for wid, ulen, pk in [(1, None, False), (2, None, False), (4, None, False), (5, None, False),
-                              (3, 4096, False), (3, None, True)]:
-            if wid == args.workload and ulen == args.uniform_len and not pk:
+        # float32 at a size that is not launch-bound (the float32 workload is 16 K pairs)
+        f32_large = W.custom_workload(W.F32, 4, 16, 16, 2048, 2048, 64, 64, False, 0,
+                                      "mha_fp32_b4_h16_n2048_d64")
+        for owl, ulen, pk in [(W.WORKLOADS[1], None, False), (f32_large, None, False),
+                              (W.WORKLOADS[2], None, False), (W.WORKLOADS[4], None, False),
+                              (W.WORKLOADS[5], None, False), (W.WORKLOADS[3], 4096, False),
+                              (W.WORKLOADS[3], None, True)]:
+            if owl.wid == args.workload and ulen == args.uniform_len and not pk:
                 continue
-            owl = W.WORKLOADS[wid]
             _, ow, oms, okern, _, osplit = measure(torch, attn, W, owl, ulen, 10, 3, packed=pk)
             oflop = ow["fwd_flop"] + ow["bwd_flop"]
             ov = oflop / (oms * 1e-3) / 1e12
             label = owl.name + (f"_uniform{ulen}" if ulen else "") + ("_packed" if pk else "")
+            okernels, odom, oach = kernel_report(owl, ow, okern)
             others.append({"workload": label, "dtype": owl.dtype,
                            "value": round(ov, 2), "unit": "TFLOP/s", "ms_per_step": round(oms, 4),
                            "pct_of_peak": round(100 * ov / PEAK_TFLOPS[owl.dtype], 2),
-                           "visible_pairs": ow["pairs"], "kernels_ms": {n: round(t, 4) for n, t in okern.items()},
+                           "visible_pairs": ow["pairs"], "kernels": okernels,
+                           "roofline": {"kernel": odom, "bound": "mfma", "achieved": round(oach, 2),
+                                        "peak": PEAK_TFLOPS[owl.dtype], "unit": "TFLOP/s",
+                                        "frac": round(oach / PEAK_TFLOPS[owl.dtype], 4)},
                            "forward": "split over keys" if osplit else "unsplit",
                            "steps": 10, "warmup": 3})
         result["other_workloads"] = others

@@ -36,7 +36,11 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 
-BENCH_ARGS_TRACE = ["--steps", "10", "--warmup", "2", "--no-cpu-baseline", "--no-other-workloads"]
+# the trace pass times exactly what the default benchmark line times (its
+# step and warm-up counts), so the trace reproduces the line's roofline
+TRACE_STEPS, TRACE_WARMUP = 20, 5
+BENCH_ARGS_TRACE = ["--steps", str(TRACE_STEPS), "--warmup", str(TRACE_WARMUP), "--no-cpu-baseline",
+                    "--no-other-workloads"]
 BENCH_ARGS_PMC = ["--steps", "2", "--warmup", "1", "--no-cpu-baseline", "--no-other-workloads"]
 COPY_MIB = 1024
 
@@ -108,23 +112,64 @@ def mean(v):
     return sum(v) / len(v)
 
 
+def trace_durations(raw: str) -> dict:
+    """Per kernel of a step: the durations (s) of its timed dispatches, in
+    launch order, from the kernel trace (the first TRACE_WARMUP dispatches of
+    each kernel are the benchmark's warm-up steps and are left out)."""
+    per = collections.defaultdict(list)
+    with open(os.path.join(raw, "trace", "run_kernel_trace.csv")) as f:
+        for r in csv.DictReader(f):
+            n = short_name(r["Kernel_Name"])
+            if n in KERNELS:
+                per[n].append((int(r["Start_Timestamp"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9))
+    return {n: [d for _, d in sorted(v)][TRACE_WARMUP:] for n, v in per.items()}
+
+
+def credited_flops(bench: dict) -> dict:
+    """Algorithmic FLOPs a launch of each kernel is credited with (as bench.py):
+    visible pairs only; the dQ pass gets the G_Q product alone."""
+    P = bench["config"]["visible_pairs"]
+    dh, dv = bench["config"]["d_h"], bench["config"]["d_v"]
+    return {"fwd": 2 * P * (dh + dv), "bwd_dq": 2 * P * dh, "bwd_dkdv": 2 * P * (2 * dh + 2 * dv)}
+
+
 def write_trace(raw: str, out: str, bench: dict):
-    rows = list(csv.DictReader(open(os.path.join(raw, "trace", "run_kernel_stats.csv"))))
+    sys.path.insert(0, ROOT)
+    import bench as B  # noqa: E402  (peak and dominant kernel as the benchmark reports them)
+
+    durs = trace_durations(raw)
+    alg = credited_flops(bench)
+    peak = B.PEAK_TFLOPS["bf16"]
     o = [f"# Kernel time: {WORKLOAD}\n",
          "Made by `python -m exact_masked_scaled_amd.rocprof_evidence --raw $RAW` (pass `trace`); the command, from the",
          "repository root (`REPO=$PWD`, one MI355X; `RAW` the raw-output directory):\n", "```", command("trace"), "```\n",
-         "| kernel | calls | avg (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
-    for r in rows:
-        n = short_name(r["Name"])
-        if n is None:
+         f"Per-dispatch durations from the kernel trace (`run_kernel_trace.csv`); the first {TRACE_WARMUP} dispatches of "
+         f"each kernel are the benchmark's warm-up steps and are left out, so the {TRACE_STEPS} dispatches summarised are "
+         "the steps the bench line times. Credited TFLOP/s counts visible (query, key) pairs only (forward 2(d_h + d_v), "
+         "dQ pass 2 d_h, dK/dV pass 2(2 d_h + 2 d_v) FLOP per pair) over the mean duration; fraction of the "
+         f"{peak:.0f} TFLOP/s dense bf16 peak.\n",
+         "| kernel | timed dispatches | mean (us) | median (us) | min (us) | max (us) | credited TFLOP/s | frac of peak |",
+         "|---|---|---|---|---|---|---|---|"]
+    fr = {}
+    for k, s in KERNELS.items():
+        d = durs.get(k)
+        if not d:
             continue
-        o.append(f"| `{n}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
-                 f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
+        m = mean(d)
+        srt = sorted(d)
+        med = srt[len(srt) // 2] if len(srt) % 2 else 0.5 * (srt[len(srt) // 2 - 1] + srt[len(srt) // 2])
+        fr[s] = alg[s] / m / 1e12 / peak
+        o.append(f"| `{k}` | {len(d)} | {m * 1e6:.1f} | {med * 1e6:.1f} | {srt[0] * 1e6:.1f} | {srt[-1] * 1e6:.1f} | "
+                 f"{alg[s] / m / 1e12:.1f} | {fr[s]:.4f} |")
     k = bench["kernels"]
     o.append("")
-    o.append(f"The same run's bench line (HIP events on the launch stream, 10 timed steps) reported fwd {k['fwd']['ms']:.3f} ms, "
-             f"bwd_dq {k['bwd_dq']['ms']:.3f} ms, bwd_dkdv {k['bwd_dkdv']['ms']:.3f} ms; {bench['value']:.2f} TFLOP/s for "
-             "the whole step under the profiler. The averages above include the 2 warm-up steps.")
+    dom = B.DOMINANT
+    line = bench.get("roofline", {}).get("frac")
+    o.append(f"The same run's bench line (HIP events on the launch stream, {TRACE_STEPS} timed steps) reported fwd "
+             f"{k['fwd']['ms']:.3f} ms, bwd_dq {k['bwd_dq']['ms']:.3f} ms, bwd_dkdv {k['bwd_dkdv']['ms']:.3f} ms and "
+             f"{bench['value']:.2f} TFLOP/s for the whole step under the profiler"
+             + (f"; its roofline fraction for {dom} was {line:.4f}, the trace's {fr.get(dom, float('nan')):.4f}."
+                if line is not None else "."))
     with open(os.path.join(out, "kernel_stats_causal_gqa_b8_n4096.md"), "w") as f:
         f.write("\n".join(o) + "\n")
 

@@ -99,6 +99,39 @@ def test_mfma_busy_clock_and_wave_shares(tmp_path):
     assert (busy_any, wait_issue, wait_dep, v_, l_) == ("50.0%", "20.0%", "30.0%", "25.0%", "5.0%")
 
 
+def test_trace_summary_leaves_out_warmups_and_reproduces_the_fraction(tmp_path):
+    """The kernel-trace summary drops the benchmark's warm-up dispatches and
+    credits the same FLOPs as bench.py, so its fraction for the dominant
+    kernel is the bench line's when the durations agree."""
+    raw, out = str(tmp_path / "raw"), str(tmp_path / "out")
+    os.makedirs(os.path.join(raw, "trace"))
+    os.makedirs(out)
+    rows = []
+    t = 0
+    for i in range(R.TRACE_WARMUP + R.TRACE_STEPS):
+        for name, dur in ((FWD, 500_000), (DQ, 700_000), (DKDV, 1_000_000)):
+            if i < R.TRACE_WARMUP:
+                dur *= 3  # slow warm-ups must not count
+            rows.append({"Kernel_Name": name, "Start_Timestamp": t, "End_Timestamp": t + dur})
+            t += dur + 1000
+    with open(os.path.join(raw, "trace", "run_kernel_trace.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for r in rows:
+            w.writerow(r)
+    pairs = 10**9
+    frac = 2 * pairs * 512 / 1e-3 / 1e12 / bench.PEAK_TFLOPS["bf16"]
+    line = {"value": 1.0, "kernels": {k: {"ms": 1.0} for k in ("fwd", "bwd_dq", "bwd_dkdv")},
+            "config": {"visible_pairs": pairs, "d_h": 128, "d_v": 128}, "roofline": {"frac": round(frac, 4)}}
+    R.write_trace(raw, out, line)
+    text = open(os.path.join(out, "kernel_stats_causal_gqa_b8_n4096.md")).read()
+    row = [l for l in text.splitlines() if l.startswith("| `bwd_dkdv_quad_kernel`")][0]
+    cells = [c.strip() for c in row.split("|")[2:-1]]
+    assert cells[0] == str(R.TRACE_STEPS) and cells[1] == "1000.0" and cells[2] == "1000.0"
+    assert cells[-1] == f"{frac:.4f}"
+    assert f"the trace's {frac:.4f}" in text
+
+
 def test_recorded_commands_profile_the_committed_benchmark():
     for name in R.PASSES:
         cmd = R.command(name)
