@@ -372,7 +372,16 @@ attn_status bwd_enqueue(const attn_problem& p, const attn_mask& m, const BwdPtrs
     }
     if ((passes & kDq) && has_q) {
       kp.per_group = kp.group * nqblk * pl.dq_splits;
-      if (launch_bwd_dq(kp, p.dtype, p.d_h, p.d_v, stream) != 0) return ATTN_ERR_HIP;
+      if (rc) {  // the dQ pass reads the caller's Q, turns it as it loads it and writes q~
+        KernelParams kq = kp;
+        kq.q = off(t.Q, b0 * p.q_stride[0], es);
+        kq.q_sb = p.q_stride[0]; kq.q_sh = p.q_stride[1]; kq.q_sr = p.q_stride[2];
+        kq.qt = off((void*)rc->Qt, b0 * rc->qt_s[0], es);
+        kq.qt_sb = rc->qt_s[0]; kq.qt_sh = rc->qt_s[1]; kq.qt_sr = rc->qt_s[2];
+        if (launch_bwd_dq(kq, p.dtype, p.d_h, p.d_v, stream) != 0) return ATTN_ERR_HIP;
+      } else if (launch_bwd_dq(kp, p.dtype, p.d_h, p.d_v, stream) != 0) {
+        return ATTN_ERR_HIP;
+      }
     }
     if ((passes & kDkdv) && has_k) {
       kp.per_group = nkblk * pl.hsplits;
@@ -585,10 +594,7 @@ attn_status attn_bwd_rope(const attn_problem* prob, const attn_mask* mask, const
   rc.Qt = ws + attn_bwd_workspace_size(prob);
   rc.Kt = ws + attn_bwd_workspace_size(prob) + qt.bytes;
   for (int i = 0; i < 3; ++i) { rc.qt_s[i] = qt.s[i]; rc.kt_s[i] = kt.s[i]; }
-  if (p.n_q > 0) {
-    st = rope_enqueue(p, m, rope->cos_sin, 0, 0, Q, p.q_stride, (void*)rc.Qt, qt.s, stream);
-    if (st != ATTN_OK) return st;
-  }
+  // q~ is written by the dQ pass as it turns the rows it loads; k~ here
   if (p.n_k > 0) {
     st = rope_enqueue(p, m, rope->cos_sin, 1, 0, K, p.k_stride, (void*)rc.Kt, kt.s, stream);
     if (st != ATTN_OK) return st;

@@ -53,7 +53,9 @@ struct DqCfg {
 
 // SPLIT: the workgroup covers part s of its row block's key tiles and writes
 // its float32 partial G_Q (dq_combine_kernel sums the parts in order).
-// ROPE: G_Q is turned back in the stores (rotary positions); its own instance.
+// ROPE: rotary positions: Q is turned as it is loaded (and written through
+// to the rotated copy at p.qt for the dK/dV pass) and G_Q is turned back in
+// the stores; its own instance.
 template <typename T, int DH, int DV, bool SPLIT, bool ROPE>
 __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(const KernelParams p) {
   using C = DqCfg<T, DH, DV>;
@@ -140,6 +142,20 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(con
 #pragma unroll
     for (int ks = 0; ks < DH / 16; ++ks)
       qreg[ks] = row_active ? ld8<T>(Qb + (int64_t)qi * p.q_sr + 16 * ks + 8 * kg) : zero_op<T>();
+    if constexpr (ROPE) {
+      // rotary positions: the lane's query row turned as it is loaded (the
+      // row at position qi + rope_pos[b]), and the turned row written through
+      // to the copy the dK/dV pass reads (each active row once: one
+      // workgroup per row block and head)
+      const float* cs = p.rope_cs + (int64_t)(max(min(qi, Lq - 1), 0) + p.rope_pos[b]) * DH + 8 * kg;
+#pragma unroll
+      for (int ks = 0; ks < DH / 16; ++ks) qreg[ks] = rope8<T>(qreg[ks], cs + 16 * ks, false);
+      if (row_active) {
+        T* qt = (T*)p.qt + b * p.qt_sb + sv.q_row0 * p.qt_sr + r * p.qt_sh + (int64_t)qi * p.qt_sr;
+#pragma unroll
+        for (int ks = 0; ks < DH / 16; ++ks) st8<T>(qt + 16 * ks + 8 * kg, qreg[ks]);
+      }
+    }
 
     // per-lane LDS offsets (K and V tiles share them when d_h == d_v)
     RowOffsets<T, DH> kro;

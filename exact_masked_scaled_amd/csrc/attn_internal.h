@@ -69,6 +69,10 @@ struct KernelParams {
   // sequence b sits at position i + rope_pos[b], key j at j
   const float* rope_cs;
   int32_t rope;
+  // dQ pass with rotary positions: where the rotated query rows are written
+  // (the dK/dV pass's copy of q~), with its element strides
+  void* qt;
+  int64_t qt_sb, qt_sh, qt_sr;
   int32_t lens_q[kMaxBatchChunk];
   int32_t lens_k[kMaxBatchChunk];
   int32_t offs[kMaxBatchChunk];    // causal offsets, clamped to [0, n_k]

@@ -276,11 +276,13 @@ attn_status attn_fwd_rope(const attn_problem* prob, const attn_mask* mask, const
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* Backward with rotary positions: from the unrotated Q and K, the forward's O
- * and lse, and G_O, writes G_Q = R^T G_Q~, G_K = R^T G_K~ and G_V.  q~ and k~
- * are rotated into the workspace (attn_bwd_rope_workspace_size(prob) bytes,
- * 256-byte aligned: D, then q~, then k~, in contiguous layouts), and the
- * turn back of G_Q~ and G_K~ happens in the two passes' stores (no rounding
- * of the rotated gradients in between).  Other arguments as attn_bwd. */
+ * and lse, and G_O, writes G_Q = R^T G_Q~, G_K = R^T G_K~ and G_V.  The
+ * workspace (attn_bwd_rope_workspace_size(prob) bytes, 256-byte aligned)
+ * holds D, then q~, then k~, in contiguous layouts: k~ is rotated into it by
+ * a streaming pass, q~ is written by the dQ pass, which turns each query row
+ * as it loads it; the dK/dV pass reads both.  The turn back of G_Q~ and G_K~
+ * happens in the two passes' stores (no rounding of the rotated gradients in
+ * between).  Other arguments as attn_bwd. */
 size_t attn_bwd_rope_workspace_size(const attn_problem* prob);
 attn_status attn_bwd_rope(const attn_problem* prob, const attn_mask* mask, const attn_rope* rope,
                           const void* Q, const void* K, const void* V,
