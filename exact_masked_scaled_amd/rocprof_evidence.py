@@ -275,6 +275,8 @@ def main(argv=None) -> int:
                     help="summaries to (re)make; default all")
     ap.add_argument("--no-run", action="store_true", help="only summarise the raw output of earlier passes")
     a = ap.parse_args(argv)
+    a.raw = os.path.abspath(a.raw)  # the passes run from /tmp
+    a.out = os.path.abspath(a.out)
     want = set(a.only or ["trace", "traffic", "mfma"])
     need = {"trace": ["trace"], "traffic": ["fetch", "write"], "mfma": ["mfma", "wait"]}
     os.makedirs(a.raw, exist_ok=True)
