@@ -635,8 +635,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const KernelParams p) 
 //   XD (waves 2, 3): holds V; dP = G_O V^T, then G_S = P o (dP - D), handed on;
 //   YV (waves 4, 5): G_V += P^T G_O;     YK (waves 6, 7): G_K += G_S^T Q.
 // In iteration s, XS forms S of step s and the exponentials of step s - 1; XD
-// forms dP of step s - 1 and G_S of step s - 2; YV accumulates step s - 2 and
-// YK step s - 3.  Products and element-wise work of one wave are interleaved
+// forms dP of step s - 1 and G_S of step s - 2; YV and YK accumulate step
+// s - 3.  Products and element-wise work of one wave are interleaved
 // so the exponentials run while the matrix core works; a SIMD holds one X and
 // one Y wave.  Q / G_O tiles (and the step's lse and D rows) come through an
 // NS-stage ring of direct global-to-LDS copies, issued by the Y waves two
@@ -684,12 +684,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
   __shared__ __attribute__((aligned(16))) char st3[SB];
   __shared__ __attribute__((aligned(16))) char st4[SB];
   __shared__ __attribute__((aligned(16))) char st5[SB];
-  // P (from XS) and G_S (from XD), two slots each: per half, per 32-key block
-  // and per 16-row k-step one operand per lane, at ((h * 2 + kb) * 2 + ks) * 64 + lane
-  __shared__ op_t xp0[2 * 2 * 2 * 64];
-  __shared__ op_t xp1[2 * 2 * 2 * 64];
-  __shared__ op_t xd0[2 * 2 * 2 * 64];
-  __shared__ op_t xd1[2 * 2 * 2 * 64];
+  // P (from XS, three slots: step t in slot t % 3) and G_S (from XD, two
+  // slots: step t in slot 3 + t % 2), in one array: per half, per 32-key
+  // block and per 16-row k-step one operand per lane, at
+  // slot * XSLOT + ((h * 2 + kb) * 2 + ks) * 64 + lane.  The Y waves select
+  // their operands and tiles by offsets within one array (never by choosing
+  // between arrays), so every LDS read keeps the identity of the object it
+  // reads and waits only for copies into that object.
+  constexpr int XSLOT = 2 * 2 * 2 * 64;
+  __shared__ op_t xch[5 * XSLOT];
   auto stage = [&](auto K) __attribute__((always_inline)) -> char* {
     constexpr int k = decltype(K)::value % NS;
     if constexpr (k == 0) return st0; else if constexpr (k == 1) return st1;
@@ -966,158 +969,142 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
         __builtin_amdgcn_sched_barrier(0);
       }
     };
-    // ---- YV / YK: accumulate over one step (each transposed read feeds both key blocks)
-    auto y_iter = [&](const T* tile, const op_t* xb) __attribute__((always_inline)) {
-      const op_t* in = xb + (h * 2) * 2 * 64;
+    // ---- YV / YK: accumulate step s - 3 (each transposed read feeds both key
+    // blocks).  Both roles read that step's ring stage (G_O for YV, Q for YK)
+    // and its exchange slot (P for YV, G_S for YK), each chosen by an offset
+    // within one array.
+    auto y_iter = [&](auto U) __attribute__((always_inline)) {
+      constexpr int u = decltype(U)::value;
+      const char* stg = stage(IC<u + NS - 3>());
+      const T* tile = reinterpret_cast<const T*>(stg + (is_s ? QB : 0));
+      const op_t* in = xch + (is_s ? u % 3 : 3 + ((u + 1) & 1)) * XSLOT + (h * 2) * 2 * 64;
       op_t a[2][2];
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
         for (int st = 0; st < 2; ++st) a[kb2][st] = in[(kb2 * 2 + st) * 64 + lane];
-      if (is_s) {  // YV: G_V += P^T G_O
-        constexpr int NT = DV / 32;
+      auto products = [&](auto DC) __attribute__((always_inline)) {
+        constexpr int D = decltype(DC)::value, NT = D / 32;
 #pragma unroll
         for (int st = 0; st < 2; ++st)
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) {
-            const op_t bt = TrOffsets<T, DV>::read_at(tile, 16 * st, ofs[nt], ofs[NOFS / 2 + nt]);
+            const op_t bt = TrOffsets<T, D>::read_at(tile, 16 * st, ofs[nt], ofs[NOFS / 2 + nt]);
             mma(R[nt], a[0][st], bt);
             mma(R[NT + nt], a[1][st], bt);
           }
-      } else {     // YK: G_K += G_S^T Q
-        constexpr int NT = DH / 32;
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            const op_t bt = TrOffsets<T, DH>::read_at(tile, 16 * st, ofs[nt], ofs[NOFS / 2 + nt]);
-            mma(R[nt], a[0][st], bt);
-            mma(R[NT + nt], a[1][st], bt);
-          }
-      }
+      };
+      // YV: G_V += P^T G_O; YK: G_K += G_S^T Q.  With d_h = d_v one path, so
+      // the two roles' accumulators share one register assignment.
+      if constexpr (DH == DV) products(IC<DV>());
+      else if (is_s) products(IC<DV>());
+      else products(IC<DH>());
     };
 
     int i_rr = rr_lo, i_qb = qb_first;   // next step to copy
     int xs_qb = qb_first;            // query block of the step XS exponentiates next
-    auto next = [&](int& rr, int& qb) __attribute__((always_inline)) {
-      if (++qb == qb_end) { qb = qb_first; ++rr; }
+    // after a copy: move on to the next step while one is left (past the last
+    // step the copies repeat it, into stages no later step reads)
+    auto next = [&](int s_copied, int& rr, int& qb) __attribute__((always_inline)) {
+      if (s_copied + 1 < nsteps) {
+        if (++qb == qb_end) { qb = qb_first; ++rr; }
+      }
     };
     using F = IC<0>;
     using TR = IC<1>;
-    auto body = [&](int s, auto U) __attribute__((always_inline)) -> bool {
-      constexpr int u = decltype(U)::value;
-      if (s > nsteps + 2) return false;
-      const int ahead = min(PD - 1, nsteps - 1 - s);
-      if (is_x || ahead <= 0) stage_barrier<0>();
-      else stage_barrier<C::CPS>();
-      if (!is_x && s + PD < nsteps) { issue(i_rr, i_qb, IC<u + PD>()); next(i_rr, i_qb); }
+    // One step of one role (XS = 0, XD = 1, Y = 2).  Every role runs its own
+    // loop over the same steps with one barrier each, so a role's loop holds
+    // only its own work: the Y loop copies in every step (the same number of
+    // copies on every path), which lets the compiler's wait for an LDS read
+    // count only the copies into that read's stage instead of every copy in
+    // flight, and the X loops hold no copies at all.
+    //   RAMP: the step may lie in the ramp-up (0 .. 2) or ramp-down (the last
+    //   steps), where roles skip parts; the steady range 3 .. nsteps - 1 has
+    //   no such branches, so its loop keeps every register block in place.
+    auto step = [&](int s, auto U, auto ROLE, auto RAMP) __attribute__((always_inline)) {
+      constexpr int u = decltype(U)::value, role = decltype(ROLE)::value;
+      constexpr bool ramp = decltype(RAMP)::value;
       constexpr int jn = u & 1;  // parity of step s (NS even)
-      if (is_x && is_s) {
-        // XS: S(s) and P(s - 1) -> xp[(s - 1) & 1]
-        op_t* xw = jn ? xp0 : xp1;
+      if constexpr (role == 2) {
+        // copies of step s + PD are in flight: wait for all but them
+        stage_barrier<C::CPS>();
+        issue(i_rr, i_qb, IC<u + PD>());
+        next(s + PD, i_rr, i_qb);
+        // YV / YK: step s - 3 (P or G_S of that step)
+        if (!ramp || s >= 3) y_iter(IC<u>());
+      } else if constexpr (role == 0) {
+        stage_barrier<0>();
+        // XS: S(s) and P(s - 1) -> P slot (s - 1) % 3
+        op_t* xw = xch + ((u + 2) % 3) * XSLOT;
         const float* rows = r_st(IC<u + NS - 1>());
-        const bool mf = s < nsteps, ex = s >= 1 && s <= nsteps;
         const int q0 = xs_qb * C::BM;
+        const bool mf = !ramp || s < nsteps, ex = !ramp || (s >= 1 && s <= nsteps);
         if (mf && ex) {
           if (full_tile(q0)) xs_iter(TR(), TR(), TR(), IC<jn>(), q_st(U), q0, rows, xw);
           else xs_iter(TR(), TR(), F(), IC<jn>(), q_st(U), q0, rows, xw);
-        } else if (ex) {
-          if (full_tile(q0)) xs_iter(F(), TR(), TR(), IC<jn>(), q_st(U), q0, rows, xw);
-          else xs_iter(F(), TR(), F(), IC<jn>(), q_st(U), q0, rows, xw);
-        } else if (mf) {
-          xs_iter(TR(), F(), TR(), IC<jn>(), q_st(U), q0, rows, xw);
+        } else if constexpr (ramp) {
+          if (ex) {
+            if (full_tile(q0)) xs_iter(F(), TR(), TR(), IC<jn>(), q_st(U), q0, rows, xw);
+            else xs_iter(F(), TR(), F(), IC<jn>(), q_st(U), q0, rows, xw);
+          } else if (mf) {
+            xs_iter(TR(), F(), TR(), IC<jn>(), q_st(U), q0, rows, xw);
+          }
         }
         if (ex) { if (++xs_qb == qb_end) xs_qb = qb_first; }
-      } else if (is_x) {
-        // XD: dP(s - 1) into parity (s - 1) & 1, G_S(s - 2) -> xd[(s - 2) & 1]
+      } else {
+        stage_barrier<0>();
+        // XD: dP(s - 1) into parity (s - 1) & 1, G_S(s - 2) -> G_S slot 3 + (s - 2) % 2
         constexpr int jd = (u + 1) & 1;
-        const bool mf = s >= 1 && s <= nsteps, ex = s >= 2 && s <= nsteps + 1;
         const T* Os = o_st(IC<u + NS - 1>());
         const float* rows = r_st(IC<u + NS - 2>());
-        const op_t* pin = jn ? xp1 : xp0;    // P(s - 2)
-        op_t* xw = jn ? xd1 : xd0;           // slot (s - 2) & 1
+        const op_t* pin = xch + ((u + 1) % 3) * XSLOT;  // P(s - 2)
+        op_t* xw = xch + (3 + (u & 1)) * XSLOT;         // G_S(s - 2)
+        const bool mf = !ramp || (s >= 1 && s <= nsteps), ex = !ramp || (s >= 2 && s <= nsteps + 1);
         if (mf && ex) xd_iter(TR(), TR(), IC<jd>(), Os, rows, pin, xw);
-        else if (ex) xd_iter(F(), TR(), IC<jd>(), Os, rows, pin, xw);
-        else if (mf) xd_iter(TR(), F(), IC<jd>(), Os, rows, pin, xw);
-      } else if (is_s) {
-        // YV: step s - 2 with P from xp[(s - 2) & 1]
-        if (s >= 2 && s <= nsteps + 1) y_iter(o_st(IC<u + NS - 2>()), jn ? xp1 : xp0);
-      } else {
-        // YK: step s - 3 with G_S from xd[(s - 3) & 1]
-        if (s >= 3) y_iter(q_st(IC<u + NS - 3>()), jn ? xd0 : xd1);
-      }
-      return true;
-    };
-    if (!is_x) {
-      issue(i_rr, i_qb, IC<0>());
-      next(i_rr, i_qb);
-      if (1 < nsteps) { issue(i_rr, i_qb, IC<1>()); next(i_rr, i_qb); }
-    }
-    // Steps 3 .. nsteps - 1 do the whole of every role's work; only the
-    // ramp-up (0 .. 2) and ramp-down (the last steps) skip parts.  The ramps
-    // run through `body`, the steady range through `steady`, which has no
-    // ramp branches, so the steady loop keeps every role's register blocks
-    // in place (ramp branches inside the loop made the register allocator
-    // copy whole S / dP blocks at their joins every step).  Every wave runs
-    // the same sequence of steps, one barrier each.
-    auto steady = [&](int s, auto U) __attribute__((always_inline)) {
-      constexpr int u = decltype(U)::value;
-      const int ahead = min(PD - 1, nsteps - 1 - s);
-      if (is_x || ahead <= 0) stage_barrier<0>();
-      else stage_barrier<C::CPS>();
-      if (!is_x && s + PD < nsteps) { issue(i_rr, i_qb, IC<u + PD>()); next(i_rr, i_qb); }
-      constexpr int jn = u & 1;
-      if (is_x && is_s) {
-        op_t* xw = jn ? xp0 : xp1;
-        const float* rows = r_st(IC<u + NS - 1>());
-        const int q0 = xs_qb * C::BM;
-        if (full_tile(q0)) xs_iter(TR(), TR(), TR(), IC<jn>(), q_st(U), q0, rows, xw);
-        else xs_iter(TR(), TR(), F(), IC<jn>(), q_st(U), q0, rows, xw);
-        if (++xs_qb == qb_end) xs_qb = qb_first;
-      } else if (is_x) {
-        constexpr int jd = (u + 1) & 1;
-        xd_iter(TR(), TR(), IC<jd>(), o_st(IC<u + NS - 1>()), r_st(IC<u + NS - 2>()), jn ? xp1 : xp0,
-                jn ? xd1 : xd0);
-      } else if constexpr (DH == DV) {
-        // YV and YK run the same products on different tiles: one path, so
-        // their accumulators share one register assignment
-        const T* tile = is_s ? o_st(IC<u + NS - 2>()) : q_st(IC<u + NS - 3>());
-        const op_t* in = (is_s ? (jn ? xp1 : xp0) : (jn ? xd0 : xd1)) + (h * 2) * 2 * 64;
-        op_t a[2][2];
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-          for (int st = 0; st < 2; ++st) a[kb2][st] = in[(kb2 * 2 + st) * 64 + lane];
-        constexpr int NT = DV / 32;
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            const op_t bt = TrOffsets<T, DV>::read_at(tile, 16 * st, ofs[nt], ofs[NOFS / 2 + nt]);
-            mma(R[nt], a[0][st], bt);
-            mma(R[NT + nt], a[1][st], bt);
-          }
-      } else if (is_s) {
-        y_iter(o_st(IC<u + NS - 2>()), jn ? xp1 : xp0);
-      } else {
-        y_iter(q_st(IC<u + NS - 3>()), jn ? xd0 : xd1);
+        else if constexpr (ramp) {
+          if (ex) xd_iter(F(), TR(), IC<jd>(), Os, rows, pin, xw);
+          else if (mf) xd_iter(TR(), F(), IC<jd>(), Os, rows, pin, xw);
+        }
       }
     };
     static_assert(NS == 6, "the steady loop below is written for six ring stages");
-    if (body(0, IC<0>()) && body(1, IC<1>()) && body(2, IC<2>())) {
-      int s = 3;
-      for (; s + NS <= nsteps; s += NS) {
-        steady(s, IC<3>());
-        steady(s + 1, IC<4>());
-        steady(s + 2, IC<5>());
-        steady(s + 3, IC<0>());
-        steady(s + 4, IC<1>());
-        steady(s + 5, IC<2>());
+    auto run = [&](auto ROLE) __attribute__((always_inline)) {
+      // steps 0 .. nsteps + 2: the ramp-up, the steady loop, the ramp-down
+      auto ramp_step = [&](int s, auto U) __attribute__((always_inline)) -> bool {
+        if (s > nsteps + 2) return false;
+        step(s, U, ROLE, TR());
+        return true;
+      };
+      if (ramp_step(0, IC<0>()) && ramp_step(1, IC<1>()) && ramp_step(2, IC<2>())) {
+        int s = 3;
+        for (; s + NS <= nsteps; s += NS) {
+          step(s, IC<3>(), ROLE, F());
+          step(s + 1, IC<4>(), ROLE, F());
+          step(s + 2, IC<5>(), ROLE, F());
+          step(s + 3, IC<0>(), ROLE, F());
+          step(s + 4, IC<1>(), ROLE, F());
+          step(s + 5, IC<2>(), ROLE, F());
+        }
+        // the remaining steps s .. nsteps + 2 (at most 8; s % NS == 3)
+        if (ramp_step(s, IC<3>()) && ramp_step(s + 1, IC<4>()) && ramp_step(s + 2, IC<5>()) &&
+            ramp_step(s + 3, IC<0>()) && ramp_step(s + 4, IC<1>()) && ramp_step(s + 5, IC<2>()) &&
+            ramp_step(s + 6, IC<3>()))
+          ramp_step(s + 7, IC<4>());
       }
-      // the remaining steps s .. nsteps + 2 (at most 8; s % NS == 3)
-      if (body(s, IC<3>()) && body(s + 1, IC<4>()) && body(s + 2, IC<5>()) && body(s + 3, IC<0>()) &&
-          body(s + 4, IC<1>()) && body(s + 5, IC<2>()) && body(s + 6, IC<3>()))
-        body(s + 7, IC<4>());
+    };
+    if (is_x && is_s) {
+      run(IC<0>());
+    } else if (is_x) {
+      run(IC<1>());
+    } else {
+      // the first two steps' copies; then each step copies the step PD ahead
+      issue(i_rr, i_qb, IC<0>());
+      next(0, i_rr, i_qb);
+      issue(i_rr, i_qb, IC<1>());
+      next(1, i_rr, i_qb);
+      run(IC<2>());
+      // no copy may still be writing LDS when the workgroup ends
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
   }
 
