@@ -778,45 +778,63 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
     const int n_q = Lq, group = p.group;
     const float* const rows_lane = (lane < 32 ? p.lse : p.delta) + b * p.lse_sb + sv.q_row0 + (lane & 31);
     const int yw = w & 3;  // copy slot of a Y wave
+    // per-lane source offset (elements) of each copy instruction within a
+    // 32-row block
     int64_t c_off[C::JPW];
-    int c_row[C::JPW];
 #pragma unroll
     for (int i = 0; i < C::JPW; ++i) {
       const int job = yw + 4 * i;
-      if (job < C::QCH / 64) {
+      if (i < C::QCH / 256) {
         using L = Tile<T, DH>;
         const int pc = job * 64 + lane, row = pc / L::CH;
-        c_row[i] = row;
         c_off[i] = row * q_sr + ((pc % L::CH) ^ L::f(row)) * L::EPC;
       } else {
         using L = Tile<T, DV>;
         const int pc = (job - C::QCH / 64) * 64 + lane, row = pc / L::CH;
-        c_row[i] = row;
         c_off[i] = row * o_sr + ((pc % L::CH) ^ L::f(row)) * L::EPC;
       }
     }
+    // Exactly CPS copies on every path.
+    static_assert(C::QCH % 256 == 0 && C::OCH % 256 == 0, "each Y wave copies whole Q and G_O wave rows");
     auto issue = [&](int rr, int qb, auto ST) __attribute__((always_inline)) {
       const int r = g * group + rr;
       const int q0 = qb * C::BM;
-      const bool whole = q0 + C::BM <= n_q;
       const T* qt = q_base + r * q_sh + (int64_t)q0 * q_sr;
       const T* ot = o_base + r * o_sh + (int64_t)q0 * o_sr;
+      // rows past the last active one repeat it (finite data only): a lane
+      // whose row lies past it reads that row's chunk instead
+      const int last = n_q - 1 - q0;  // last active row of the block (>= 31: all rows active)
+      const int64_t last_q = (int64_t)last * q_sr, last_o = (int64_t)last * o_sr;
+      int64_t off[C::JPW];
 #pragma unroll
       for (int i = 0; i < C::JPW; ++i) {
         const int job = yw + 4 * i;
+        if (i < C::QCH / 256) {
+          using L = Tile<T, DH>;
+          const int pc = job * 64 + lane, row = pc / L::CH;
+          off[i] = row <= last ? c_off[i] : last_q + ((pc % L::CH) ^ L::f(row)) * L::EPC;
+        } else {
+          using L = Tile<T, DV>;
+          const int pc = (job - C::QCH / 64) * 64 + lane, row = pc / L::CH;
+          off[i] = row <= last ? c_off[i] : last_o + ((pc % L::CH) ^ L::f(row)) * L::EPC;
+        }
+      }
+      const int qq = q0 + min(lane & 31, last) - (lane & 31);
+#pragma unroll
+      for (int i = 0; i < C::JPW; ++i) {
+        const int job = yw + 4 * i;  // i < QCH / 256: a Q chunk (yw < 4)
         const T* src;
         T* dst;
-        if (job < C::QCH / 64) {
-          src = qt + (whole ? c_off[i] : c_off[i] + (int64_t)(min(q0 + c_row[i], n_q - 1) - q0 - c_row[i]) * q_sr);
+        if (i < C::QCH / 256) {
+          src = qt + off[i];
           dst = q_st(ST) + job * 64 * Tile<T, DH>::EPC;
         } else {
-          src = ot + (whole ? c_off[i] : c_off[i] + (int64_t)(min(q0 + c_row[i], n_q - 1) - q0 - c_row[i]) * o_sr);
+          src = ot + off[i];
           dst = o_st(ST) + (job - C::QCH / 64) * 64 * Tile<T, DV>::EPC;
         }
         __builtin_amdgcn_global_load_lds((const void*)src, (ATTN_LDS void*)dst, 16, 0, 0);
       }
       // every Y wave copies the same lse / D rows (keeps the per-wave count equal)
-      const int qq = whole ? q0 : min(q0 + (lane & 31), n_q - 1) - (lane & 31);
       load_lane_floats(rows_lane + (int64_t)r * r_sh + qq, r_st(ST));
     };
 
@@ -1000,6 +1018,39 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
       else if (is_s) products(IC<DV>());
       else products(IC<DH>());
     };
+    // With d_h = d_v the steady loop reads each step's transposed tile
+    // operands one step early (its stage has been complete since two barriers
+    // before): after the barrier only the exchange-slot reads stand between
+    // a Y wave and its products.
+    op_t ybt[2][DV / 32];
+    auto y_load = [&](auto U) __attribute__((always_inline)) {  // operands of step u - 3
+      constexpr int u = decltype(U)::value;
+      const char* stg = stage(IC<u + NS - 3>());
+      const T* tile = reinterpret_cast<const T*>(stg + (is_s ? QB : 0));
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int nt = 0; nt < DV / 32; ++nt)
+          ybt[st][nt] = TrOffsets<T, DV>::read_at(tile, 16 * st, ofs[nt], ofs[NOFS / 2 + nt]);
+    };
+    auto y_iter_pre = [&](auto U) __attribute__((always_inline)) {
+      constexpr int u = decltype(U)::value;
+      const op_t* in = xch + (is_s ? u % 3 : 3 + ((u + 1) & 1)) * XSLOT + (h * 2) * 2 * 64;
+      op_t a[2][2];
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) a[kb2][st] = in[(kb2 * 2 + st) * 64 + lane];
+      constexpr int NT = DV / 32;
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          mma(R[nt], a[0][st], ybt[st][nt]);
+          mma(R[NT + nt], a[1][st], ybt[st][nt]);
+        }
+      y_load(IC<u + 1>());
+    };
 
     int i_rr = rr_lo, i_qb = qb_first;   // next step to copy
     int xs_qb = qb_first;            // query block of the step XS exponentiates next
@@ -1031,7 +1082,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
         issue(i_rr, i_qb, IC<u + PD>());
         next(s + PD, i_rr, i_qb);
         // YV / YK: step s - 3 (P or G_S of that step)
-        if (!ramp || s >= 3) y_iter(IC<u>());
+        if constexpr (!ramp && DH == DV) y_iter_pre(U);
+        else if (!ramp || s >= 3) y_iter(IC<u>());
       } else if constexpr (role == 0) {
         stage_barrier<0>();
         // XS: S(s) and P(s - 1) -> P slot (s - 1) % 3
@@ -1077,6 +1129,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
       };
       if (ramp_step(0, IC<0>()) && ramp_step(1, IC<1>()) && ramp_step(2, IC<2>())) {
         int s = 3;
+        if constexpr (decltype(ROLE)::value == 2 && DH == DV) {
+          if (s + NS <= nsteps) y_load(IC<3>());
+        }
         for (; s + NS <= nsteps; s += NS) {
           step(s, IC<3>(), ROLE, F());
           step(s + 1, IC<4>(), ROLE, F());

@@ -410,14 +410,17 @@ __device__ __forceinline__ void wait_tile_loads() { __builtin_amdgcn_s_waitcnt(0
 // wave's vector-memory operations (issued in order) are still outstanding and
 // all of its LDS accesses are complete, then synchronises the workgroup.
 // Unlike __syncthreads(), whose fence drains every pending global-to-LDS copy,
-// this lets the copies of later stages stay in flight.  The memory clobbers
-// keep the compiler from moving memory accesses across it.
+// this lets the copies of later stages stay in flight.  The wait is the
+// compiler's own s_waitcnt (so its count of copies in flight, which decides
+// the waits it inserts before later LDS reads, knows which copies have
+// landed); the barrier's memory clobber keeps memory accesses from moving
+// across it.
 template <int N>
 __device__ __forceinline__ void stage_barrier() {
   static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
-  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else if constexpr (N < 10) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
-  else asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+  // s_waitcnt fields: vmcnt[3:0] and [15:14], expcnt[6:4] (7: no wait), lgkmcnt[11:8] (0)
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (7 << 4));
+  asm volatile("s_barrier" ::: "memory");
 }
 
 // 64 lanes copy one float each into 256 consecutive LDS bytes (lane i ->
