@@ -168,15 +168,21 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(con
       if constexpr (DH == DV) return kro; else return vro_own;
     }();
 
-    // one key tile, 32 keys at a time: S^T, dP^T, G_S^T, then
+    // The dP^T chain starts from -D_i (one query per lane: every element of
+    // the lane's block has the same D_i), so it ends at dP - D_i.
+    f32x16 negd;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) negd[e] = -Di;
+
+    // one key tile, 32 keys at a time: S^T, dP^T - D, G_S^T, then
     // G_Q^T += K^T G_S^T (only one 32-key slice of S^T / dP^T is live at once)
     auto tile = [&](const int t, const T* Ks, const T* Vs) __attribute__((always_inline)) {
       const bool masked = t >= nfull;  // tile straddles the causal diagonal or the key length
 #pragma unroll
       for (int mt = 0; mt < C::BN / 32; ++mt) {
-        f32x16 s, dp;
+        f32x16 s, dp = negd;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) { s[e] = 0.f; dp[e] = 0.f; }
+        for (int e = 0; e < 16; ++e) s[e] = 0.f;
         if constexpr (sizeof(T) == 2 && DH == DV) {
           // the S and dP chains side by side, each operand read PF k-steps
           // ahead of its product (the order pinned through scheduling)
@@ -215,13 +221,13 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(con
             const int key = t * C::BN + 32 * mt + 8 * (e >> 2) + 4 * kg + (e & 3);
             float pv = __builtin_amdgcn_exp2f(fmaf(s[e], p.scale_log2, -lse2));
             pv = key < kmax_lane ? pv : 0.f;
-            dp[e] = pv * (dp[e] - Di);
+            dp[e] = pv * dp[e];
           }
         } else {
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const float pv = __builtin_amdgcn_exp2f(fmaf(s[e], p.scale_log2, -lse2));
-            dp[e] = pv * (dp[e] - Di);
+            dp[e] = pv * dp[e];
           }
         }
         // G_Q^T += K^T G_S^T: A = K^T (lane = d) by transposed read, B = G_S^T
@@ -245,10 +251,21 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(con
     const bool fast = fits_u32<T>(rows_k, p.k_sr, DH) && fits_u32<T>(rows_k, p.v_sr, DV);
     const uint32_t k_srb = (uint32_t)(p.k_sr * (int64_t)sizeof(T)), v_srb = (uint32_t)(p.v_sr * (int64_t)sizeof(T));
     const __amdgpu_buffer_rsrc_t k_rs = buf_rsrc(Kb, 0xffffffffu), v_rs = buf_rsrc(Vb, 0xffffffffu);
+    // per-lane copy offsets, fixed for the loop (tiles wholly below L_k take
+    // them with the tile's row offset as the scalar offset; the last,
+    // partial tile clamps its rows)
+    uint32_t k_off[KL::N], v_off[VL::N];
+    KL::lane_offsets(p.k_sr, tid, k_off);
+    VL::lane_offsets(p.v_sr, tid, v_off);
     auto copy_tile = [&](int t, T* kl, T* vl) __attribute__((always_inline)) {
       if (fast) {
-        KL::issue_buf(k_rs, k_srb, t * C::BN, Lk, kl, tid);
-        VL::issue_buf(v_rs, v_srb, t * C::BN, Lk, vl, tid);
+        if ((t + 1) * C::BN <= Lk) {
+          KL::issue_buf_full(k_rs, (uint32_t)(t * C::BN) * k_srb, k_off, kl, tid);
+          VL::issue_buf_full(v_rs, (uint32_t)(t * C::BN) * v_srb, v_off, vl, tid);
+        } else {
+          KL::issue_buf(k_rs, k_srb, t * C::BN, Lk, kl, tid);
+          VL::issue_buf(v_rs, v_srb, t * C::BN, Lk, vl, tid);
+        }
       } else {
         KL::issue_rows(Kb, p.k_sr, t * C::BN, Lk, kl, tid);
         VL::issue_rows(Vb, p.v_sr, t * C::BN, Lk, vl, tid);
