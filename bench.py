@@ -37,7 +37,7 @@ PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA, published
 PEAK_HBM_GBS = 8000.0
 METRIC = "attention fwd+bwd TFLOP/s and % of MFMA peak (bf16 causal GQA, n=4096)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_dkdv_causal_gqa_b8_n4096_traffic.txt")
-KERNEL_SOURCES = ("attn_bwd.hip", "attn_device.h", "attn_internal.h")
+KERNEL_SOURCES = ("attn_bwd_quad.hip", "attn_device.h", "attn_internal.h")
 DOMINANT = "bwd_dkdv"
 
 

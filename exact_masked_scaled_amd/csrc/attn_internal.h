@@ -116,6 +116,8 @@ attn_status linear_bwd(attn_gemm ctx, const attn_linear& L, const void* X, const
 int launch_fwd(const KernelParams& p, int dtype, int d_h, int d_v, void* stream);
 int launch_bwd_dq(const KernelParams& p, int dtype, int d_h, int d_v, void* stream);
 int launch_bwd_dkdv(const KernelParams& p, int dtype, int d_h, int d_v, void* stream);
+// bf16 dK/dV pass by the four-role kernel (attn_bwd_quad.hip)
+int launch_bwd_dkdv_quad(const KernelParams& p, int d_h, int d_v, void* stream);
 int launch_dkdv_combine(const KernelParams& p, int dtype, int d_h, int d_v, void* stream);
 // forward split over the keys (p.splits > 1): partial pass, then the merge
 int launch_fwd_split(const KernelParams& p, int dtype, int d_h, int d_v, void* stream);

@@ -9,7 +9,10 @@ the forward split over the keys and the backward:
 * rows 2^24 + 512 elements apart with the heads interleaved inside a row
   ([B, n, H, d] storage), so a 64-row tile spans more than 2^31 bytes and the
   forward takes its general copy path, and the last rows of each tensor lie
-  past 4 GiB.
+  past 4 GiB;
+* rows 2^26 + 512 elements apart in the same storage, so even a 32-row block
+  of Q or G_O spans more than 4 GiB and the bf16 dK/dV pass takes its 64-bit
+  copy path instead of buffer copies.
 
 Each tensor sits in one large allocation with only its strided rows written
 (about 35-70 GB of device memory per case, freed between cases)."""
@@ -28,6 +31,7 @@ pytestmark = pytest.mark.gpu
 
 BATCH_STRIDE = 2 ** 31 + 256
 ROW_STRIDE = 2 ** 24 + 512
+ROW_STRIDE_HUGE = 2 ** 26 + 512
 NEED_BYTES = 100 * 2 ** 30  # device memory the largest case needs, with margin
 
 CASES = [
@@ -35,6 +39,7 @@ CASES = [
     ("batch_bf16", "batch", W.BF16, 2, 4, 2, 200, 200, 128, True, [0, 30], [200, 137], [200, 181]),
     ("batch_f32", "batch", W.F32, 2, 2, 1, 130, 150, 64, False, 0, [130, 77], [150, 99]),
     ("rows_bf16", "rows", W.BF16, 1, 4, 2, 160, 160, 128, True, 0, None, None),
+    ("rows_huge_bf16", "rows_huge", W.BF16, 1, 4, 2, 40, 40, 128, True, 0, None, None),
 ]
 
 
@@ -53,8 +58,9 @@ def _strided(torch, layout, dtype, B, H, n, d):
     if layout == "batch":
         size, strides = (B - 1) * BATCH_STRIDE + H * n * d, (BATCH_STRIDE, n * d, d, 1)
     else:
-        assert H * d <= ROW_STRIDE
-        size, strides = B * n * ROW_STRIDE, (n * ROW_STRIDE, d, ROW_STRIDE, 1)
+        rs = ROW_STRIDE if layout == "rows" else ROW_STRIDE_HUGE
+        assert H * d <= rs
+        size, strides = B * n * rs, (n * rs, d, rs, 1)
     buf = torch.empty(size, dtype=dtype, device="cuda")
     return torch.as_strided(buf, (B, H, n, d), strides)
 
