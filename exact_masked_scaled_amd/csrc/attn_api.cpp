@@ -127,6 +127,7 @@ int chunk_size(const KernelParams& kp, int B) {
 struct BwdPlan {
   int32_t dq_splits = 1, hsplits = 1;
   int64_t q_rows = 0, k_rows = 0;      // rows of lse / D, and of the key partials
+  size_t row_bytes = 0;                 // one float per row of lse: the -D array, then the lse2 array
   size_t d_bytes = 0, dq_bytes = 0, kv_bytes = 0;
 };
 BwdPlan bwd_plan(const attn_problem& p, bool rope) {
@@ -134,7 +135,8 @@ BwdPlan bwd_plan(const attn_problem& p, bool rope) {
   const bool packed = p.cu_seqlens_q != nullptr;
   pl.q_rows = packed ? (int64_t)p.H_q * std::max(p.cu_seqlens_q[p.B], 0) : (int64_t)p.B * p.H_q * p.n_q;
   pl.k_rows = packed ? (int64_t)p.H_kv * std::max(p.cu_seqlens_k[p.B], 0) : (int64_t)p.B * p.H_kv * p.n_k;
-  pl.d_bytes = align_up((size_t)p.B * (size_t)p.H_q * (size_t)p.n_q * sizeof(float), kWsAlign);
+  pl.row_bytes = align_up((size_t)p.B * (size_t)p.H_q * (size_t)p.n_q * sizeof(float), kWsAlign);
+  pl.d_bytes = 2 * pl.row_bytes;
   if (p.B <= 0 || p.H_kv <= 0 || rope) return pl;
   const int64_t nb = std::min(p.B, kMaxBatchChunk);
   const int64_t group = p.H_q / p.H_kv;
@@ -342,7 +344,7 @@ attn_status bwd_enqueue(const attn_problem& p, const attn_mask& m, const BwdPtrs
   }
   const int nqblk = (p.n_q + bwd_dq_block_rows(p.dtype) - 1) / bwd_dq_block_rows(p.dtype);
   const int nkblk = (p.n_k + bwd_dkdv_block_keys(p.dtype) - 1) / bwd_dkdv_block_keys(p.dtype);
-  // workspace: D, then the partials of divided passes
+  // workspace: -D, lse2, then the partials of divided passes
   const BwdPlan pl = bwd_plan(p, rc != nullptr);
   float* part_q = delta ? (float*)((char*)delta + pl.d_bytes) : nullptr;
   float* part_kv = delta ? (float*)((char*)delta + pl.d_bytes + pl.dq_bytes) : nullptr;
@@ -362,6 +364,7 @@ attn_status bwd_enqueue(const attn_problem& p, const attn_mask& m, const BwdPtrs
     kp.dout = off(t.dO, b0 * p.o_stride[0], es);
     kp.lse = t.lse ? const_cast<float*>(t.lse) + row0 : nullptr;
     kp.delta = delta ? delta + row0 : nullptr;
+    kp.lse2 = delta ? (float*)((char*)delta + pl.row_bytes) + row0 : nullptr;
     kp.dq = off(t.dQ, b0 * p.q_stride[0], es);
     kp.dk = off(t.dK, b0 * p.k_stride[0], es);
     kp.dv = off(t.dV, b0 * p.v_stride[0], es);

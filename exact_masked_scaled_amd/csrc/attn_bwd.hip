@@ -114,8 +114,12 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(con
     }
   }
   const float Di = row_active ? dpart + partner32(dpart) : 0.f;
-  if (row_exists && kg == 0 && sidx == 0) p.delta[rowbase + qi] = Di;
   const float lse2 = row_active ? p.lse[rowbase + qi] * 1.4426950408889634f : 0.f;
+  // for the dK/dV pass: -D_i (its dP chains start from it) and lse_i log2 e
+  if (row_exists && kg == 0 && sidx == 0) {
+    p.delta[rowbase + qi] = -Di;
+    p.lse2[rowbase + qi] = lse2;
+  }
 
   const int act_hi = min(q_lo + C::BM, Lq);
   int ntiles = 0, nfull = 0;
@@ -447,7 +451,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const KernelParams p) 
     // here, so no argument load sits behind the copies in the memory queue)
     const T* const q_base = (const T*)p.q + b * p.q_sb + sv.q_row0 * p.q_sr;
     const T* const o_base = (const T*)p.dout + b * p.o_sb + sv.q_row0 * p.o_sr;
-    const float* const rows_base = (lane < 32 ? p.lse : p.delta) + b * p.lse_sb + sv.q_row0;
+    const float* const rows_base = (lane < 32 ? p.lse2 : p.delta) + b * p.lse_sb + sv.q_row0;
     const int64_t q_sh = p.q_sh, o_sh = p.o_sh, q_sr = p.q_sr, o_sr = p.o_sr, r_sh = p.lse_sh;
     // copies of rows past the last active one repeat it (finite data only)
     const int n_q = Lq, group = p.group;
@@ -506,8 +510,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const KernelParams p) 
       f32x4 l4[4], d4[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        l4[j] = *reinterpret_cast<const f32x4*>(&lse_s[8 * j + 4 * kg]) * 1.4426950408889634f;
-        d4[j] = *reinterpret_cast<const f32x4*>(&dlt_s[8 * j + 4 * kg]);
+        l4[j] = *reinterpret_cast<const f32x4*>(&lse_s[8 * j + 4 * kg]);  // lse log2 e
+        d4[j] = *reinterpret_cast<const f32x4*>(&dlt_s[8 * j + 4 * kg]);  // -D
       }
 
       // S and dP for the wave's keys (lane = key, registers = queries)
@@ -535,7 +539,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const KernelParams p) 
           for (int e = 0; e < 16; ++e) {
             const float pv = __builtin_amdgcn_exp2f(sv[kt][e] * p.scale_log2 - l4[e >> 2][e & 3]);
             sv[kt][e] = pv;
-            dp[kt][e] = pv * (dp[kt][e] - d4[e >> 2][e & 3]);
+            dp[kt][e] = pv * (dp[kt][e] + d4[e >> 2][e & 3]);
           }
       } else {
         const int off_eff = p.causal ? off : p.n_k;  // j <= i + n_k always holds
@@ -549,7 +553,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const KernelParams p) 
             float pv = __builtin_amdgcn_exp2f(sv[kt][e] * p.scale_log2 - l4[e >> 2][e & 3]);
             pv = vis ? pv : 0.f;
             sv[kt][e] = pv;
-            dp[kt][e] = pv * (dp[kt][e] - d4[e >> 2][e & 3]);
+            dp[kt][e] = pv * (dp[kt][e] + d4[e >> 2][e & 3]);
           }
         }
       }

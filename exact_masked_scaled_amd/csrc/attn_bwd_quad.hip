@@ -171,7 +171,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
     const int64_t q_sh = p.q_sh, o_sh = p.o_sh, q_sr = p.q_sr, o_sr = p.o_sr, r_sh = p.lse_sh;
     // copies of rows past the last active one repeat it (finite data only)
     const int n_q = Lq, group = p.group;
-    const float* const rows_lane = (lane < 32 ? p.lse : p.delta) + b * p.lse_sb + sv.q_row0 + (lane & 31);
+    // the step's rows: lse log2 e (lanes 0-31) and -D (lanes 32-63), from the dQ pass
+    const float* const rows_lane = (lane < 32 ? p.lse2 : p.delta) + b * p.lse_sb + sv.q_row0 + (lane & 31);
     const int yw = w & 3;  // copy slot of a Y wave
     // Copy instruction i of a Y wave moves job yw + 4 i of the step's 64-lane
     // jobs (Q chunks first, then G_O; i < QCH / 256 a Q chunk since yw < 4).
@@ -302,7 +303,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
         if constexpr (ex) {
 #pragma unroll
           for (int e = EPK * ks; e < EPK * (ks + 1); ++e) {
-            const float lse2 = l4v[e >> 2][e & 3] * 1.4426950408889634f;
+            const float lse2 = l4v[e >> 2][e & 3];
             const int q = q0_old + 8 * (e >> 2) + 4 * kg + (e & 3);
 #pragma unroll
             for (int kb2 = 0; kb2 < 2; ++kb2) {
@@ -341,19 +342,25 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
       f32x16& o0 = R[XB + 2 * jo];
       f32x16& o1 = R[XB + 2 * jo + 1];
       if constexpr (mf) {
+        // the dP chains start from -D of their rows (rows: the dP step's), so
+        // they end at dP - D
+        f32x16 nd;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) { d0[e] = 0.f; d1[e] = 0.f; }
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(&rows[C::BM + 8 * j + 4 * kg]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) nd[4 * j + e] = v[e];
+        }
+        d0 = nd;
+        d1 = nd;
       }
       constexpr int KS = DV / 16;
       constexpr int EPK = 16 / KS;
       const op_t* pin = xpb + (h * 2) * 2 * 64;
       op_t* xo = xb + (h * 2) * 2 * 64;
-      // operands are read one k-step ahead of their products; D and P up front
-      f32x4 d4v[4];
+      // operands are read one k-step ahead of their products; P up front
       op_t pp[2][2];
       if constexpr (ex) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) d4v[j] = *reinterpret_cast<const f32x4*>(&rows[C::BM + 8 * j + 4 * kg]);
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
@@ -372,9 +379,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
         if constexpr (ex) {
 #pragma unroll
           for (int e = EPK * ks; e < EPK * (ks + 1); ++e) {
-            const float dd = d4v[e >> 2][e & 3];
-            o0[e] = (float)pp[0][e >> 3][e & 7] * (o0[e] - dd);
-            o1[e] = (float)pp[1][e >> 3][e & 7] * (o1[e] - dd);
+            o0[e] = (float)pp[0][e >> 3][e & 7] * o0[e];
+            o1[e] = (float)pp[1][e >> 3][e & 7] * o1[e];
           }
           if (EPK * (ks + 1) % 8 == 0) {
             const int st = EPK * (ks + 1) / 8 - 1;
@@ -512,7 +518,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
         // XD: dP(s - 1) into parity (s - 1) & 1, G_S(s - 2) -> G_S slot 3 + (s - 2) % 2
         constexpr int jd = (u + 1) & 1;
         const T* Os = o_st(IC<u + NS - 1>());
-        const float* rows = r_st(IC<u + NS - 2>());
+        const float* rows = r_st(IC<u + NS - 1>());  // -D of step s - 1
         const op_t* pin = xch + ((u + 1) % 3) * XSLOT;  // P(s - 2)
         op_t* xw = xch + (3 + (u & 1)) * XSLOT;         // G_S(s - 2)
         const bool mf = !ramp || (s >= 1 && s <= nsteps), ex = !ramp || (s >= 2 && s <= nsteps + 1);

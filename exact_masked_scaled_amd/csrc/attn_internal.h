@@ -23,7 +23,8 @@ struct KernelParams {
   const void* dout;   // G_O
   void* o_out;        // forward: O
   float* lse;         // [B][H_q][n_q]
-  float* delta;       // workspace: D = rowsum(G_O o O), [B][H_q][n_q]
+  float* delta;       // workspace: -D = -rowsum(G_O o O), indexed like lse (written by the dQ pass)
+  float* lse2;        // workspace: lse * log2(e), indexed like lse (written by the dQ pass)
   void* dq;
   void* dk;
   void* dv;

@@ -113,7 +113,7 @@ typedef struct {
    * NULL) and no padding rows exist.  Element (row t, head h, column c) of Q
    * is at t * q_stride[2] + h * q_stride[1] + c: q_stride[0] (and the other
    * batch strides) must be 0.  n_q and n_k are upper bounds of the lengths
-   * (they size the launch grids).  lse and the workspace's D are then
+   * (they size the launch grids).  lse and the workspace's per-row arrays are then
    * [H_q][cu_seqlens_q[B]] float32.  Requires cu_seqlens_*[0] == 0,
    * non-decreasing entries and row totals below 2^31. */
   const int32_t* cu_seqlens_q;
@@ -133,10 +133,11 @@ typedef struct {
 attn_status attn_validate(const attn_problem* prob, const attn_mask* mask);
 
 /* Bytes of device workspace attn_bwd needs for `prob` (256-byte aligned
- * base): per-row float32 D_i = rowsum(G_O o O), the row scalar c_i of
- * "Appendix A.10" eq. A.10.7 (c_i = sum_j A_ij sum_l G_O[i,l] V[j,l] =
- * sum_l G_O[i,l] O[i,l]), B * H_q * n_q floats (an
- * upper bound of H_q * cu_seqlens_q[B] in the packed layout), and, when the
+ * base): two per-row float32 arrays of B * H_q * n_q floats each (an upper
+ * bound of H_q * cu_seqlens_q[B] in the packed layout), -D_i with
+ * D_i = rowsum(G_O o O), the row scalar c_i of "Appendix A.10" eq. A.10.7
+ * (c_i = sum_j A_ij sum_l G_O[i,l] V[j,l] = sum_l G_O[i,l] O[i,l]), and
+ * lse_i * log2(e), both written by the dQ pass for the dK/dV pass, and, when the
  * problem's grids are too small for the GPU, float32 partials of divided
  * passes: the dQ pass over parts of the keys (when it has fewer than 384
  * workgroups of 128 rows and the keys span at least 8 tiles of 64: parts =
@@ -218,10 +219,12 @@ attn_status attn_bwd_noalloc(const attn_problem* prob, const attn_mask* mask,
 /* The backward in its two passes, for callers that schedule or time them
  * separately; attn_bwd is exactly attn_bwd_dq followed by attn_bwd_dkdv on
  * one stream with one workspace.  Each validates like attn_bwd.
- *   dq:   forms D_i = rowsum(G_O o O) (the row scalar c_i of eq. A.10.7) into
- *         the workspace and writes G_Q (eqs. A.10.6-A.10.8);
- *   dkdv: reads D from the workspace and writes G_K and G_V (eqs. A.10.5-7,
- *         A.10.9), summed over the query heads of each KV head.
+ *   dq:   forms D_i = rowsum(G_O o O) (the row scalar c_i of eq. A.10.7),
+ *         stores -D_i and lse_i log2(e) in the workspace and writes G_Q
+ *         (eqs. A.10.6-A.10.8);
+ *   dkdv: reads those two arrays from the workspace and writes G_K and G_V
+ *         (eqs. A.10.5-7, A.10.9), summed over the query heads of each KV
+ *         head.
  * Each G_Q, G_K and G_V element is written exactly once (no atomics), so
  * results are bitwise reproducible. */
 attn_status attn_bwd_dq(const attn_problem* prob, const attn_mask* mask,
@@ -278,7 +281,7 @@ attn_status attn_fwd_rope(const attn_problem* prob, const attn_mask* mask, const
 /* Backward with rotary positions: from the unrotated Q and K, the forward's O
  * and lse, and G_O, writes G_Q = R^T G_Q~, G_K = R^T G_K~ and G_V.  The
  * workspace (attn_bwd_rope_workspace_size(prob) bytes, 256-byte aligned)
- * holds D, then q~, then k~, in contiguous layouts: k~ is rotated into it by
+ * holds attn_bwd's workspace, then q~, then k~, in contiguous layouts: k~ is rotated into it by
  * a streaming pass, q~ is written by the dQ pass, which turns each query row
  * as it loads it; the dK/dV pass reads both.  The turn back of G_Q~ and G_K~
  * happens in the two passes' stores (no rounding of the rotated gradients in
@@ -357,7 +360,7 @@ attn_status attn_self_attention_fwd(const attn_problem* prob, const attn_mask* m
 /* Its backward: from X, W_qkv, the forward's QKV, O and lse, and G_O, writes
  * G_X [rows][d_model] = G_Q W_Q^T + G_K W_K^T + G_V W_V^T and G_W [d_model][C]
  * = X^T [G_Q | G_K | G_V] (either may be NULL).  The workspace
- * (attn_self_attention_bwd_workspace_size bytes, 256-byte aligned) holds D
+ * (attn_self_attention_bwd_workspace_size bytes, 256-byte aligned) holds attn_bwd's workspace
  * and [G_Q | G_K | G_V] [rows][C]. */
 size_t attn_self_attention_bwd_workspace_size(const attn_problem* prob);
 attn_status attn_self_attention_bwd(const attn_problem* prob, const attn_mask* mask, attn_gemm ctx,

@@ -136,12 +136,12 @@ def _al(x):
 
 def test_workspace_size():
     lib_or_skip()
-    # a grid that fills the GPU: D only
+    # a grid that fills the GPU: the two per-row arrays (-D and lse log2 e) only
     p = prob(B=8, H_q=32, H_kv=8, n_q=4096, n_k=4096, d_h=128, d_v=128)
-    assert A.workspace_size(p) == _al(8 * 32 * 4096 * 4)
+    assert A.workspace_size(p) == 2 * _al(8 * 32 * 4096 * 4)
     assert A.workspace_size(prob(B=0)) == 0
-    # float32 (no head split) with few keys (no key split): D only
-    assert A.workspace_size(prob(B=3, H_q=4, n_q=100, d_h=128, dtype=A.F32)) == _al(3 * 4 * 100 * 4)
+    # float32 (no head split) with few keys (no key split): the per-row arrays only
+    assert A.workspace_size(prob(B=3, H_q=4, n_q=100, d_h=128, dtype=A.F32)) == 2 * _al(3 * 4 * 100 * 4)
 
 
 def test_workspace_size_divided_passes():
@@ -159,7 +159,7 @@ def test_workspace_size_divided_passes():
     s = min(-(-512 // dq_wgs), 128 // 4, 16)
     hs = min(-(-256 // kv_wgs), 32, 8)
     assert (s, hs) == (4, 2)
-    want = _al(rows * 4) + _al(s * rows * 128 * 4) + _al(hs * krows * 256 * 4)
+    want = 2 * _al(rows * 4) + _al(s * rows * 128 * 4) + _al(hs * krows * 256 * 4)
     assert A.workspace_size(p) == want
     # packed rows: partial rows follow the packed totals
     pk = packed([0, 100, 300], [0, 600, 1200], H_q=4, H_kv=2)
@@ -167,7 +167,7 @@ def test_workspace_size_divided_passes():
     dq_wgs, kv_wgs = 2 * 4 * 2, 2 * 2 * 5
     s = min(-(-512 // dq_wgs), 10 // 4, 16)
     hs = min(-(-256 // kv_wgs), 2, 8)
-    assert A.workspace_size(pk) == (_al(2 * 4 * 200 * 4) + _al(s * rows_p * 128 * 4)
+    assert A.workspace_size(pk) == (2 * _al(2 * 4 * 200 * 4) + _al(s * rows_p * 128 * 4)
                                     + _al(hs * krows_p * (128 + 64) * 4))
 
 
