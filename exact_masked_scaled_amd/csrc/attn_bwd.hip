@@ -186,6 +186,9 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(con
       const bool masked = t >= nfull;  // tile straddles the causal diagonal or the key length
 #pragma unroll
       for (int mt = 0; mt < C::BN / 32; ++mt) {
+        // each slice's chains scheduled on their own (their read-ahead order
+        // below is pinned per slice)
+        __builtin_amdgcn_sched_barrier(0);
         f32x16 s, dp = negd;
 #pragma unroll
         for (int e = 0; e < 16; ++e) s[e] = 0.f;
