@@ -283,20 +283,24 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
       }
       constexpr int KS = DH / 16;
       constexpr int EPK = 16 / KS;  // elements of each block finished per k-step
-      // operands are read one k-step ahead of their products, the rows up front
+      // the rows up front
       f32x4 l4v[4];
       if constexpr (ex) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) l4v[j] = *reinterpret_cast<const f32x4*>(&rows[8 * j + 4 * kg]);
       }
-      op_t a_nxt;
-      if constexpr (mf) a_nxt = row_op(Qs, ofs[0]);
+      constexpr int PF = 2;  // operand reads run PF k-steps ahead of their products
+      op_t qa[PF + 1];
+      if constexpr (mf) {
+#pragma unroll
+        for (int j = 0; j < PF; ++j) qa[j] = row_op(Qs, ofs[j]);
+      }
       op_t* xo = xb + (h * 2) * 2 * 64;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         if constexpr (mf) {
-          const op_t a = a_nxt;
-          if (ks + 1 < KS) a_nxt = row_op(Qs, ofs[ks + 1]);
+          const op_t a = qa[ks % (PF + 1)];
+          if (ks + PF < KS) qa[(ks + PF) % (PF + 1)] = row_op(Qs, ofs[ks + PF]);
           mma(s0, a, op_part(R[ks / 4], ks % 4));
           mma(s1, a, op_part(R[(DH / 16 + ks) / 4], (DH / 16 + ks) % 4));
         }
@@ -358,7 +362,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
       constexpr int EPK = 16 / KS;
       const op_t* pin = xpb + (h * 2) * 2 * 64;
       op_t* xo = xb + (h * 2) * 2 * 64;
-      // operands are read one k-step ahead of their products; P up front
+      // P up front
       op_t pp[2][2];
       if constexpr (ex) {
 #pragma unroll
@@ -366,13 +370,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
 #pragma unroll
           for (int st = 0; st < 2; ++st) pp[kb2][st] = pin[(kb2 * 2 + st) * 64 + lane];
       }
-      op_t a_nxt;
-      if constexpr (mf) a_nxt = row_op(Os, ofs[0]);
+      constexpr int PF = 2;  // operand reads run PF k-steps ahead of their products
+      op_t oa[PF + 1];
+      if constexpr (mf) {
+#pragma unroll
+        for (int j = 0; j < PF; ++j) oa[j] = row_op(Os, ofs[j]);
+      }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         if constexpr (mf) {
-          const op_t a = a_nxt;
-          if (ks + 1 < KS) a_nxt = row_op(Os, ofs[ks + 1]);
+          const op_t a = oa[ks % (PF + 1)];
+          if (ks + PF < KS) oa[(ks + PF) % (PF + 1)] = row_op(Os, ofs[ks + PF]);
           mma(d0, a, op_part(R[ks / 4], ks % 4));
           mma(d1, a, op_part(R[(DV / 16 + ks) / 4], (DV / 16 + ks) % 4));
         }
