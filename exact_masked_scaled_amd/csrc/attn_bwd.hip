@@ -99,27 +99,39 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(con
   T* dQb = (T*)p.dq + b * p.dq_sb + sv.q_row0 * p.dq_sr + r * p.dq_sh;
   const int64_t rowbase = b * p.lse_sb + r * p.lse_sh + sv.q_row0;
 
-  // this lane's G_O row (B operand of dP^T = V G_O^T) and D_i = G_O . O
-  op_t doreg[DV / 16];
+  // this lane's G_O row (B operand of dP^T = V G_O^T) and D_i = G_O . O; the
+  // row's loads (and its lse) are issued together under one branch, so they
+  // are in flight at once and waited for once
+  op_t doreg[DV / 16], oreg[DV / 16];
+  float lse_i = 0.f;
+  if (row_active) {
+#pragma unroll
+    for (int ks = 0; ks < DV / 16; ++ks) {
+      doreg[ks] = ld8<T>(dOb + (int64_t)qi * p.o_sr + 16 * ks + 8 * kg);
+      oreg[ks] = ld8<T>(Ob + (int64_t)qi * p.o_sr + 16 * ks + 8 * kg);
+    }
+    lse_i = p.lse[rowbase + qi];
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < DV / 16; ++ks) doreg[ks] = oreg[ks] = zero_op<T>();
+  }
   float dpart = 0.f;
 #pragma unroll
-  for (int ks = 0; ks < DV / 16; ++ks) {
-    if (row_active) {
-      doreg[ks] = ld8<T>(dOb + (int64_t)qi * p.o_sr + 16 * ks + 8 * kg);
-      const op_t o8 = ld8<T>(Ob + (int64_t)qi * p.o_sr + 16 * ks + 8 * kg);
+  for (int ks = 0; ks < DV / 16; ++ks)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) dpart += (float)doreg[ks][e] * (float)o8[e];
-    } else {
-      doreg[ks] = zero_op<T>();
-    }
-  }
+    for (int e = 0; e < 8; ++e) dpart += (float)doreg[ks][e] * (float)oreg[ks][e];
   const float Di = row_active ? dpart + partner32(dpart) : 0.f;
-  const float lse2 = row_active ? p.lse[rowbase + qi] * 1.4426950408889634f : 0.f;
-  // for the dK/dV pass: -D_i (its dP chains start from it) and lse_i log2 e
-  if (row_exists && kg == 0 && sidx == 0) {
-    p.delta[rowbase + qi] = -Di;
-    p.lse2[rowbase + qi] = lse2;
-  }
+  const float lse2 = row_active ? lse_i * 1.4426950408889634f : 0.f;
+  // Stores that nothing in this kernel reads back go last: a store's address
+  // and data registers stay claimed until it completes, so an early store
+  // makes the next reuse of those registers wait for its write to finish.
+  // For the dK/dV pass: -D_i (its dP chains start from it) and lse_i log2 e.
+  auto row_stores = [&]() __attribute__((always_inline)) {
+    if (row_exists && kg == 0 && sidx == 0) {
+      p.delta[rowbase + qi] = -Di;
+      p.lse2[rowbase + qi] = lse2;
+    }
+  };
 
   const int act_hi = min(q_lo + C::BM, Lq);
   int ntiles = 0, nfull = 0;
@@ -144,22 +156,26 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(con
     for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
 
   if (t_hi > t_lo) {
+    // this lane's Q row (the loads under one branch, so they are all in
+    // flight at once)
     op_t qreg[DH / 16];
+    if (row_active) {
 #pragma unroll
-    for (int ks = 0; ks < DH / 16; ++ks)
-      qreg[ks] = row_active ? ld8<T>(Qb + (int64_t)qi * p.q_sr + 16 * ks + 8 * kg) : zero_op<T>();
+      for (int ks = 0; ks < DH / 16; ++ks) qreg[ks] = ld8<T>(Qb + (int64_t)qi * p.q_sr + 16 * ks + 8 * kg);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < DH / 16; ++ks) qreg[ks] = zero_op<T>();
+    }
+    // rotary positions: the lane's query row is turned (the row at position
+    // qi + rope_pos[b]) once the first key tile's copies are in flight; its
+    // table entries are loaded with the row, so that wait overlaps the copies
+    f32x4 qtab[ROPE ? DH / 16 : 1][2];
     if constexpr (ROPE) {
-      // rotary positions: the lane's query row turned as it is loaded (the
-      // row at position qi + rope_pos[b]), and the turned row written through
-      // to the copy the dK/dV pass reads (each active row once: one
-      // workgroup per row block and head)
       const float* cs = p.rope_cs + (int64_t)(max(min(qi, Lq - 1), 0) + p.rope_pos[b]) * DH + 8 * kg;
 #pragma unroll
-      for (int ks = 0; ks < DH / 16; ++ks) qreg[ks] = rope8<T>(qreg[ks], cs + 16 * ks, false);
-      if (row_active) {
-        T* qt = (T*)p.qt + b * p.qt_sb + sv.q_row0 * p.qt_sr + r * p.qt_sh + (int64_t)qi * p.qt_sr;
-#pragma unroll
-        for (int ks = 0; ks < DH / 16; ++ks) st8<T>(qt + 16 * ks + 8 * kg, qreg[ks]);
+      for (int ks = 0; ks < DH / 16; ++ks) {
+        qtab[ks][0] = *reinterpret_cast<const f32x4*>(cs + 16 * ks);
+        qtab[ks][1] = *reinterpret_cast<const f32x4*>(cs + 16 * ks + 4);
       }
     }
 
@@ -281,6 +297,10 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(con
       }
     };
     copy_tile(t_lo, k_lds0, v_lds0);
+    if constexpr (ROPE) {
+#pragma unroll
+      for (int ks = 0; ks < DH / 16; ++ks) qreg[ks] = rope8_tab<T>(qreg[ks], qtab[ks][0], qtab[ks][1], false);
+    }
     wait_tile_loads();
     __syncthreads();
     // two tiles per trip so each LDS buffer address is a compile-time constant
@@ -294,6 +314,15 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(con
       if (t + 1 < wtiles) tile(t + 1, k_lds1, v_lds1);
       wait_tile_loads();
       __syncthreads();
+    }
+    if constexpr (ROPE) {
+      // the turned row written through to the copy the dK/dV pass reads (each
+      // active row once: one workgroup per row block and head)
+      if (row_active) {
+        T* qt = (T*)p.qt + b * p.qt_sb + sv.q_row0 * p.qt_sr + r * p.qt_sh + (int64_t)qi * p.qt_sr;
+#pragma unroll
+        for (int ks = 0; ks < DH / 16; ++ks) st8<T>(qt + 16 * ks + 8 * kg, qreg[ks]);
+      }
     }
   }
 
@@ -314,6 +343,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(con
           *reinterpret_cast<f32x4*>(pq + d) = v4;
         }
     }
+    row_stores();
     return;
   }
   if (row_exists) {
@@ -352,6 +382,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(con
         st4<T>(dQb + (int64_t)qi * p.dq_sr + d, v[0], v[1], v[2], v[3]);
       }
   }
+  row_stores();
 }
 
 // ============================================================== dK/dV pass

@@ -147,14 +147,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
       const int nks = is_s ? DH / 16 : DV / 16;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
+        // keys past L_k read the last key's row (L_k > 0 here) and take
+        // zeros: the loads need no branch, so they are all in flight at once
         const int key = kh0 + 32 * kb2 + (lane & 31);
         const bool ok = key < Lk;
-        const T* row = src + (int64_t)key * sr + 8 * kg;
+        const T* row = src + (int64_t)min(key, Lk - 1) * sr + 8 * kg;
         constexpr int NK = (DH > DV ? DH : DV) / 16;
 #pragma unroll
         for (int ks = 0; ks < NK; ++ks) {
           if (ks >= nks) continue;
-          const op_t v = ok ? ld8<T>(row + 16 * ks) : zero_op<T>();
+          op_t v = ld8<T>(row + 16 * ks);
+          if (!ok) v = zero_op<T>();
           // operand kb2 * nks + ks: the block index is a constant in each role's branch
           if (is_s) {
             if (ks < DH / 16) set_op_part(R[(kb2 * (DH / 16) + ks) / 4], (kb2 * (DH / 16) + ks) % 4, v);
@@ -585,40 +588,51 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
   auto store = [&](auto NTC, auto TURN, T* dst, int64_t sr, float sc) __attribute__((always_inline)) {
     constexpr int NT = decltype(NTC)::value;
     constexpr bool turn = decltype(TURN)::value;
+    // blocks of eight values, i = (kb2, nt, half of the register block)
+    constexpr int NBLK = 2 * NT * 2;
     const bool odd = (lane & 1) != 0;
+    auto key = [&](int i, int e) __attribute__((always_inline)) {
+      const int eh = 8 * (i & 1);
+      return kh0 + 32 * (i / (2 * NT)) + 8 * ((eh + e) >> 2) + 4 * kg + ((eh + e) & 3);
+    };
+    // rotary positions: G_K = R^T G_K~, key kk at position kk.  A block's
+    // eight table entries are read TD blocks ahead of its stores, clamped into
+    // the valid keys (whose rows exist), and pinned by an empty asm where they
+    // are used, so the compiler cannot sink the loads into the guarded stores;
+    // keys past L_k keep their exact zeros.
+    constexpr int TD = 2;
+    float2 t[TD + 1][8];
+    auto load = [&](int i) __attribute__((always_inline)) {
+      const int c2 = (32 * ((i >> 1) % NT) + (lane & 31)) & ~1;
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
+      for (int e = 0; e < 8; ++e) {
+        const int kc = max(min(key(i, e), Lk - 1), 0);
+        t[i % (TD + 1)][e] = *reinterpret_cast<const float2*>(p.rope_cs + (int64_t)kc * DH + c2);
+      }
+    };
+    if constexpr (turn) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
+      for (int i = 0; i < TD; ++i) load(i);
+    }
 #pragma unroll
-        for (int eh = 0; eh < 16; eh += 8) {
-          float2 t[8];
-          if constexpr (turn) {
-            // rotary positions: G_K = R^T G_K~, key kk at position kk.  Eight
-            // table entries are read up front, clamped into the valid keys
-            // (whose rows exist), and pinned by an empty asm so the compiler
-            // cannot sink each load into its guarded store and wait for them
-            // one at a time; keys past L_k keep their exact zeros.
+    for (int i = 0; i < NBLK; ++i) {
+      const int kb2 = i / (2 * NT), nt = (i >> 1) % NT, eh = 8 * (i & 1);
+      if constexpr (turn) {
+        if (i + TD < NBLK) load(i + TD);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int kk = kh0 + 32 * kb2 + 8 * ((eh + e) >> 2) + 4 * kg + ((eh + e) & 3);
-              const int kc = max(min(kk, Lk - 1), 0);
-              t[e] = *reinterpret_cast<const float2*>(p.rope_cs + (int64_t)kc * DH + ((32 * nt + (lane & 31)) & ~1));
-            }
+        for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(t[i % (TD + 1)][e].x), "+v"(t[i % (TD + 1)][e].y));
+      }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(t[e].x), "+v"(t[e].y));
-          }
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int kk = kh0 + 32 * kb2 + 8 * ((eh + e) >> 2) + 4 * kg + ((eh + e) & 3);
-            float val = R[kb2 * NT + nt][eh + e] * sc;
-            if constexpr (turn) {
-              const float turned = rope_back_lanes(val, t[e].x, t[e].y, odd);
-              val = kk < Lk ? turned : val;
-            }
-            if (kk < nk_lim) dst[(int64_t)kk * sr + 32 * nt + (lane & 31)] = (T)val;
-          }
+      for (int e = 0; e < 8; ++e) {
+        const int kk = key(i, e);
+        float val = R[kb2 * NT + nt][eh + e] * sc;
+        if constexpr (turn) {
+          const float turned = rope_back_lanes(val, t[i % (TD + 1)][e].x, t[i % (TD + 1)][e].y, odd);
+          val = kk < Lk ? turned : val;
         }
+        if (kk < nk_lim) dst[(int64_t)kk * sr + 32 * nt + (lane & 31)] = (T)val;
+      }
+    }
   };
   if constexpr (HSPLIT) {
     // float32 partials of this part of the heads (no rotation: the split is

@@ -307,7 +307,9 @@ template <typename T>
 __device__ __forceinline__ bool fits_u32(int64_t rows, int64_t row_stride, int width) {
   if (row_stride < 0) return false;
   const int64_t r = rows > 1 ? rows : 1;
-  return (r - 1) * row_stride * (int64_t)sizeof(T) + (int64_t)width * (int64_t)sizeof(T) <= 0xffffffffLL;
+  // (a shift and a 64-bit compare with zero stay in scalar instructions; an
+  // unsigned 64-bit ordered compare would go through vector registers)
+  return ((uint64_t)((r - 1) * row_stride * (int64_t)sizeof(T) + (int64_t)width * (int64_t)sizeof(T)) >> 32) == 0;
 }
 
 // ---------------------------------------------------------------- tile staging
@@ -487,12 +489,11 @@ __device__ __forceinline__ void rope_pair(float c, float s, float& x0, float& x1
   x1 = y1;
 }
 
-// Eight consecutive columns (starting at an even column c0) of a row:
-// cs8 = table row + c0 holds (cos, sin) of the four pairs in order.
+// Eight consecutive columns (starting at an even column c0) of a row, turned
+// by the four pairs' table entries (t0, t1) = (cos, sin) of each pair in order.
 template <typename T>
-__device__ __forceinline__ typename Op<T>::type rope8(const typename Op<T>::type& x, const float* cs8, bool inverse) {
-  const f32x4 t0 = *reinterpret_cast<const f32x4*>(cs8);
-  const f32x4 t1 = *reinterpret_cast<const f32x4*>(cs8 + 4);
+__device__ __forceinline__ typename Op<T>::type rope8_tab(const typename Op<T>::type& x, const f32x4& t0,
+                                                          const f32x4& t1, bool inverse) {
   const float tab[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
   float v[8];
 #pragma unroll
@@ -500,6 +501,12 @@ __device__ __forceinline__ typename Op<T>::type rope8(const typename Op<T>::type
 #pragma unroll
   for (int m = 0; m < 4; ++m) rope_pair(tab[2 * m], inverse ? -tab[2 * m + 1] : tab[2 * m + 1], v[2 * m], v[2 * m + 1]);
   return to_op<T>(v);
+}
+
+// The same reading the entries at cs8 = table row + c0.
+template <typename T>
+__device__ __forceinline__ typename Op<T>::type rope8(const typename Op<T>::type& x, const float* cs8, bool inverse) {
+  return rope8_tab<T>(x, *reinterpret_cast<const f32x4*>(cs8), *reinterpret_cast<const f32x4*>(cs8 + 4), inverse);
 }
 
 // A value of column c whose pair partner (column c ^ 1) sits in lane ^ 1:

@@ -131,9 +131,27 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(const 
   if (t_hi > t_lo) {
     // Q of this lane's row as the B operand of S^T = K Q^T (row k order)
     op_t qreg[DH / 16];
+    // (the row's loads under one branch, so they are all in flight at once)
+    if (row_active) {
 #pragma unroll
-    for (int ks = 0; ks < DH / 16; ++ks)
-      qreg[ks] = row_active ? ld8<T>(Qb + (int64_t)qi * p.q_sr + 16 * ks + 8 * kg) : zero_op<T>();
+      for (int ks = 0; ks < DH / 16; ++ks) qreg[ks] = ld8<T>(Qb + (int64_t)qi * p.q_sr + 16 * ks + 8 * kg);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < DH / 16; ++ks) qreg[ks] = zero_op<T>();
+    }
+    // rotary positions: the table entries of the lane's row (at position
+    // qi + rope_pos[b]; inactive rows hold zeros and read an active row's
+    // entries) are loaded with the row, so the turn below, made once the
+    // first tiles are in flight, does not wait for them one by one
+    f32x4 qtab[ROPE ? DH / 16 : 1][2];
+    if constexpr (ROPE) {
+      const float* cs = p.rope_cs + (int64_t)(max(min(qi, Lq - 1), 0) + p.rope_pos[b]) * DH + 8 * kg;
+#pragma unroll
+      for (int ks = 0; ks < DH / 16; ++ks) {
+        qtab[ks][0] = *reinterpret_cast<const f32x4*>(cs + 16 * ks);
+        qtab[ks][1] = *reinterpret_cast<const f32x4*>(cs + 16 * ks + 4);
+      }
+    }
 
     RowOffsets<T, DH> kro;
     TrOffsets<T, DV> vto;
@@ -172,12 +190,9 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(const 
     };
     copy_tile(t_lo, k_lds0, v_lds0);
     if constexpr (ROPE) {
-      // rotary positions: the lane's row at position qi + rope_pos[b], turned
-      // while the first tiles are in flight
-      // (inactive rows hold zeros and read an active row's entries)
-      const float* cs = p.rope_cs + (int64_t)(max(min(qi, Lq - 1), 0) + p.rope_pos[b]) * DH + 8 * kg;
+      // the lane's row turned while the first tiles are in flight
 #pragma unroll
-      for (int ks = 0; ks < DH / 16; ++ks) qreg[ks] = rope8<T>(qreg[ks], cs + 16 * ks, false);
+      for (int ks = 0; ks < DH / 16; ++ks) qreg[ks] = rope8_tab<T>(qreg[ks], qtab[ks][0], qtab[ks][1], false);
     }
     wait_tile_loads();
     __syncthreads();
