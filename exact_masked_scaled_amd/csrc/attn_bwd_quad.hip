@@ -429,11 +429,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) {
             const op_t bt = TrOffsets<T, D>::read_at(tile, 16 * st, ofs[nt], ofs[NOFS / 2 + nt]);
-            mma(R[nt], a[0][st], bt);
-            mma(R[NT + nt], a[1][st], bt);
+            mma(R[nt], bt, a[0][st]);
+            mma(R[NT + nt], bt, a[1][st]);
           }
       };
-      // YV: G_V += P^T G_O; YK: G_K += G_S^T Q.  With d_h = d_v one path, so
+      // YV: G_V^T += G_O^T P; YK: G_K^T += Q^T G_S (the transposed tile
+      // operand as A, the exchanged one as B, so a lane accumulates one key's
+      // columns and stores them four at a time).  With d_h = d_v one path, so
       // the two roles' accumulators share one register assignment.
       if constexpr (DH == DV) products(IC<DV>());
       else if (is_s) products(IC<DV>());
@@ -467,8 +469,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          mma(R[nt], a[0][st], ybt[st][nt]);
-          mma(R[NT + nt], a[1][st], ybt[st][nt]);
+          mma(R[nt], ybt[st][nt], a[0][st]);
+          mma(R[NT + nt], ybt[st][nt], a[1][st]);
         }
       y_load(IC<u + 1>());
     };
@@ -584,31 +586,27 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
     }
   }
 
-  // store: YV holds G_V, YK G_K (scaled) of both key blocks; lane = column, registers = keys
+  // store: YV holds G_V, YK G_K (scaled) of both key blocks, transposed:
+  // block kb2 * NT + nt of a lane holds key kh0 + 32 kb2 + lane % 32, element
+  // e column 32 nt + 8 (e / 4) + 4 kg + e % 4, so four consecutive columns go
+  // out in one store
   auto store = [&](auto NTC, auto TURN, T* dst, int64_t sr, float sc) __attribute__((always_inline)) {
     constexpr int NT = decltype(NTC)::value;
     constexpr bool turn = decltype(TURN)::value;
-    // blocks of eight values, i = (kb2, nt, half of the register block)
-    constexpr int NBLK = 2 * NT * 2;
-    const bool odd = (lane & 1) != 0;
-    auto key = [&](int i, int e) __attribute__((always_inline)) {
-      const int eh = 8 * (i & 1);
-      return kh0 + 32 * (i / (2 * NT)) + 8 * ((eh + e) >> 2) + 4 * kg + ((eh + e) & 3);
-    };
-    // rotary positions: G_K = R^T G_K~, key kk at position kk.  A block's
-    // eight table entries are read TD blocks ahead of its stores, clamped into
+    constexpr int NBLK = 2 * NT;  // blocks i = (kb2, nt)
+    // rotary positions: G_K = R^T G_K~, key kk at position kk; a lane's four
+    // columns are two pairs, whose (cos, sin) entries are one 16-byte read.
+    // A block's entries are read TD blocks ahead of its stores, clamped into
     // the valid keys (whose rows exist), and pinned by an empty asm where they
     // are used, so the compiler cannot sink the loads into the guarded stores;
     // keys past L_k keep their exact zeros.
     constexpr int TD = 2;
-    float2 t[TD + 1][8];
+    f32x4 t[TD + 1][4];
     auto load = [&](int i) __attribute__((always_inline)) {
-      const int c2 = (32 * ((i >> 1) % NT) + (lane & 31)) & ~1;
+      const int kc = max(min(kh0 + 32 * (i / NT) + (lane & 31), Lk - 1), 0);
+      const float* row = p.rope_cs + (int64_t)kc * DH + 32 * (i % NT) + 4 * kg;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int kc = max(min(key(i, e), Lk - 1), 0);
-        t[i % (TD + 1)][e] = *reinterpret_cast<const float2*>(p.rope_cs + (int64_t)kc * DH + c2);
-      }
+      for (int q4 = 0; q4 < 4; ++q4) t[i % (TD + 1)][q4] = *reinterpret_cast<const f32x4*>(row + 8 * q4);
     };
     if constexpr (turn) {
 #pragma unroll
@@ -616,21 +614,29 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
     }
 #pragma unroll
     for (int i = 0; i < NBLK; ++i) {
-      const int kb2 = i / (2 * NT), nt = (i >> 1) % NT, eh = 8 * (i & 1);
+      const int kb2 = i / NT, nt = i % NT;
+      const int kk = kh0 + 32 * kb2 + (lane & 31);
       if constexpr (turn) {
         if (i + TD < NBLK) load(i + TD);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(t[i % (TD + 1)][e].x), "+v"(t[i % (TD + 1)][e].y));
+        for (int q4 = 0; q4 < 4; ++q4) asm volatile("" : "+v"(t[i % (TD + 1)][q4]));
       }
+      if (kk < nk_lim) {
+        T* out = dst + (int64_t)kk * sr + 32 * nt + 4 * kg;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int kk = key(i, e);
-        float val = R[kb2 * NT + nt][eh + e] * sc;
-        if constexpr (turn) {
-          const float turned = rope_back_lanes(val, t[i % (TD + 1)][e].x, t[i % (TD + 1)][e].y, odd);
-          val = kk < Lk ? turned : val;
+        for (int q4 = 0; q4 < 4; ++q4) {
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = R[kb2 * NT + nt][4 * q4 + e] * sc;
+          if constexpr (turn) {
+            if (kk < Lk) {
+              const f32x4 c = t[i % (TD + 1)][q4];
+              rope_pair(c[0], -c[1], v[0], v[1]);
+              rope_pair(c[2], -c[3], v[2], v[3]);
+            }
+          }
+          ::attn::st4<T>(out + 8 * q4, v[0], v[1], v[2], v[3]);
         }
-        if (kk < nk_lim) dst[(int64_t)kk * sr + 32 * nt + (lane & 31)] = (T)val;
       }
     }
   };
@@ -642,15 +648,20 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
       auto store_part = [&](auto NTC, float* base, int D, float sc) __attribute__((always_inline)) {
         constexpr int NT = decltype(NTC)::value;
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+          const int kk = kh0 + 32 * kb2 + (lane & 31);
+          if (kk < nk_lim) {
+            float* out = base + ((int64_t)hs * p.part_krows + krow + kk) * D + 4 * kg;
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
+            for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              const int kk = kh0 + 32 * kb2 + 8 * (e >> 2) + 4 * kg + (e & 3);
-              if (kk < nk_lim)
-                base[((int64_t)hs * p.part_krows + krow + kk) * D + 32 * nt + (lane & 31)] = R[kb2 * NT + nt][e] * sc;
-            }
+              for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x16& r = R[kb2 * NT + nt];
+                ::attn::st4<float>(out + 32 * nt + 8 * q4, r[4 * q4] * sc, r[4 * q4 + 1] * sc, r[4 * q4 + 2] * sc,
+                           r[4 * q4 + 3] * sc);
+              }
+          }
+        }
       };
       if (is_s) store_part(IC<DV / 32>(), p.part_dv, DV, 1.f);
       else store_part(IC<DH / 32>(), p.part_dk, DH, p.scale);
