@@ -306,6 +306,17 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(con
     // two tiles per trip so each LDS buffer address is a compile-time constant
     for (int t = t_lo; t < t_hi; t += 2) {
       if (t + 1 < t_hi) copy_tile(t + 1, k_lds1, v_lds1);
+      if constexpr (ROPE) {
+        // the turned row written through to the copy the dK/dV pass reads
+        // (each active row once: one workgroup per row block and head),
+        // before the first tile's products, so they cover its latency before
+        // the tile's wait
+        if (t == t_lo && row_active) {
+          T* qt = (T*)p.qt + b * p.qt_sb + sv.q_row0 * p.qt_sr + r * p.qt_sh + (int64_t)qi * p.qt_sr;
+#pragma unroll
+          for (int ks = 0; ks < DH / 16; ++ks) st8<T>(qt + 16 * ks + 8 * kg, qreg[ks]);
+        }
+      }
       if (t < wtiles) tile(t, k_lds0, v_lds0);
       wait_tile_loads();
       __syncthreads();
@@ -314,15 +325,6 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(con
       if (t + 1 < wtiles) tile(t + 1, k_lds1, v_lds1);
       wait_tile_loads();
       __syncthreads();
-    }
-    if constexpr (ROPE) {
-      // the turned row written through to the copy the dK/dV pass reads (each
-      // active row once: one workgroup per row block and head)
-      if (row_active) {
-        T* qt = (T*)p.qt + b * p.qt_sb + sv.q_row0 * p.qt_sr + r * p.qt_sh + (int64_t)qi * p.qt_sr;
-#pragma unroll
-        for (int ks = 0; ks < DH / 16; ++ks) st8<T>(qt + 16 * ks + 8 * kg, qreg[ks]);
-      }
     }
   }
 
@@ -346,13 +348,40 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(con
     row_stores();
     return;
   }
-  if (row_exists) {
-    const float sc = row_active ? p.scale : 0.f;
-    // rotary positions: G_Q = R^T G_Q~ (the lane's four columns are two
-    // pairs); inactive rows (zeros) read an active row's table entries
-    constexpr bool turn = ROPE;
-    f32x4 tab[DH / 32][4];
-    if (turn) {
+  // rotary positions: G_Q = R^T G_Q~ (the lane's four columns are two
+  // pairs); inactive rows (zeros) read an active row's table entries
+  constexpr bool turn = ROPE;
+  f32x4 tab[DH / 32][4];
+  if constexpr (turn) {
+    // Each lane needs 16-byte pieces of its own row's table entries, so
+    // reading them directly touches a different table row in every lane.
+    // Where each wave's K / V buffer (free after the loop's last barrier)
+    // holds the wave's 32 table rows, the wave instead copies those rows in
+    // whole 1 KB pieces into it (the 16-byte chunk c of row r at position
+    // c ^ (r % 16), so the lanes' reads below hit distinct banks) and reads
+    // its entries from there.
+    constexpr bool staged = sizeof(v_lds0) >= 32 * DH * sizeof(float);
+    if constexpr (staged) {
+      constexpr int CH = DH / 4, RPI = 64 / CH;  // chunks per row, rows per copy
+      static_assert(CH >= 16 && 64 % CH == 0, "table staging needs 16 to 64 chunks per row");
+      float* tl = w == 0 ? (float*)k_lds0 : w == 1 ? (float*)k_lds1 : w == 2 ? (float*)v_lds0 : (float*)v_lds1;
+      const int r_lo = q_lo + 32 * w;
+      const int base_pos = max(min(r_lo, Lq - 1), 0) + p.rope_pos[b];
+      const __amdgpu_buffer_rsrc_t trs = buf_rsrc(p.rope_cs + (int64_t)base_pos * DH, 32u * DH * 4u);
+#pragma unroll
+      for (int i = 0; i < 32 / RPI; ++i) {
+        const int r = i * RPI + lane / CH, pos = lane % CH;
+        const int rel = max(min(r_lo + r, Lq - 1), 0) + p.rope_pos[b] - base_pos;
+        buf_copy16(trs, tl + i * 256, (uint32_t)(rel * DH * 4 + ((pos ^ (r & 15)) * 16)), 0u);
+      }
+      wait_tile_loads();
+      const int r = lane & 31;
+      const f32x4* row = reinterpret_cast<const f32x4*>(tl + r * DH);
+#pragma unroll
+      for (int dt = 0; dt < DH / 32; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) tab[dt][j] = row[(8 * dt + 2 * j + kg) ^ (r & 15)];
+    } else {
       // all of the row's table entries in flight at once (pinned so the
       // compiler keeps the loads together)
       const float* cs = p.rope_cs + (int64_t)(max(min(qi, Lq - 1), 0) + p.rope_pos[b]) * DH;
@@ -365,6 +394,9 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(con
 #pragma unroll
         for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(tab[dt][j]));
     }
+  }
+  if (row_exists) {
+    const float sc = row_active ? p.scale : 0.f;
 #pragma unroll
     for (int dt = 0; dt < DH / 32; ++dt)
 #pragma unroll
