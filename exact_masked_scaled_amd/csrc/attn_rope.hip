@@ -33,6 +33,26 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(const RopeParams p) {
   T* Y = (T*)p.y + b * p.y_sb + (int64_t)p.row0[b] * p.y_sr + h * p.y_sh;
   const bool inv = p.inverse != 0;
   const int64_t first = (int64_t)blockIdx.x * RPT * kTrips;
+  if (first + (int64_t)kTrips * RPT <= L) {
+    // every trip's row exists: all loads issued before the first turn, so
+    // the trips' memory latencies overlap
+    typename Op<T>::type x[kTrips];
+    f32x4 c[kTrips][2];
+#pragma unroll
+    for (int t = 0; t < kTrips; ++t) {
+      const int64_t i = first + t * RPT + row_in;
+      x[t] = ld8<T>(X + i * p.x_sr + c0);
+      const float* cs = p.cs + (i + p.pos0[b]) * D + c0;
+      c[t][0] = *reinterpret_cast<const f32x4*>(cs);
+      c[t][1] = *reinterpret_cast<const f32x4*>(cs + 4);
+    }
+#pragma unroll
+    for (int t = 0; t < kTrips; ++t) {
+      const int64_t i = first + t * RPT + row_in;
+      st8<T>(Y + i * p.y_sr + c0, rope8_tab<T>(x[t], c[t][0], c[t][1], inv));
+    }
+    return;
+  }
 #pragma unroll
   for (int t = 0; t < kTrips; ++t) {
     const int64_t i = first + t * RPT + row_in;
