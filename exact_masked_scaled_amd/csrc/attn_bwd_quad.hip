@@ -26,7 +26,8 @@ namespace attn {
 //   XS (waves 0, 1): holds K; S = Q K^T, then P = exp(S - lse) on the visible
 //       set, handed on as bf16 MFMA operands;
 //   XD (waves 2, 3): holds V; dP = G_O V^T, then G_S = P o (dP - D), handed on;
-//   YV (waves 4, 5): G_V += P^T G_O;     YK (waves 6, 7): G_K += G_S^T Q.
+//   YV (waves 4, 5): G_V += P^T G_O;     YK (waves 6, 7): G_K += G_S^T Q,
+//       both accumulated as their transposes (a lane holds one key's columns).
 // In iteration s, XS forms S of step s and the exponentials of step s - 1; XD
 // forms dP of step s - 1 and G_S of step s - 2; YV and YK accumulate step
 // s - 3.  Products and element-wise work of one wave are interleaved
