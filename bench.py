@@ -39,6 +39,8 @@ METRIC = "attention fwd+bwd TFLOP/s and % of MFMA peak (bf16 causal GQA, n=4096)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_dkdv_causal_gqa_b8_n4096_traffic.txt")
 KERNEL_SOURCES = ("attn_bwd_quad.hip", "attn_device.h", "attn_internal.h")
 DOMINANT = "bwd_dkdv"
+BACKWARD_KIND = {True: "score gradients kept (per-row pass, dK/dV pass storing G_S, dQ product)",
+                 False: "two passes (dQ pass and dK/dV pass, both recomputing S and dP)"}
 
 
 def kernel_source_hash() -> str:
@@ -119,11 +121,15 @@ def kernel_report(wl, work, kern_ms):
     fractions of the dtype's dense MFMA peak; the dominant (longest) kernel
     and its algorithmic rate.  Algorithmic FLOPs are credited without double
     counting the recomputed products: the dQ pass gets the G_Q product only,
-    the dK/dV pass the recomputed scores, dP, G_V and G_K."""
+    the dK/dV pass the recomputed scores, dP, G_V and G_K.  With the score
+    gradients kept, the per-row pass has no products and the dQ product
+    from the stored gradients is credited 2 d_h per pair."""
     peak = PEAK_TFLOPS[wl.dtype]
     P, dh, dv_ = work["pairs"], wl.d_h, wl.d_v
-    alg = {"fwd": 2 * P * (dh + dv_), "bwd_dq": 2 * P * dh, "bwd_dkdv": 2 * P * (2 * dh + 2 * dv_)}
-    executed = {"fwd": 2 * P * (dh + dv_), "bwd_dq": 2 * P * (2 * dh + dv_), "bwd_dkdv": 2 * P * (2 * dh + 2 * dv_)}
+    alg = {"fwd": 2 * P * (dh + dv_), "bwd_dq": 2 * P * dh, "bwd_dkdv": 2 * P * (2 * dh + 2 * dv_),
+           "bwd_rows": 0, "bwd_dq_gs": 2 * P * dh}
+    executed = {"fwd": 2 * P * (dh + dv_), "bwd_dq": 2 * P * (2 * dh + dv_), "bwd_dkdv": 2 * P * (2 * dh + 2 * dv_),
+                "bwd_rows": 0, "bwd_dq_gs": 2 * P * dh}
     kernels = {}
     for n, t in kern_ms.items():
         sec = t * 1e-3
@@ -136,9 +142,13 @@ def kernel_report(wl, work, kern_ms):
     return kernels, dominant, alg[dominant] / (kern_ms[dominant] * 1e-3) / 1e12
 
 
-def measure(torch, attn, W, wl, uniform_len, steps, warmup, packed=False):
-    """Time `steps` steps (forward, dQ pass, dK/dV pass) of one workload with
-    its inputs resident; returns (inputs, work, ms per step, ms per kernel, device).
+def measure(torch, attn, W, wl, uniform_len, steps, warmup, packed=False, keep_gs=True):
+    """Time `steps` steps (forward, then the backward) of one workload with
+    its inputs resident; returns (inputs, work, ms per step, ms per kernel,
+    device, forward split?, score gradients kept?).  The backward keeps the
+    score gradients G_S (per-row pass, dK/dV pass storing G_S, dQ product)
+    where the library supports it and ``keep_gs`` is set, else it runs the
+    dQ pass and the dK/dV pass, both recomputing S and dP.
     With ``packed`` the same sequences are stored one after another without
     padding rows ([rows, H, d] tensors and row offsets): same visible pairs."""
     import numpy as np
@@ -172,16 +182,22 @@ def measure(torch, attn, W, wl, uniform_len, steps, warmup, packed=False):
         o = torch.empty(wl.B, wl.H_q, wl.n_q, wl.d_v, dtype=q.dtype, device=q.device)
         lse = torch.empty(wl.B, wl.H_q, wl.n_q, dtype=torch.float32, device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    prob = attn.make_problem(wl.B, wl.H_q, wl.H_kv, wl.n_q, wl.n_k, wl.d_h, wl.d_v,
-                             attn.BF16 if wl.dtype == W.BF16 else attn.F32)
-    ws = torch.empty(attn.workspace_size(prob), dtype=torch.uint8, device=q.device)
-    staged = attn.StagedBackward(q, k, v, o, lse, do, dq, dk, dv, ws, **kw)
-    stream = torch.cuda.current_stream()
-    names = ("fwd", "bwd_dq", "bwd_dkdv")
-    # the forward split over the keys where the library's automatic part
-    # count divides it (few query rows per KV head against long key ranges)
     pf = attn._problem_from(q, k, v, attn._strides(o), kw.get("cu_seqlens_q"), kw.get("cu_seqlens_k"),
                             kw.get("max_seqlen_q"), kw.get("max_seqlen_k"))
+    gs = keep_gs and attn.gs_workspace_size(pf) > attn.workspace_size(pf)
+    need = attn.gs_workspace_size(pf) if gs else attn.workspace_size(pf)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    staged = attn.StagedBackward(q, k, v, o, lse, do, dq, dk, dv, ws, **kw)
+    stream = torch.cuda.current_stream()
+    if gs:
+        names = ("fwd", "bwd_rows", "bwd_dkdv", "bwd_dq_gs")
+        backward = [lambda: staged.gs_stage(0, stream), lambda: staged.gs_stage(1, stream),
+                    lambda: staged.gs_stage(2, stream)]
+    else:
+        names = ("fwd", "bwd_dq", "bwd_dkdv")
+        backward = [lambda: staged.dq(stream), lambda: staged.dkdv(stream)]
+    # the forward split over the keys where the library's automatic part
+    # count divides it (few query rows per KV head against long key ranges)
     split_fwd = attn.splitkv_workspace_size(pf, 0) > attn.splitkv_workspace_size(pf, 1)
     ws_f = torch.empty(max(attn.splitkv_workspace_size(pf, 0), 1), dtype=torch.uint8, device=q.device) \
         if split_fwd else None
@@ -198,12 +214,10 @@ def measure(torch, attn, W, wl, uniform_len, steps, warmup, packed=False):
         forward()
         if events is not None:
             events[1].record(stream)
-        staged.dq(stream)
-        if events is not None:
-            events[2].record(stream)
-        staged.dkdv(stream)
-        if events is not None:
-            events[3].record(stream)
+        for j, run in enumerate(backward):
+            run()
+            if events is not None:
+                events[j + 2].record(stream)
 
     for _ in range(warmup):
         step()
@@ -218,9 +232,9 @@ def measure(torch, attn, W, wl, uniform_len, steps, warmup, packed=False):
     ms_per_step = (t1 - t0) * 1e3 / steps
     kern_ms = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps for j, n in enumerate(names)}
     device = q.device
-    del q, k, v, do, o, lse, dq, dk, dv, ws, staged, ws_f
+    del q, k, v, do, o, lse, dq, dk, dv, ws, staged, ws_f, backward
     torch.cuda.synchronize()
-    return inp, work, ms_per_step, kern_ms, device, split_fwd
+    return inp, work, ms_per_step, kern_ms, device, split_fwd, gs
 
 
 def measure_forward_split(torch, attn, W, wl, steps, warmup):
@@ -401,6 +415,9 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="time only the selected workload (default: also every other configuration, briefly)")
+    ap.add_argument("--two-pass", action="store_true",
+                    help="run the backward as the dQ pass and the dK/dV pass (both recompute S and dP) "
+                         "instead of keeping the score gradients")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after timing, run a plain elementwise copy of this many MiB (3 launches) "
                          "so HBM byte counters can be scaled against a kernel of known traffic")
@@ -422,9 +439,9 @@ def main(argv=None):
         return 2
     attn.lib()  # fail loudly without the library
     wl = W.WORKLOADS[args.workload]
-    inp, work, ms_per_step, kern_ms, dev_of, split_fwd = measure(torch, attn, W, wl, args.uniform_len, args.steps,
-                                                                 args.warmup)
-    names = ("fwd", "bwd_dq", "bwd_dkdv")
+    inp, work, ms_per_step, kern_ms, dev_of, split_fwd, gs = measure(torch, attn, W, wl, args.uniform_len,
+                                                                     args.steps, args.warmup,
+                                                                     keep_gs=not args.two_pass)
 
     flop = work["fwd_flop"] + work["bwd_flop"]
     value = flop / (ms_per_step * 1e-3) / 1e12
@@ -458,6 +475,7 @@ def main(argv=None):
         },
         "kernels": kernels,
         "forward": "split over keys" if split_fwd else "unsplit",
+        "backward": BACKWARD_KIND[gs],
         "roofline": roof,
         "cpu_baseline": None,
     }
@@ -481,7 +499,8 @@ def main(argv=None):
                               (W.WORKLOADS[3], None, True)]:
             if owl.wid == args.workload and ulen == args.uniform_len and not pk:
                 continue
-            _, ow, oms, okern, _, osplit = measure(torch, attn, W, owl, ulen, 10, 3, packed=pk)
+            _, ow, oms, okern, _, osplit, ogs = measure(torch, attn, W, owl, ulen, 10, 3, packed=pk,
+                                                        keep_gs=not args.two_pass)
             oflop = ow["fwd_flop"] + ow["bwd_flop"]
             ov = oflop / (oms * 1e-3) / 1e12
             label = owl.name + (f"_uniform{ulen}" if ulen else "") + ("_packed" if pk else "")
@@ -494,7 +513,7 @@ def main(argv=None):
                                         "peak": PEAK_TFLOPS[owl.dtype], "unit": "TFLOP/s",
                                         "frac": round(oach / PEAK_TFLOPS[owl.dtype], 4)},
                            "forward": "split over keys" if osplit else "unsplit",
-                           "steps": 10, "warmup": 3})
+                           "backward": BACKWARD_KIND[ogs], "steps": 10, "warmup": 3})
         result["other_workloads"] = others
         # forward only, split over the keys, where few query rows meet a long key range
         fsplit = []

@@ -34,7 +34,8 @@ F32 = 0
 BF16 = 1
 
 # every symbol the header declares
-EXPORTS = ("attn_validate", "attn_bwd_workspace_size", "attn_fwd", "attn_bwd", "attn_bwd_noalloc",
+EXPORTS = ("attn_validate", "attn_bwd_workspace_size", "attn_fwd", "attn_bwd", "attn_bwd_gs_workspace_size",
+           "attn_bwd_gs", "attn_bwd_gs_stage", "attn_bwd_noalloc",
            "attn_bwd_dq", "attn_bwd_dkdv", "attn_fwd_splitkv_workspace_size", "attn_fwd_splitkv",
            "attn_rope_apply", "attn_fwd_rope_workspace_size", "attn_fwd_rope",
            "attn_bwd_rope_workspace_size", "attn_bwd_rope", "attn_gemm_create", "attn_gemm_destroy",
@@ -104,6 +105,12 @@ def lib():
     L.attn_fwd.restype = ctypes.c_int
     L.attn_bwd.argtypes = [P, M, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.attn_bwd.restype = ctypes.c_int
+    L.attn_bwd_gs_workspace_size.argtypes = [P]
+    L.attn_bwd_gs_workspace_size.restype = ctypes.c_size_t
+    L.attn_bwd_gs.argtypes = [P, M, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.attn_bwd_gs.restype = ctypes.c_int
+    L.attn_bwd_gs_stage.argtypes = [P, M, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, ctypes.c_int32, vp]
+    L.attn_bwd_gs_stage.restype = ctypes.c_int
     L.attn_bwd_noalloc.argtypes = [P, M, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.attn_bwd_noalloc.restype = ctypes.c_int
     L.attn_bwd_dq.argtypes = [P, M, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
@@ -221,6 +228,10 @@ def validate(prob: Problem, mask: Mask) -> int:
 
 def workspace_size(prob: Problem) -> int:
     return int(lib().attn_bwd_workspace_size(ctypes.byref(prob)))
+
+
+def gs_workspace_size(prob: Problem) -> int:
+    return int(lib().attn_bwd_gs_workspace_size(ctypes.byref(prob)))
 
 
 # ---------------------------------------------------------------------------
@@ -373,9 +384,11 @@ def fwd_splitkv(q, k, v, *, num_splits=0, causal=False, offset=0, seqlens_q=None
 
 def bwd(q, k, v, o, lse, do, *, causal=False, offset=0, seqlens_q=None, seqlens_k=None,
         dq=None, dk=None, dv=None, workspace=None, stream=None, cu_seqlens_q=None, cu_seqlens_k=None,
-        max_seqlen_q=None, max_seqlen_k=None):
+        max_seqlen_q=None, max_seqlen_k=None, keep_gs=False):
     """G_Q, G_K, G_V.  ``do`` must have the strides of ``o``; outputs are
-    allocated contiguous unless given (then with the strides of q / k / v)."""
+    allocated contiguous unless given (then with the strides of q / k / v).
+    ``keep_gs`` calls attn_bwd_gs (G_S kept in the workspace) instead of
+    attn_bwd."""
     torch = _torch()
     nd = 3 if (cu_seqlens_q is not None or cu_seqlens_k is not None) else 4
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
@@ -395,16 +408,17 @@ def bwd(q, k, v, o, lse, do, *, causal=False, offset=0, seqlens_q=None, seqlens_
         if dv.stride() != v.stride():
             raise ValueError("v must be contiguous when dv is not given")
     prob = _problem_from(q, k, v, _strides(o), cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
-    need = workspace_size(prob)
+    need = gs_workspace_size(prob) if keep_gs else workspace_size(prob)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     mask, keep = make_mask(causal, offset, seqlens_q, seqlens_k)
-    st = lib().attn_bwd(ctypes.byref(prob), ctypes.byref(mask), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
-                        _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
-                        ctypes.c_size_t(workspace.numel()), _stream(stream))
+    fn = lib().attn_bwd_gs if keep_gs else lib().attn_bwd
+    st = fn(ctypes.byref(prob), ctypes.byref(mask), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+            _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+            ctypes.c_size_t(workspace.numel()), _stream(stream))
     del keep
     if st != OK:
-        raise AttnError(st, "attn_bwd")
+        raise AttnError(st, "attn_bwd_gs" if keep_gs else "attn_bwd")
     return dq, dk, dv
 
 
@@ -468,6 +482,15 @@ class StagedBackward:
         self._check(lib().attn_bwd_dkdv(ctypes.byref(self.prob), ctypes.byref(self.mask), _ptr(q),
                                         _ptr(k), _ptr(v), _ptr(lse), _ptr(do), _ptr(dk), _ptr(dv),
                                         self.ws, self.ws_bytes, _stream(stream)), "attn_bwd_dkdv")
+
+    def gs_stage(self, stage, stream=None):
+        """Stage 0, 1 or 2 of attn_bwd_gs (the workspace must hold
+        gs_workspace_size bytes)."""
+        q, k, v, o, lse, do, dq, dk, dv, ws = self.t
+        self._check(lib().attn_bwd_gs_stage(ctypes.byref(self.prob), ctypes.byref(self.mask), _ptr(q), _ptr(k),
+                                            _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
+                                            self.ws, self.ws_bytes, ctypes.c_int32(stage), _stream(stream)),
+                    "attn_bwd_gs_stage")
 
 
 # ---------------------------------------------------------------------------

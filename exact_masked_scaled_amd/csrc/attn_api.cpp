@@ -126,11 +126,16 @@ int chunk_size(const KernelParams& kp, int B) {
 // size and the call agree; not used with rotary positions.
 struct BwdPlan {
   int32_t dq_splits = 1, hsplits = 1;
+  // G_S kept (attn_bwd_gs): one 4 KB block per (sequence, query head,
+  // 32-row block, 128-key block, 64-key half)
+  bool gs = false;
+  int32_t gs_nqb = 0, gs_nkb = 0;
+  size_t gs_bytes = 0;
   int64_t q_rows = 0, k_rows = 0;      // rows of lse / D, and of the key partials
   size_t row_bytes = 0;                 // one float per row of lse: the -D array, then the lse2 array
   size_t d_bytes = 0, dq_bytes = 0, kv_bytes = 0;
 };
-BwdPlan bwd_plan(const attn_problem& p, bool rope) {
+BwdPlan bwd_plan(const attn_problem& p, bool rope, bool keep_gs = false) {
   BwdPlan pl;
   const bool packed = p.cu_seqlens_q != nullptr;
   pl.q_rows = packed ? (int64_t)p.H_q * std::max(p.cu_seqlens_q[p.B], 0) : (int64_t)p.B * p.H_q * p.n_q;
@@ -150,6 +155,17 @@ BwdPlan bwd_plan(const attn_problem& p, bool rope) {
   if (pl.dq_splits > 1) pl.dq_bytes = align_up((size_t)pl.dq_splits * pl.q_rows * p.d_h * sizeof(float), kWsAlign);
   if (pl.hsplits > 1)
     pl.kv_bytes = align_up((size_t)pl.hsplits * pl.k_rows * (p.d_h + p.d_v) * sizeof(float), kWsAlign);
+  // G_S kept: bf16 grids that need no division (the divided passes stay two-pass)
+  // (the product pass addresses a sequence's K rows with 32-bit offsets)
+  const bool k_fits = p.k_stride[2] >= 0 &&
+                      (p.n_k - 1) * (int64_t)p.k_stride[2] * 2 + (int64_t)p.d_h * 2 <= (int64_t)0xffffffff;
+  if (keep_gs && p.dtype == ATTN_BF16 && pl.dq_splits == 1 && pl.hsplits == 1 && p.n_q > 0 && p.n_k > 0 &&
+      (p.d_h == 64 || p.d_h == 128) && (p.d_v == 64 || p.d_v == 128) && k_fits) {
+    pl.gs = true;
+    pl.gs_nqb = (int32_t)((p.n_q + 31) / 32);
+    pl.gs_nkb = (int32_t)((p.n_k + 127) / 128);
+    pl.gs_bytes = align_up((size_t)p.B * p.H_q * pl.gs_nqb * pl.gs_nkb * 8192, kWsAlign);
+  }
   return pl;
 }
 
@@ -168,6 +184,15 @@ size_t attn_bwd_workspace_size(const attn_problem* prob) {
   if ((prob->cu_seqlens_q == nullptr) != (prob->cu_seqlens_k == nullptr)) return 0;
   const BwdPlan pl = bwd_plan(*prob, false);
   return pl.d_bytes + pl.dq_bytes + pl.kv_bytes;
+}
+
+size_t attn_bwd_gs_workspace_size(const attn_problem* prob) {
+  if (prob == nullptr || prob->B < 0 || prob->H_q < 0 || prob->H_kv < 0 || prob->n_q < 0 || prob->n_k < 0 ||
+      prob->d_h < 0 || prob->d_v < 0)
+    return 0;
+  if ((prob->cu_seqlens_q == nullptr) != (prob->cu_seqlens_k == nullptr)) return 0;
+  const BwdPlan pl = bwd_plan(*prob, false, true);
+  return pl.d_bytes + pl.dq_bytes + pl.kv_bytes + pl.gs_bytes;
 }
 
 attn_status attn_fwd(const attn_problem* prob, const attn_mask* mask, const void* Q, const void* K,
@@ -301,7 +326,7 @@ struct RopeCtx {
 // Checks of attn_bwd and its two passes: validate, then the pointers the
 // requested passes read or write and the workspace.
 attn_status bwd_check(const attn_problem* prob, const attn_mask* mask, const BwdPtrs& t, void* workspace,
-                      size_t workspace_bytes, int passes) {
+                      size_t workspace_bytes, int passes, bool keep_gs = false) {
   attn_status st = validate_problem(prob, mask);
   if (st != ATTN_OK) return st;
   const attn_problem& p = *prob;
@@ -316,7 +341,7 @@ attn_status bwd_check(const attn_problem* prob, const attn_mask* mask, const Bwd
   if (has_k && (passes & kDkdv) && !(ok(t.K) && ok(t.V) && ok(t.dK) && ok(t.dV)))
     return ATTN_ERR_INVALID_ARG;
   if (has_k && has_q && (passes & kDq) && !(ok(t.K) && ok(t.V))) return ATTN_ERR_INVALID_ARG;
-  const size_t need_ws = attn_bwd_workspace_size(prob);
+  const size_t need_ws = keep_gs ? attn_bwd_gs_workspace_size(prob) : attn_bwd_workspace_size(prob);
   if (need_ws > 0 &&
       (workspace == nullptr || workspace_bytes < need_ws || ((uintptr_t)workspace % kWsAlign) != 0))
     return ATTN_ERR_WORKSPACE;
@@ -325,7 +350,7 @@ attn_status bwd_check(const attn_problem* prob, const attn_mask* mask, const Bwd
 
 // Enqueue the requested passes per sequence chunk (arguments checked).
 attn_status bwd_enqueue(const attn_problem& p, const attn_mask& m, const BwdPtrs& t, float* delta, void* stream,
-                        int passes, const RopeCtx* rc) {
+                        int passes, const RopeCtx* rc, bool keep_gs = false, int stage = -1) {
   if (p.B == 0 || (p.n_q == 0 && p.n_k == 0)) return ATTN_OK;
   const bool has_q = p.n_q > 0, has_k = p.n_k > 0;
   const size_t es = esize(p.dtype);
@@ -345,9 +370,10 @@ attn_status bwd_enqueue(const attn_problem& p, const attn_mask& m, const BwdPtrs
   const int nqblk = (p.n_q + bwd_dq_block_rows(p.dtype) - 1) / bwd_dq_block_rows(p.dtype);
   const int nkblk = (p.n_k + bwd_dkdv_block_keys(p.dtype) - 1) / bwd_dkdv_block_keys(p.dtype);
   // workspace: -D, lse2, then the partials of divided passes
-  const BwdPlan pl = bwd_plan(p, rc != nullptr);
+  const BwdPlan pl = bwd_plan(p, rc != nullptr, keep_gs && passes == (kDq | kDkdv));
   float* part_q = delta ? (float*)((char*)delta + pl.d_bytes) : nullptr;
   float* part_kv = delta ? (float*)((char*)delta + pl.d_bytes + pl.dq_bytes) : nullptr;
+  void* gs_buf = delta && pl.gs ? (void*)((char*)delta + pl.d_bytes + pl.dq_bytes + pl.kv_bytes) : nullptr;
   kp.splits = pl.dq_splits;
   kp.part_rows = pl.q_rows;
   kp.hsplits = pl.hsplits;
@@ -373,6 +399,31 @@ attn_status bwd_enqueue(const attn_problem& p, const attn_mask& m, const BwdPtrs
       kp.part_dk = part_kv + b0 * kp.krow_sb * p.d_h;
       kp.part_dv = part_kv + (int64_t)pl.hsplits * pl.k_rows * p.d_h + b0 * kp.krow_sb * p.d_v;
     }
+    if (pl.gs) {
+      // -D and lse log2 e first (stage 0), then the dK/dV pass writing G_S
+      // (stage 1), then G_Q from it (stage 2); the chunk's G_S blocks start
+      // at its first sequence's
+      const int rqblk = (p.n_q + bwd_gs_block_rows() - 1) / bwd_gs_block_rows();
+      kp.gs = (char*)gs_buf + (size_t)b0 * p.H_q * pl.gs_nqb * pl.gs_nkb * 8192;
+      kp.gs_nqb = pl.gs_nqb;
+      kp.gs_nkb = pl.gs_nkb;
+      if (stage < 0 || stage == 0) {
+        KernelParams kr = kp;
+        kr.gs = nullptr;
+        kr.per_group = kr.group * rqblk;
+        if (launch_bwd_rows(kr, p.d_v, stream) != 0) return ATTN_ERR_HIP;
+      }
+      if (stage < 0 || stage == 1) {
+        kp.per_group = nkblk;
+        if (launch_bwd_dkdv(kp, p.dtype, p.d_h, p.d_v, stream) != 0) return ATTN_ERR_HIP;
+      }
+      if (stage < 0 || stage == 2) {
+        kp.per_group = (int32_t)bwd_dq_gs_items(p.n_q, kp.group);
+        if (launch_bwd_dq_gs(kp, p.d_h, stream) != 0) return ATTN_ERR_HIP;
+      }
+      kp.gs = nullptr;
+      continue;
+    }
     if ((passes & kDq) && has_q) {
       kp.per_group = kp.group * nqblk * pl.dq_splits;
       if (rc) {  // the dQ pass reads the caller's Q, turns it as it loads it and writes q~
@@ -396,10 +447,10 @@ attn_status bwd_enqueue(const attn_problem& p, const attn_mask& m, const BwdPtrs
 }
 
 attn_status bwd_passes(const attn_problem* prob, const attn_mask* mask, const BwdPtrs& t, void* workspace,
-                       size_t workspace_bytes, void* stream, int passes) {
-  const attn_status st = bwd_check(prob, mask, t, workspace, workspace_bytes, passes);
+                       size_t workspace_bytes, void* stream, int passes, bool keep_gs = false, int stage = -1) {
+  const attn_status st = bwd_check(prob, mask, t, workspace, workspace_bytes, passes, keep_gs);
   if (st != ATTN_OK) return st;
-  return bwd_enqueue(*prob, *mask, t, (float*)workspace, stream, passes, nullptr);
+  return bwd_enqueue(*prob, *mask, t, (float*)workspace, stream, passes, nullptr, keep_gs, stage);
 }
 
 }  // namespace
@@ -411,6 +462,29 @@ attn_status attn_bwd(const attn_problem* prob, const attn_mask* mask, const void
                      void* dV, void* workspace, size_t workspace_bytes, void* stream) {
   const BwdPtrs t{Q, K, V, O, dO, lse, dQ, dK, dV};
   return bwd_passes(prob, mask, t, workspace, workspace_bytes, stream, kDq | kDkdv);
+}
+
+attn_status attn_bwd_gs(const attn_problem* prob, const attn_mask* mask, const void* Q, const void* K,
+                        const void* V, const void* O, const float* lse, const void* dO, void* dQ, void* dK,
+                        void* dV, void* workspace, size_t workspace_bytes, void* stream) {
+  const BwdPtrs t{Q, K, V, O, dO, lse, dQ, dK, dV};
+  return bwd_passes(prob, mask, t, workspace, workspace_bytes, stream, kDq | kDkdv, true);
+}
+
+attn_status attn_bwd_gs_stage(const attn_problem* prob, const attn_mask* mask, const void* Q, const void* K,
+                              const void* V, const void* O, const float* lse, const void* dO, void* dQ, void* dK,
+                              void* dV, void* workspace, size_t workspace_bytes, int32_t stage, void* stream) {
+  if (stage < 0 || stage > 2) return ATTN_ERR_INVALID_ARG;
+  const BwdPtrs t{Q, K, V, O, dO, lse, dQ, dK, dV};
+  if (attn_bwd_gs_workspace_size(prob) > attn_bwd_workspace_size(prob)) {
+    return bwd_passes(prob, mask, t, workspace, workspace_bytes, stream, kDq | kDkdv, true, stage);
+  }
+  // the two-pass backward: its dQ pass (with D) as stage 0, its dK/dV pass as stage 1
+  if (stage == 2) {
+    const attn_status st = validate_problem(prob, mask);
+    return st;
+  }
+  return bwd_passes(prob, mask, t, workspace, workspace_bytes, stream, stage == 0 ? kDq : kDkdv);
 }
 
 attn_status attn_bwd_dq(const attn_problem* prob, const attn_mask* mask, const void* Q, const void* K,

@@ -37,12 +37,6 @@
 
 namespace attn {
 
-
-
-__device__ __forceinline__ int key_limit_b(int i, int Lk, int causal, int off) {
-  return causal ? min(Lk, i + off + 1) : Lk;
-}
-
 // ============================================================== dQ pass
 template <typename T, int DH, int DV>
 struct DqCfg {

@@ -64,11 +64,12 @@ struct DkvQuadCfg {
 // BUF: Q / G_O blocks of 32 rows span less than 4 GiB, so the ring copies are
 // buffer loads from one resource per block (below).  Separate instances keep
 // the other paths' registers out of each kernel.
-template <typename T, int DH, int DV, bool HSPLIT, bool ROPE, bool BUF>
+template <typename T, int DH, int DV, bool HSPLIT, bool ROPE, bool BUF, bool GS>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParams p) {
   static_assert(sizeof(T) == 2, "four-role dK/dV pass is the bf16 path");
   using C = DkvQuadCfg<T, DH, DV>;
   using op_t = typename Op<T>::type;
+  using gop_t = __attribute__((address_space(1))) op_t;
   constexpr int NS = C::NS, PD = C::PD;
   // one __shared__ array per ring stage (Q tile, G_O tile, lse/D rows),
   // selected at compile time so reads need not wait for unrelated copies
@@ -342,7 +343,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
     };
     // ---- XD: dP of one step (both key blocks share each G_O operand read)
     // interleaved with G_S of an earlier step (P from XS)
-    auto xd_iter = [&](auto MF, auto EX, auto J, const T* Os, const float* rows, const op_t* xpb, op_t* xb) __attribute__((always_inline)) {
+    auto xd_iter = [&](auto MF, auto EX, auto J, const T* Os, const float* rows, const op_t* xpb, op_t* xb, gop_t* gsb) __attribute__((always_inline)) {
       constexpr bool mf = decltype(MF)::value, ex = decltype(EX)::value;
       constexpr int jn = decltype(J)::value, jo = jn ^ 1;
       f32x16& d0 = R[XB + 2 * jn];
@@ -407,6 +408,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
           }
         }
         __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (GS && ex) {
+        // G_S kept for the dQ product: the block just handed on, read back
+        // transposed (lane = query row, eight keys per operand) and written
+        // as the product's four B operands, 16 bytes per lane each
+        const __bf16* blk = reinterpret_cast<const __bf16*>(xo);
+        const int goff = gs_lane_offset(lane);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int st = 0; st < 2; ++st) gsb[(mt * 2 + st) * 64 + lane] = gs_read(blk, mt * 2048 + st * 256 + goff);
       }
     };
     // ---- YV / YK: accumulate step s - 3 (each transposed read feeds both key
@@ -478,6 +490,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
 
     int i_rr = rr_lo, i_qb = qb_first;   // next step to copy
     int xs_qb = qb_first;            // query block of the step XS exponentiates next
+    // G_S kept: the step XD forms G_S of next, and this (sequence, KV head,
+    // key block, half)'s blocks (one per query head and 32-row block)
+    int xd_rr = rr_lo, xd_qb = qb_first;
+    gop_t* const gs_kh = GS ? (gop_t*)p.gs +
+                                  ((size_t)(b * p.H_kv + g) * p.group * p.gs_nqb * p.gs_nkb + kb) * 512 + h * 256
+                            : nullptr;
     // after a copy: move on to the next step while one is left (past the last
     // step the copies repeat it, into stages no later step reads)
     auto next = [&](int s_copied, int& rr, int& qb) __attribute__((always_inline)) {
@@ -528,7 +546,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
         }
         if (ex) { if (++xs_qb == qb_end) xs_qb = qb_first; }
       } else {
-        stage_barrier<0>();
+        // with G_S kept, XD's barrier leaves its block stores in flight (it
+        // issues no other memory access in the loop)
+        stage_barrier<GS ? 63 : 0>();
         // XD: dP(s - 1) into parity (s - 1) & 1, G_S(s - 2) -> G_S slot 3 + (s - 2) % 2
         constexpr int jd = (u + 1) & 1;
         const T* Os = o_st(IC<u + NS - 1>());
@@ -536,10 +556,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
         const op_t* pin = xch + ((u + 1) % 3) * XSLOT;  // P(s - 2)
         op_t* xw = xch + (3 + (u & 1)) * XSLOT;         // G_S(s - 2)
         const bool mf = !ramp || (s >= 1 && s <= nsteps), ex = !ramp || (s >= 2 && s <= nsteps + 1);
-        if (mf && ex) xd_iter(TR(), TR(), IC<jd>(), Os, rows, pin, xw);
+        gop_t* gsb = nullptr;
+        if constexpr (GS) gsb = gs_kh + ((size_t)xd_rr * p.gs_nqb + xd_qb) * p.gs_nkb * 512;
+        if (mf && ex) xd_iter(TR(), TR(), IC<jd>(), Os, rows, pin, xw, gsb);
         else if constexpr (ramp) {
-          if (ex) xd_iter(F(), TR(), IC<jd>(), Os, rows, pin, xw);
-          else if (mf) xd_iter(TR(), F(), IC<jd>(), Os, rows, pin, xw);
+          if (ex) xd_iter(F(), TR(), IC<jd>(), Os, rows, pin, xw, gsb);
+          else if (mf) xd_iter(TR(), F(), IC<jd>(), Os, rows, pin, xw, gsb);
+        }
+        if constexpr (GS) {
+          if (ex) { if (++xd_qb == qb_end) { xd_qb = qb_first; ++xd_rr; } }
         }
       }
     };
@@ -679,13 +704,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
 template <typename T, int DH, int DV, bool BUF>
 static void launch_quad(const KernelParams& p, int64_t grid, void* stream) {
   if (p.hsplits > 1)
-    hipLaunchKernelGGL((bwd_dkdv_quad_kernel<T, DH, DV, true, false, BUF>), dim3((unsigned)grid), dim3(512), 0,
+    hipLaunchKernelGGL((bwd_dkdv_quad_kernel<T, DH, DV, true, false, BUF, false>), dim3((unsigned)grid), dim3(512), 0,
                        (hipStream_t)stream, p);
   else if (p.rope & kRopeDK)
-    hipLaunchKernelGGL((bwd_dkdv_quad_kernel<T, DH, DV, false, true, BUF>), dim3((unsigned)grid), dim3(512), 0,
+    hipLaunchKernelGGL((bwd_dkdv_quad_kernel<T, DH, DV, false, true, BUF, false>), dim3((unsigned)grid), dim3(512), 0,
+                       (hipStream_t)stream, p);
+  else if (p.gs != nullptr)
+    hipLaunchKernelGGL((bwd_dkdv_quad_kernel<T, DH, DV, false, false, BUF, true>), dim3((unsigned)grid), dim3(512), 0,
                        (hipStream_t)stream, p);
   else
-    hipLaunchKernelGGL((bwd_dkdv_quad_kernel<T, DH, DV, false, false, BUF>), dim3((unsigned)grid), dim3(512), 0,
+    hipLaunchKernelGGL((bwd_dkdv_quad_kernel<T, DH, DV, false, false, BUF, false>), dim3((unsigned)grid), dim3(512), 0,
                        (hipStream_t)stream, p);
 }
 

@@ -177,6 +177,30 @@ __device__ __forceinline__ typename Op<T>::type ld_tr(const T* X, int kb, int nb
   }
 }
 
+// Lane byte offset, inside one 4 KB G_S block, of the transposed read that
+// gives the G_Q product its B operand (lane = query row, eight keys in C
+// order) for 32-key slice mt and 16-key step st: add mt * 2048 + st * 256,
+// and 128 for the second four keys.  The block holds, at 16-byte chunk
+// (kb2 * 2 + st') * 64 + kg' * 32 + k', the eight rows 16 st' + 8 (e / 4) +
+// 4 kg' + e % 4 (e = 0..7) of key 32 kb2 + k' (the XD waves' operand layout),
+// so four consecutive rows of one key are one 8-byte word, which is what
+// ds_read_b64_tr_b16 transposes (source lane s of a 16-lane group reads key
+// (s / 4) of its group's four and rows 4 (s % 4) .. + 3).
+__device__ __forceinline__ int gs_lane_offset(int lane) {
+  const int s = lane & 15, grp = lane >> 4;
+  return (((grp & 1) * 64 + (s & 1) * 32 + 4 * (grp >> 1) + (s >> 2)) * 16 + 8 * ((s >> 1) & 1));
+}
+
+__device__ __forceinline__ bf16x8 gs_read(const __bf16* blk, int off) {
+  const char* base = reinterpret_cast<const char*>(blk);
+  i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4*)(base + off));
+  i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4*)(base + off + 128));
+  union { i16x4 v[2]; bf16x8 b; } u;
+  u.v[0] = lo;
+  u.v[1] = hi;
+  return u.b;
+}
+
 // ---------------------------------------------------------------- precomputed LDS offsets
 // The swizzle of a tile depends on the row only through row % 16, and every
 // read pattern below starts at a multiple of 16 rows, so a lane's byte
@@ -458,6 +482,12 @@ __device__ __forceinline__ SeqView seq_view(const KernelParams& p, int b) {
   s.q_row0 = p.varlen ? p.row0_q[b] : 0;
   s.k_row0 = p.varlen ? p.row0_k[b] : 0;
   return s;
+}
+// Keys [0, key_limit_b) of a sequence are visible to query row i: all L_k
+// keys, or with the causal rule those at j <= i + off (off the sequence's
+// clamped causal offset).
+__device__ __forceinline__ int key_limit_b(int i, int Lk, int causal, int off) {
+  return causal ? min(Lk, i + off + 1) : Lk;
 }
 
 __device__ __forceinline__ bool map_work(int wg, int groups, int per_group, int xcd_map,

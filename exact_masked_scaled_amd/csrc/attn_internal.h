@@ -74,6 +74,16 @@ struct KernelParams {
   // (the dK/dV pass's copy of q~), with its element strides
   void* qt;
   int64_t qt_sb, qt_sh, qt_sr;
+  // backward keeping G_S (bf16): the dK/dV pass writes each step's G_S as
+  // 4 KB blocks, block ((((b * H_kv + g) * group + rr) * gs_nqb + qb) * gs_nkb
+  // + kb) * 2 + half for query head rr of the group, 32-row block qb, 128-key
+  // block kb and its 64-key half; the dQ pass then reads them instead of
+  // recomputing S and dP.  Null when not used.
+  void* gs;
+  int32_t gs_nqb, gs_nkb;
+  // dQ pass mode: 0 the full pass (D, S, dP, G_S, G_Q), 1 only the per-row
+  // -D and lse log2 e, 2 G_Q from the kept G_S blocks
+  int32_t dq_mode;
   int32_t lens_q[kMaxBatchChunk];
   int32_t lens_k[kMaxBatchChunk];
   int32_t offs[kMaxBatchChunk];    // causal offsets, clamped to [0, n_k]
@@ -119,6 +129,14 @@ int launch_bwd_dq(const KernelParams& p, int dtype, int d_h, int d_v, void* stre
 int launch_bwd_dkdv(const KernelParams& p, int dtype, int d_h, int d_v, void* stream);
 // bf16 dK/dV pass by the four-role kernel (attn_bwd_quad.hip)
 int launch_bwd_dkdv_quad(const KernelParams& p, int d_h, int d_v, void* stream);
+// backward with G_S kept (bf16): the per-row pass (-D, lse log2 e) and G_Q
+// from the kept blocks; both use the dQ pass's grid (bwd_gs_block_rows rows
+// per workgroup)
+int launch_bwd_rows(const KernelParams& p, int d_v, void* stream);
+int launch_bwd_dq_gs(const KernelParams& p, int d_h, void* stream);
+int bwd_gs_block_rows();
+// workgroups of the G_Q product per (sequence, KV head)
+int64_t bwd_dq_gs_items(int n_q, int group);
 int launch_dkdv_combine(const KernelParams& p, int dtype, int d_h, int d_v, void* stream);
 // forward split over the keys (p.splits > 1): partial pass, then the merge
 int launch_fwd_split(const KernelParams& p, int dtype, int d_h, int d_v, void* stream);

@@ -53,14 +53,19 @@ PASSES = {
     "wait": (["--pmc", "SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY",
               "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "GRBM_GUI_ACTIVE"], BENCH_ARGS_PMC),
 }
-# the three kernels of a step, by the names bench.py reports them under
-KERNELS = {"fwd_kernel": "fwd", "bwd_dq_kernel": "bwd_dq", "bwd_dkdv_quad_kernel": "bwd_dkdv"}
+# the kernels of a step, by the names bench.py reports them under (the
+# two-pass backward's dQ pass, or with G_S kept the per-row pass and the G_Q
+# product)
+KERNELS = {"fwd_kernel": "fwd", "bwd_dq_kernel": "bwd_dq", "bwd_rows_kernel": "bwd_rows",
+           "bwd_dkdv_quad_kernel": "bwd_dkdv", "bwd_dq_gs_kernel": "bwd_dq_gs"}
 SIMDS, XCDS = 1024, 8  # MI355X: 256 CUs x 4 SIMDs, 8 XCDs
 WORKLOAD = "causal GQA bf16, B=8 H_q=32 H_kv=8 n=4096 d=128, padded lengths (seed 1003)"
 
 
-def short_name(mangled: str):
-    m = re.match(r"_ZN4attn\d+(\w+?)I", mangled)
+def short_name(name: str):
+    """The kernel's name without namespace and template arguments; the
+    profiler reports some names mangled and others demangled."""
+    m = re.match(r"_ZN4attn\d+(\w+?)I", name) or re.search(r"attn::(\w+)<", name)
     return m.group(1) if m else None
 
 
@@ -130,7 +135,8 @@ def credited_flops(bench: dict) -> dict:
     visible pairs only; the dQ pass gets the G_Q product alone."""
     P = bench["config"]["visible_pairs"]
     dh, dv = bench["config"]["d_h"], bench["config"]["d_v"]
-    return {"fwd": 2 * P * (dh + dv), "bwd_dq": 2 * P * dh, "bwd_dkdv": 2 * P * (2 * dh + 2 * dv)}
+    return {"fwd": 2 * P * (dh + dv), "bwd_dq": 2 * P * dh, "bwd_rows": 0, "bwd_dkdv": 2 * P * (2 * dh + 2 * dv),
+            "bwd_dq_gs": 2 * P * dh}
 
 
 def write_trace(raw: str, out: str, bench: dict):
@@ -146,7 +152,8 @@ def write_trace(raw: str, out: str, bench: dict):
          f"Per-dispatch durations from the kernel trace (`run_kernel_trace.csv`); the first {TRACE_WARMUP} dispatches of "
          f"each kernel are the benchmark's warm-up steps and are left out, so the {TRACE_STEPS} dispatches summarised are "
          "the steps the bench line times. Credited TFLOP/s counts visible (query, key) pairs only (forward 2(d_h + d_v), "
-         "dQ pass 2 d_h, dK/dV pass 2(2 d_h + 2 d_v) FLOP per pair) over the mean duration; fraction of the "
+         "dQ pass 2 d_h, dK/dV pass 2(2 d_h + 2 d_v), the dQ product from stored score gradients 2 d_h, the per-row "
+         "pass 0 FLOP per pair) over the mean duration; fraction of the "
          f"{peak:.0f} TFLOP/s dense bf16 peak.\n",
          "| kernel | timed dispatches | mean (us) | median (us) | min (us) | max (us) | credited TFLOP/s | frac of peak |",
          "|---|---|---|---|---|---|---|---|"]
@@ -165,8 +172,8 @@ def write_trace(raw: str, out: str, bench: dict):
     o.append("")
     dom = B.DOMINANT
     line = bench.get("roofline", {}).get("frac")
-    o.append(f"The same run's bench line (HIP events on the launch stream, {TRACE_STEPS} timed steps) reported fwd "
-             f"{k['fwd']['ms']:.3f} ms, bwd_dq {k['bwd_dq']['ms']:.3f} ms, bwd_dkdv {k['bwd_dkdv']['ms']:.3f} ms and "
+    o.append(f"The same run's bench line (HIP events on the launch stream, {TRACE_STEPS} timed steps) reported "
+             + ", ".join(f"{n} {v['ms']:.3f} ms" for n, v in k.items()) + " and "
              f"{bench['value']:.2f} TFLOP/s for the whole step under the profiler"
              + (f"; its roofline fraction for {dom} was {line:.4f}, the trace's {fr.get(dom, float('nan')):.4f}."
                 if line is not None else "."))
@@ -226,7 +233,8 @@ def write_mfma(raw: str, out: str, bench: dict):
     A, Wt = counters(raw, "mfma"), counters(raw, "wait")
     P = bench["config"]["visible_pairs"]
     dh, dv = bench["config"]["d_h"], bench["config"]["d_v"]
-    executed = {"fwd": 2 * P * (dh + dv), "bwd_dq": 2 * P * (2 * dh + dv), "bwd_dkdv": 2 * P * (2 * dh + 2 * dv)}
+    executed = {"fwd": 2 * P * (dh + dv), "bwd_dq": 2 * P * (2 * dh + dv), "bwd_rows": 0,
+                "bwd_dkdv": 2 * P * (2 * dh + 2 * dv), "bwd_dq_gs": 2 * P * dh}
     o = [f"# MFMA utilisation and wave-time breakdown: {WORKLOAD}\n",
          "Made by `python -m exact_masked_scaled_amd.rocprof_evidence --raw $RAW` (passes `mfma`, `wait`); the commands,",
          "from the repository root (`REPO=$PWD`, one MI355X; `RAW` the raw-output directory):\n", "```", command("mfma"), command("wait"), "```\n",
@@ -242,6 +250,8 @@ def write_mfma(raw: str, out: str, bench: dict):
         if k not in A:
             continue
         a = {c: mean(v) for c, v in A[k].items()}
+        if a["SQ_INSTS_MFMA"] == 0:  # the per-row pass has no products
+            continue
         act = a["GRBM_GUI_ACTIVE"] / XCDS
         busy = a["SQ_VALU_MFMA_BUSY_CYCLES"] / (act * SIMDS)
         co = a["SQ_VALU_MFMA_COEXEC_CYCLES"] / a["SQ_VALU_MFMA_BUSY_CYCLES"]
@@ -262,7 +272,7 @@ def write_mfma(raw: str, out: str, bench: dict):
                  f"{100 * w['SQ_WAIT_ANY'] / t:.1f}% | {100 * w['SQ_ACTIVE_INST_VALU'] / t:.1f}% | "
                  f"{100 * w['SQ_ACTIVE_INST_LDS'] / t:.1f}% |")
     o += ["", "Executed MFMA work per visible pair: forward 2(d_h + d_v), dQ pass 2(2d_h + d_v) (it recomputes S and dP), "
-          "dK/dV pass 2(2d_h + 2d_v) FLOP."]
+          "dK/dV pass 2(2d_h + 2d_v), dQ product from stored score gradients 2d_h FLOP (the per-row pass has none)."]
     with open(os.path.join(out, "mfma_utilisation_causal_gqa_b8_n4096.md"), "w") as f:
         f.write("\n".join(o) + "\n")
 

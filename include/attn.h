@@ -199,6 +199,41 @@ attn_status attn_bwd(const attn_problem* prob, const attn_mask* mask,
                      void* dQ, void* dK, void* dV,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* The same backward with G_S kept instead of recomputed: G_Q = G_S K /
+ * sqrt(d_h) ("Appendix A.10" eq. A.10.8) read from the G_S the dK/dV pass
+ * forms for G_K (eq. A.10.9), rather than from S and G_A formed a second
+ * time.  Three steps on `stream`: the per-row -D_i and lse_i * log2(e); the
+ * dK/dV pass, which also writes G_S in bf16 to the workspace (2 bytes per
+ * (row, key) of every 32-row block against every 128-key block it visits);
+ * G_Q as one product over those blocks.  Same arguments and results as
+ * attn_bwd up to rounding (G_Q sums the same bf16 G_S in the same key
+ * order; G_S itself may round differently from the two-pass dQ pass's).
+ * `workspace` must hold attn_bwd_gs_workspace_size(prob) bytes, 256-byte
+ * aligned: attn_bwd's, then the G_S blocks of the whole batch (B * H_q *
+ * ceil(n_q / 32) * ceil(n_k / 128) * 8 KB; 8.6 GB for B = 8, H_q = 32,
+ * n = 4096).  bf16 problems with d_h, d_v in {64, 128} whose grids need no
+ * division and whose K rows of one sequence span less than 4 GiB take this
+ * path; for any other problem the size is attn_bwd_workspace_size's and the
+ * call runs attn_bwd. */
+size_t attn_bwd_gs_workspace_size(const attn_problem* prob);
+attn_status attn_bwd_gs(const attn_problem* prob, const attn_mask* mask,
+                        const void* Q, const void* K, const void* V,
+                        const void* O, const float* lse, const void* dO,
+                        void* dQ, void* dK, void* dV,
+                        void* workspace, size_t workspace_bytes, void* stream);
+/* attn_bwd_gs one step at a time, for callers that time or schedule them
+ * apart: stage 0, 1, 2 in this order (on one stream, same arguments and
+ * workspace) equals one attn_bwd_gs call.  With G_S kept they are the
+ * per-row pass, the dK/dV pass and the G_Q product; otherwise stage 0 is
+ * attn_bwd_dq, stage 1 attn_bwd_dkdv and stage 2 does nothing.  Other stage
+ * values return ATTN_ERR_INVALID_ARG. */
+attn_status attn_bwd_gs_stage(const attn_problem* prob, const attn_mask* mask,
+                              const void* Q, const void* K, const void* V,
+                              const void* O, const float* lse, const void* dO,
+                              void* dQ, void* dK, void* dV,
+                              void* workspace, size_t workspace_bytes,
+                              int32_t stage, void* stream);
+
 /* For callers that cannot allocate (code under HIP graph capture, tight
  * serving loops, harnesses that forbid allocation): attn_bwd with its
  * workspace in a fixed device array of the library instead of a caller

@@ -48,10 +48,11 @@ def bench_forward_splits(prob) -> int:
     return 0 if A.splitkv_workspace_size(prob, 0) > A.splitkv_workspace_size(prob, 1) else 1
 
 
-def run_gpu(inp: W.Inputs, backward=True, poison_outputs=True, num_splits=1):
+def run_gpu(inp: W.Inputs, backward=True, poison_outputs=True, num_splits=1, keep_gs=False):
     """Forward (+ backward) on the GPU; returns device tensors.  num_splits 1
     runs attn_fwd; any other value runs attn_fwd_splitkv with that part count
-    (0: automatic, the benchmark's choice)."""
+    (0: automatic, the benchmark's choice).  keep_gs runs the backward as
+    attn_bwd_gs."""
     import torch
     wl = inp.wl
     q, k, v = to_device(inp.Q), to_device(inp.K), to_device(inp.V)
@@ -72,11 +73,12 @@ def run_gpu(inp: W.Inputs, backward=True, poison_outputs=True, num_splits=1):
         do = to_device(inp.GO)
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         prob = A._problem_from(q, k, v, A._strides(o))
-        ws = torch.empty(max(A.workspace_size(prob), 1), dtype=torch.uint8, device=q.device)
+        need = A.gs_workspace_size(prob) if keep_gs else A.workspace_size(prob)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
         if poison_outputs:
             poison(dq), poison(dk), poison(dv)
-            ws.fill_(0xFF)  # NaN bit patterns in the float32 workspace
-        dq, dk, dv = A.bwd(q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws, **kw)
+            ws.fill_(0xFF)  # NaN bit patterns in the float32 workspace (and in kept G_S)
+        dq, dk, dv = A.bwd(q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws, keep_gs=keep_gs, **kw)
         res.update({"GQ": dq, "GK": dk, "GV": dv})
     torch.cuda.synchronize()
     return res

@@ -108,6 +108,30 @@ def test_calls_reject_before_any_launch():
     assert A.status_string(A.EMPTY_ROW).startswith("an active query row")
 
 
+def test_gs_backward_errors_before_any_device_work():
+    """attn_bwd_gs and attn_bwd_gs_stage check the stage, the problem and the
+    workspace (which must also hold G_S) on the host before any launch."""
+    L = lib_or_skip()
+    fake = ctypes.c_void_p(0x10000)
+    null = ctypes.c_void_p(0)
+    p = A.make_problem(8, 32, 8, 4096, 4096, 128, 128, A.BF16)  # a grid the passes do not divide
+    m, keep = A.make_mask(causal=True)
+    args = [fake] * 9
+    small = ctypes.c_size_t(A.workspace_size(p))  # enough for attn_bwd, not for G_S
+    assert A.gs_workspace_size(p) > small.value
+    assert L.attn_bwd_gs(ctypes.byref(p), ctypes.byref(m), *args, fake, small, null) == A.WORKSPACE
+    for stage in (0, 1, 2):
+        assert L.attn_bwd_gs_stage(ctypes.byref(p), ctypes.byref(m), *args, fake, small,
+                                   ctypes.c_int32(stage), null) == A.WORKSPACE
+    for stage in (-1, 3):
+        assert L.attn_bwd_gs_stage(ctypes.byref(p), ctypes.byref(m), *args, fake,
+                                   ctypes.c_size_t(A.gs_workspace_size(p)), ctypes.c_int32(stage),
+                                   null) == A.INVALID_ARG
+    m2, keep2 = A.make_mask(causal=True, offset=-1)  # an active row with no visible key
+    assert L.attn_bwd_gs(ctypes.byref(p), ctypes.byref(m2), *args, fake,
+                         ctypes.c_size_t(A.gs_workspace_size(p)), null) == A.EMPTY_ROW
+
+
 def test_noalloc_backward_errors_before_any_device_work():
     """attn_bwd_noalloc checks the problem and its fixed workspace's size on
     the host before it touches a device (so these run without a GPU)."""
@@ -142,6 +166,24 @@ def test_workspace_size():
     assert A.workspace_size(prob(B=0)) == 0
     # float32 (no head split) with few keys (no key split): the per-row arrays only
     assert A.workspace_size(prob(B=3, H_q=4, n_q=100, d_h=128, dtype=A.F32)) == 2 * _al(3 * 4 * 100 * 4)
+
+
+def test_gs_workspace_size():
+    """attn_bwd_gs keeps G_S: the per-row arrays plus one 4 KB block per
+    (sequence, query head, 32-row block, 128-key block, 64-key half); float32
+    problems and grids the two-pass backward would divide need only
+    attn_bwd's workspace (attn_bwd_gs runs attn_bwd for them)."""
+    lib_or_skip()
+    p = prob(B=8, H_q=32, H_kv=8, n_q=4096, n_k=4096, d_h=128, d_v=128)
+    assert A.gs_workspace_size(p) == 2 * _al(8 * 32 * 4096 * 4) + _al(8 * 32 * 128 * 32 * 8192)
+    p = prob(B=2, H_q=4, H_kv=2, n_q=300, n_k=500, d_h=64, d_v=128)
+    if A.workspace_size(p) == 2 * _al(2 * 4 * 300 * 4):  # not divided
+        assert A.gs_workspace_size(p) == A.workspace_size(p) + _al(2 * 4 * 10 * 4 * 8192)
+    f32 = prob(B=3, H_q=4, n_q=100, d_h=128, dtype=A.F32)
+    assert A.gs_workspace_size(f32) == A.workspace_size(f32)
+    small = prob(B=1, H_q=8, H_kv=1, n_q=128, n_k=4096, d_h=128, d_v=128)  # divided passes
+    assert A.workspace_size(small) > 2 * _al(8 * 128 * 4)
+    assert A.gs_workspace_size(small) == A.workspace_size(small)
 
 
 def test_workspace_size_divided_passes():

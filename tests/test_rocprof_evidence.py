@@ -144,3 +144,10 @@ def test_recorded_commands_profile_the_committed_benchmark():
         assert sum(n.startswith("GRBM_") for n in names) <= 2
         if any(n in ("FETCH_SIZE", "WRITE_SIZE") for n in names):
             assert len(names) == 1
+
+
+def test_short_name_mangled_and_demangled():
+    """The profiler reports some kernel names mangled, others demangled."""
+    assert R.short_name("_ZN4attn15bwd_rows_kernelIDF16bLi128EEEvNS_12KernelParamsE") == "bwd_rows_kernel"
+    assert R.short_name("void attn::bwd_dq_gs_kernel<128>(attn::KernelParams)") == "bwd_dq_gs_kernel"
+    assert R.short_name("void at::native::elementwise_kernel<128, 2>(int)") is None
