@@ -116,11 +116,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_gs_kernel(const KernelParams p)
   if (ntiles > 0) {
     TrOffsets<T, DH> kto;
     kto.init(lane);
-    // this wave's blocks: tile t is block t of (sequence, KV head, head rr,
-    // 32-row block), 4 KB each
+    // this wave's blocks (tile-major, 4 KB each): tile t's lies g_step
+    // bytes after tile t - 1's, and the workgroup's waves read adjacent ones
+    const size_t g_step = (size_t)p.gs_nqb * p.group * 4096;
     const char* gsw = reinterpret_cast<const char*>(p.gs) +
-                      ((((size_t)(b * p.H_kv + g) * p.group + (head_ok ? rr : 0)) * p.gs_nqb + (size_t)(w_lo / 32)) *
-                       p.gs_nkb) * 2 * 4096;
+                      ((size_t)(b * p.H_kv + g) * 2 * p.gs_nkb * p.gs_nqb + (size_t)(w_lo / 32)) * p.group * 4096 +
+                      (size_t)(head_ok ? rr : 0) * 4096;
     // Every tile issues the same loads (the K-tile copies and four G_S
     // operand loads per lane), so each wait below is a fixed count: K rows
     // at or past L_k lie outside the K resource and read as zeros, and a G_S
@@ -138,21 +139,26 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_gs_kernel(const KernelParams p)
       else return k_lds2;
     };
     op_t gr[PF][4];
-    auto issue = [&](int t, auto I) __attribute__((always_inline)) {
+    auto issue = [&](int t, auto I, auto LOADG) __attribute__((always_inline)) {
       constexpr int i = decltype(I)::value;
       KL::issue_buf_full(k_rs, (uint32_t)(t * BN) * k_srb, k_off, kbuf(I), tid);
-      const __amdgpu_buffer_rsrc_t g_rs = buf_rsrc(gsw + (size_t)t * 4096, t < wtiles ? 4096u : 0u);
+      if constexpr (decltype(LOADG)::value) {
+        const __amdgpu_buffer_rsrc_t g_rs = buf_rsrc(gsw + (size_t)t * g_step, t < wtiles ? 4096u : 0u);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        gr[i][j] = __builtin_bit_cast(op_t, __builtin_amdgcn_raw_buffer_load_b128(g_rs, lane * 16 + j * 1024, 0, 0));
+        for (int e = 0; e < 4; ++e)
+          gr[i][e] = __builtin_bit_cast(op_t, __builtin_amdgcn_raw_buffer_load_b128(g_rs, lane * 16 + e * 1024, 0, 0));
+      }
     };
-    constexpr int PER = KL::N + 4;  // loads per tile and lane
-    // tile t: loads of tile t + 2 into the stage tile t - 1 used (free since
-    // the last barrier), tile t's products, then a barrier after waiting for
-    // everything but tile t + 2's loads
-    auto step = [&](int t, auto I) __attribute__((always_inline)) {
+    // Tile t issues tile t + 2's loads into the stage tile t - 1 used (free
+    // since the last barrier), multiplies tile t, then waits for everything
+    // but tile t + 2's loads.  The last round's steps load no G_S (nothing
+    // would read it: the compiler would drop such loads and the fixed count
+    // would then no longer cover tile t + 1), so they wait for all but the
+    // K copies of tile t + 2.
+    auto step = [&](int t, auto I, auto TAIL) __attribute__((always_inline)) {
       constexpr int i = decltype(I)::value;
-      issue(t + 2, IC<(i + 2) % PF>());
+      constexpr bool tail = decltype(TAIL)::value;
+      issue(t + 2, IC<(i + 2) % PF>(), IC<!tail>());
       if (t < wtiles) {
 #pragma unroll
         for (int mt = 0; mt < BN / 32; ++mt)
@@ -161,17 +167,24 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_gs_kernel(const KernelParams p)
 #pragma unroll
             for (int dt = 0; dt < DH / 32; ++dt) mma(acc[dt], kto.read(kbuf(I), 32 * mt + 16 * st, dt), gr[i][mt * 2 + st]);
       }
-      stage_barrier<PER>();
+      stage_barrier<tail ? KL::N : KL::N + 4>();
     };
-    issue(0, IC<0>());
-    issue(1, IC<1>());
-    stage_barrier<PER>();
-    for (int t = 0; t < ntiles; t += 3) {
-      step(t, IC<0>());
-      if (t + 1 >= ntiles) break;
-      step(t + 1, IC<1>());
-      if (t + 2 >= ntiles) break;
-      step(t + 2, IC<2>());
+    issue(0, IC<0>(), IC<1>());
+    issue(1, IC<1>(), IC<1>());
+    stage_barrier<KL::N + 4>();
+    // Whole rounds of three tiles in the loop and the rest after it: an exit
+    // from inside the loop body would reach the loop head on the compiler's
+    // paths with the latest G_S stage still in flight, and it would then wait
+    // for that stage at the head.
+    int t = 0;
+    for (; t + 3 <= ntiles; t += 3) {
+      step(t, IC<0>(), IC<0>());
+      step(t + 1, IC<1>(), IC<0>());
+      step(t + 2, IC<2>(), IC<0>());
+    }
+    if (t < ntiles) {
+      step(t, IC<0>(), IC<1>());
+      if (t + 1 < ntiles) step(t + 1, IC<1>(), IC<1>());
     }
     // no copy may still be writing LDS when the workgroup ends
     wait_tile_loads();

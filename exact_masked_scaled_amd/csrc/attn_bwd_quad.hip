@@ -493,9 +493,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
     // G_S kept: the step XD forms G_S of next, and this (sequence, KV head,
     // key block, half)'s blocks (one per query head and 32-row block)
     int xd_rr = rr_lo, xd_qb = qb_first;
-    gop_t* const gs_kh = GS ? (gop_t*)p.gs +
-                                  ((size_t)(b * p.H_kv + g) * p.group * p.gs_nqb * p.gs_nkb + kb) * 512 + h * 256
-                            : nullptr;
+    gop_t* const gs_kh =
+        GS ? (gop_t*)p.gs + ((size_t)(b * p.H_kv + g) * 2 * p.gs_nkb + 2 * kb + h) * p.gs_nqb * p.group * 256
+           : nullptr;
     // after a copy: move on to the next step while one is left (past the last
     // step the copies repeat it, into stages no later step reads)
     auto next = [&](int s_copied, int& rr, int& qb) __attribute__((always_inline)) {
@@ -557,7 +557,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_quad_kernel(const KernelParam
         op_t* xw = xch + (3 + (u & 1)) * XSLOT;         // G_S(s - 2)
         const bool mf = !ramp || (s >= 1 && s <= nsteps), ex = !ramp || (s >= 2 && s <= nsteps + 1);
         gop_t* gsb = nullptr;
-        if constexpr (GS) gsb = gs_kh + ((size_t)xd_rr * p.gs_nqb + xd_qb) * p.gs_nkb * 512;
+        if constexpr (GS) gsb = gs_kh + ((size_t)xd_qb * p.group + xd_rr) * 256;
         if (mf && ex) xd_iter(TR(), TR(), IC<jd>(), Os, rows, pin, xw, gsb);
         else if constexpr (ramp) {
           if (ex) xd_iter(F(), TR(), IC<jd>(), Os, rows, pin, xw, gsb);

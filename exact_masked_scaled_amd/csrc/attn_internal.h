@@ -75,15 +75,14 @@ struct KernelParams {
   void* qt;
   int64_t qt_sb, qt_sh, qt_sr;
   // backward keeping G_S (bf16): the dK/dV pass writes each step's G_S as
-  // 4 KB blocks, block ((((b * H_kv + g) * group + rr) * gs_nqb + qb) * gs_nkb
-  // + kb) * 2 + half for query head rr of the group, 32-row block qb, 128-key
-  // block kb and its 64-key half; the dQ pass then reads them instead of
-  // recomputing S and dP.  Null when not used.
+  // 4 KB blocks, block (((b * H_kv + g) * 2 gs_nkb + t) * gs_nqb + qb) * group
+  // + rr for 64-key tile t (half t % 2 of 128-key block t / 2), 32-row block
+  // qb and query head rr of the group (tile-major, so the blocks the G_Q
+  // product reads together, and the ones the dK/dV pass writes in a row, lie
+  // side by side); the G_Q product then reads them instead of recomputing S
+  // and dP.  Null when not used.
   void* gs;
   int32_t gs_nqb, gs_nkb;
-  // dQ pass mode: 0 the full pass (D, S, dP, G_S, G_Q), 1 only the per-row
-  // -D and lse log2 e, 2 G_Q from the kept G_S blocks
-  int32_t dq_mode;
   int32_t lens_q[kMaxBatchChunk];
   int32_t lens_k[kMaxBatchChunk];
   int32_t offs[kMaxBatchChunk];    // causal offsets, clamped to [0, n_k]

@@ -96,3 +96,30 @@ def test_bwd_gs_stages_equal_one_call():
     two = A.bwd(q, k, v, o, lse, do, causal=True)
     for a, b in zip(two[1:], (dk, dv)):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_bwd_gs_repeatable_full_size():
+    """The headline workload at full size (long key ranges: many rounds of
+    the product pass's tile ring and every remainder length): three G_S
+    backwards give bit-identical results, and G_K, G_V equal the two-pass
+    backward's, so no stage of either pass is read before it has landed."""
+    import torch
+    from exact_masked_scaled_amd import attn as A
+
+    inp = W.make_inputs(3)
+    wl = inp.wl
+    P.say(f"[bwd_gs] repeatable full size: {wl.describe()}")
+    kw = inp.mask_kwargs()
+    q, k, v, do = (P.to_device(x) for x in (inp.Q, inp.K, inp.V, inp.GO))
+    o, lse = A.fwd(q, k, v, **kw)
+    prob = A._problem_from(q, k, v, A._strides(o))
+    assert A.gs_workspace_size(prob) > A.workspace_size(prob)
+    ws = torch.empty(A.gs_workspace_size(prob), dtype=torch.uint8, device=q.device)
+    first = [t.clone() for t in A.bwd(q, k, v, o, lse, do, workspace=ws, keep_gs=True, **kw)]
+    for _ in range(2):
+        again = A.bwd(q, k, v, o, lse, do, workspace=ws, keep_gs=True, **kw)
+        for n, a, b in zip(("G_Q", "G_K", "G_V"), first, again):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), n
+    two = A.bwd(q, k, v, o, lse, do, **kw)
+    for n, a, b in zip(("G_K", "G_V"), first[1:], two[1:]):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), n

@@ -81,29 +81,33 @@ def test_workload1_full():
 
 
 FULL_SIZE = [(1, "bench"), (2, "bench"), (3, "bench"), (4, "bench"), (5, "bench"),
-             (1, "unsplit"), (4, "unsplit"), (5, "unsplit")]
+             (1, "unsplit"), (4, "unsplit"), (5, "unsplit"), (2, "two-pass"), (3, "two-pass")]
 
 
 @pytest.mark.parametrize("wid,forward", FULL_SIZE, ids=lambda x: str(x))
 @pytest.mark.timeout(900)
 def test_full_size_every_group(wid, forward):
-    """The five workloads at full size, with the forward the benchmark runs
-    ("bench": split over the keys with the automatic part count where that
-    divides the problem, else unsplit) or the unsplit forward: every element
-    of O, lse, G_Q, G_K and G_V against the float64 oracle, one (sequence,
-    KV head) group at a time, plus the structural zeros of padded keys and
-    inactive rows."""
+    """The five workloads at full size, with the forward and backward the
+    benchmark runs ("bench": split over the keys with the automatic part
+    count where that divides the problem, else unsplit; the backward keeping
+    G_S where the library supports it, else the two passes), the unsplit
+    forward, or the benchmark's forward with the two-pass backward
+    ("two-pass"): every element of O, lse, G_Q, G_K and G_V against the
+    float64 oracle, one (sequence, KV head) group at a time, plus the
+    structural zeros of padded keys and inactive rows."""
     inp = W.make_inputs(wid)
     wl = inp.wl
     prob = A.make_problem(wl.B, wl.H_q, wl.H_kv, wl.n_q, wl.n_k, wl.d_h, wl.d_v,
                           A.BF16 if wl.dtype == W.BF16 else A.F32)
-    ns = P.bench_forward_splits(prob) if forward == "bench" else 1
-    label = f"workload {wid} ({'split forward, automatic parts' if ns == 0 else 'unsplit forward'})"
+    ns = P.bench_forward_splits(prob) if forward != "unsplit" else 1
+    gs = forward == "bench" and A.gs_workspace_size(prob) > A.workspace_size(prob)
+    label = (f"workload {wid} ({'split forward, automatic parts' if ns == 0 else 'unsplit forward'}, "
+             f"{'G_S kept' if gs else 'two-pass'} backward)")
     P.say(f"[parity] {label}: {wl.describe()} lens_k={inp.seqlens_k}")
-    gpu = P.run_gpu(inp, num_splits=ns)
+    gpu = P.run_gpu(inp, num_splits=ns, keep_gs=gs)
     errs = P.compare_groups(inp, gpu, progress=8)
     P.record(f"workload {wid}", errs, forward="split" if ns == 0 else "unsplit", dtype=wl.dtype,
-             elements={n: int(t.numel()) for n, t in gpu.items()})
+             backward="G_S kept" if gs else "two-pass", elements={n: int(t.numel()) for n, t in gpu.items()})
     P.assert_within(errs, wl.dtype, label)
     if inp.seqlens_k:
         for b, L in enumerate(inp.seqlens_k):
