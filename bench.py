@@ -239,7 +239,8 @@ def measure(torch, attn, W, wl, uniform_len, steps, warmup, packed=False, keep_g
 
 def measure_forward_split(torch, attn, W, wl, steps, warmup):
     """Forward only, unsplit (attn_fwd) against split over the keys
-    (attn_fwd_splitkv, automatic part count), inputs resident; ms per call."""
+    (attn_fwd_splitkv, automatic part count), inputs resident; median ms per
+    call."""
     import numpy as np
 
     inp = W.make_inputs(wl, with_grad=False) if wl.wid in W.WORKLOADS else \
@@ -263,13 +264,17 @@ def measure_forward_split(torch, attn, W, wl, steps, warmup):
     for name, fn in calls.items():
         for _ in range(warmup):
             fn()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(steps):
-            fn()
-        e1.record(stream)
         torch.cuda.synchronize()
-        out[name] = e0.elapsed_time(e1) / steps
+        # one event pair per call and the median: these calls last tens of
+        # microseconds, so a stall of the submitting thread would otherwise
+        # count as GPU time
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for e0, e1 in evs:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        out[name] = float(np.median([e0.elapsed_time(e1) for e0, e1 in evs]))
     work = W.work(wl, inp.seqlens_q, inp.seqlens_k)
     del q, k, v, o, lse, ws
     return out, work
