@@ -138,6 +138,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_gs_kernel(const KernelParams p)
       else if constexpr (decltype(I)::value == 1) return k_lds1;
       else return k_lds2;
     };
+    // G_S is read once: non-temporal loads (cache-policy bit 1, "nt" on
+    // gfx950) keep it from displacing the K tiles the next items reuse
+    // (measured: the pass 0.574 -> 0.533 ms, same box)
+    constexpr int kNonTemporal = 2;
     op_t gr[PF][4];
     auto issue = [&](int t, auto I, auto LOADG) __attribute__((always_inline)) {
       constexpr int i = decltype(I)::value;
@@ -146,7 +150,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_gs_kernel(const KernelParams p)
         const __amdgpu_buffer_rsrc_t g_rs = buf_rsrc(gsw + (size_t)t * g_step, t < wtiles ? 4096u : 0u);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          gr[i][e] = __builtin_bit_cast(op_t, __builtin_amdgcn_raw_buffer_load_b128(g_rs, lane * 16 + e * 1024, 0, 0));
+          gr[i][e] = __builtin_bit_cast(op_t, __builtin_amdgcn_raw_buffer_load_b128(g_rs, lane * 16 + e * 1024, 0, kNonTemporal));
       }
     };
     // Tile t issues tile t + 2's loads into the stage tile t - 1 used (free
