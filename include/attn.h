@@ -205,9 +205,11 @@ attn_status attn_bwd(const attn_problem* prob, const attn_mask* mask,
  * time.  Three steps on `stream`: the per-row -D_i and lse_i * log2(e); the
  * dK/dV pass, which also writes G_S in bf16 to the workspace (2 bytes per
  * (row, key) of every 32-row block against every 128-key block it visits);
- * G_Q as one product over those blocks.  Same arguments and results as
- * attn_bwd up to rounding (G_Q sums the same bf16 G_S in the same key
- * order; G_S itself may round differently from the two-pass dQ pass's).
+ * G_Q as one product over those blocks.  Same arguments as attn_bwd; G_K
+ * and G_V are bitwise attn_bwd's, G_Q agrees up to rounding (it sums the
+ * dK/dV pass's bf16 G_S, which may round differently from the G_S the
+ * two-pass dQ pass recomputes).  G_S is written and read with non-temporal
+ * stores and loads.
  * `workspace` must hold attn_bwd_gs_workspace_size(prob) bytes, 256-byte
  * aligned: attn_bwd's, then the G_S blocks of the whole batch (B * H_q *
  * ceil(n_q / 32) * ceil(n_k / 128) * 8 KB; 8.6 GB for B = 8, H_q = 32,
