@@ -130,6 +130,13 @@ def kernel_report(wl, work, kern_ms):
            "bwd_rows": 0, "bwd_dq_gs": 2 * P * dh}
     executed = {"fwd": 2 * P * (dh + dv_), "bwd_dq": 2 * P * (2 * dh + dv_), "bwd_dkdv": 2 * P * (2 * dh + 2 * dv_),
                 "bwd_rows": 0, "bwd_dq_gs": 2 * P * dh}
+    # the two passes of the G_S backward that are bound by HBM: algorithmic
+    # bytes (per-row pass: O and G_O read, lse read, -D and lse log2 e
+    # written; G_Q product: 2 bytes of G_S per visible pair, K read once,
+    # G_Q written), against the 8 TB/s peak
+    s = 2 if wl.dtype == "bf16" else 4
+    hbm_bytes = {"bwd_rows": work["active_q_rows"] * (2 * dv_ * s + 4 + 8),
+                 "bwd_dq_gs": 2 * P + (work["active_k_rows"] + work["active_q_rows"]) * dh * s}
     kernels = {}
     for n, t in kern_ms.items():
         sec = t * 1e-3
@@ -138,6 +145,9 @@ def kernel_report(wl, work, kern_ms):
                       "frac_of_peak": round(alg[n] / sec / 1e12 / peak, 4),
                       "executed_MFMA_TFLOP/s": round(executed[n] / sec / 1e12, 2),
                       "executed_frac_of_peak": round(executed[n] / sec / 1e12 / peak, 4)}
+        if n in hbm_bytes:
+            kernels[n]["algorithmic_GB/s"] = round(hbm_bytes[n] / sec / 1e9, 1)
+            kernels[n]["frac_of_hbm_peak"] = round(hbm_bytes[n] / sec / 1e9 / PEAK_HBM_GBS, 4)
     dominant = max(kern_ms, key=kern_ms.get)
     return kernels, dominant, alg[dominant] / (kern_ms[dominant] * 1e-3) / 1e12
 

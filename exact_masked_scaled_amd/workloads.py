@@ -267,7 +267,13 @@ def work(wl: Workload, seqlens_q=None, seqlens_k=None) -> dict:
     v = wl.B * wl.H_kv * wl.n_k * wl.d_v * s
     o = wl.B * wl.H_q * wl.n_q * wl.d_v * s
     rows = wl.B * wl.H_q * wl.n_q * 4
+    lq = seqlens_q if seqlens_q is not None else [wl.n_q] * wl.B
+    lk = seqlens_k if seqlens_k is not None else [wl.n_k] * wl.B
     return {
+        # rows the kernels read or write: active query rows of every query
+        # head, key rows below L_k of every KV head
+        "active_q_rows": sum(lq) * wl.H_q,
+        "active_k_rows": sum(lk) * wl.H_kv,
         "pairs": pairs,
         "pairs_per_sequence": pairs_b,
         "fwd_flop": 2 * pairs * (wl.d_h + wl.d_v),
