@@ -66,11 +66,11 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(const KernelParams p) {
 // pass's key-tile loop and G_Q products without S, dP and the exponentials.
 // The dK/dV pass wrote each block of G_S as this product's four B operands
 // (lane = query row, eight keys each; 1 KB per operand), so a wave loads
-// them straight into registers.  The loads through each CU bound this pass,
-// so the K tile (through LDS) serves eight waves: the heads of the KV group
-// side by side (hw = min(group, 8) of them, 32 * (8 / hw) positions each),
-// which also gives the waves nearly the same key range.  K tiles and G_S operands run
-// two tiles ahead.  A wave uses only tiles its rows see; the dK/dV pass
+// them straight into registers.  Reading G_S from HBM bounds this pass
+// (2 bytes per visible pair), so the K tile (through LDS) serves eight
+// waves: the heads of the KV group side by side (hw = min(group, 8) of them,
+// 32 * (8 / hw) positions each), which also gives the waves nearly the same
+// key range.  K tiles and G_S operands run two tiles ahead.  A wave uses only tiles its rows see; the dK/dV pass
 // wrote each such block (its key block's query range starts at or before
 // the wave's rows), and invisible pairs inside them hold exact zeros.
 template <int DH>
@@ -122,8 +122,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_gs_kernel(const KernelParams p)
     const char* gsw = reinterpret_cast<const char*>(p.gs) +
                       ((size_t)(b * p.H_kv + g) * 2 * p.gs_nkb * p.gs_nqb + (size_t)(w_lo / 32)) * p.group * 4096 +
                       (size_t)(head_ok ? rr : 0) * 4096;
-    // Every tile issues the same loads (the K-tile copies and four G_S
-    // operand loads per lane), so each wait below is a fixed count: K rows
+    // Every tile of the loop issues the same loads (the K-tile copies and
+    // four G_S operand loads per lane), so each wait below is a fixed count: K rows
     // at or past L_k lie outside the K resource and read as zeros, and a G_S
     // block past the wave's tiles has an empty resource (zeros, no memory
     // access).  K row offsets fit 32 bits (checked on the host).
