@@ -8,7 +8,9 @@ product's eight waves, and more than eight), MQA and MHA heads, both head
 widths, the causal
 rule with one offset and one per sequence, ragged and empty sequences, and
 the random sweep's bf16 problems (those whose grids would be divided run the
-two-pass backward, which attn_bwd_gs falls back to)."""
+two-pass backward, which attn_bwd_gs falls back to), 130 sequences over two
+launches, the packed layout, the three stages against the one call, and
+repeatability at full size."""
 
 import zlib
 
@@ -123,3 +125,81 @@ def test_bwd_gs_repeatable_full_size():
     two = A.bwd(q, k, v, o, lse, do, **kw)
     for n, a, b in zip(("G_K", "G_V"), first[1:], two[1:]):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16)), n
+
+
+def _takes_gs(B, H_q, H_kv, n_q, n_k, d):
+    from exact_masked_scaled_amd import attn as A
+    p = A.make_problem(B, H_q, H_kv, n_q, n_k, d, d, A.BF16)
+    return A.gs_workspace_size(p) > A.workspace_size(p)
+
+
+def test_bwd_gs_many_sequences_chunked():
+    """130 sequences (two launches of at most 128 each: the second launch's
+    G_S blocks start at its first sequence's) with their own lengths and
+    offsets, on a grid the passes do not divide, against the oracle."""
+    import numpy as np
+
+    rng = np.random.default_rng(4242)
+    B, H_q, H_kv, n, d = 130, 8, 2, 200, 128
+    assert _takes_gs(B, H_q, H_kv, n, n, d)
+    lq = [int(x) for x in rng.integers(0, n + 1, size=B)]
+    lk = [int(x) for x in rng.integers(1, n + 1, size=B)]
+    offs = [int(rng.integers(0, k_ + 1)) for k_ in lk]
+    name = "gs_many_seqs"
+    P.say(f"[bwd_gs] {name} B={B} H_q={H_q} H_kv={H_kv} n={n}")
+    wl = W.custom_workload(W.BF16, B, H_q, H_kv, n, n, d, d, True, 0, name)
+    inp = W.make_custom_inputs(wl, seed=91, seqlens_q=lq, seqlens_k=lk)
+    kw = dict(causal=True, offset=offs, seqlens_q=lq, seqlens_k=lk)
+    inp.mask_kwargs = lambda: kw
+    gpu = P.run_gpu(inp, keep_gs=True)
+    errs, _ = P.compare_full(inp, gpu)
+    P.assert_within(errs, W.BF16, name)
+    for b in range(B):
+        assert (P.to_f64(gpu["GQ"][b, :, lq[b]:]) == 0).all(), "G_Q of inactive rows"
+
+
+def test_bwd_gs_packed_layout():
+    """The packed layout ([rows, H, d] tensors, row offsets per sequence)
+    through attn_bwd_gs on a grid the passes do not divide: against the
+    packed oracle, and nothing written past the packed rows."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from exact_masked_scaled_amd import attn as A
+
+    lq = [700, 300, 1000, 513]
+    B, H_q, H_kv, d = len(lq), 32, 8, 128
+    n = max(lq)
+    assert _takes_gs(B, H_q, H_kv, n, n, d)
+    name = "gs_packed"
+    P.say(f"[bwd_gs] {name} lens={lq}")
+    wl = W.custom_workload(W.BF16, B, H_q, H_kv, n, n, d, d, True, 0, name)
+    inp = W.make_custom_inputs(wl, seed=5150)
+
+    def pack(X):
+        return np.ascontiguousarray(np.concatenate([X[b, :, :L].transpose(1, 0, 2) for b, L in enumerate(lq)], 0))
+
+    cu = np.concatenate([[0], np.cumsum(lq)]).astype(int).tolist()
+    Qp, Kp, Vp, GOp = pack(inp.Q), pack(inp.K), pack(inp.V), pack(inp.GO)
+    q, k, v, do = (P.to_device(x) for x in (Qp, Kp, Vp, GOp))
+    pk = dict(causal=True, offset=0, cu_seqlens_q=cu, cu_seqlens_k=cu)
+    o, lse = A.fwd(q, k, v, **pk)
+    rows, slack, sentinel = cu[-1], 16, 7.0
+    bufs = {nm: torch.full((rows + slack, H, d), sentinel, dtype=q.dtype, device=q.device)
+            for nm, H in (("GQ", H_q), ("GK", H_kv), ("GV", H_kv))}
+    dq, dk, dv = (bufs[nm][:rows] for nm in ("GQ", "GK", "GV"))
+    for t in (dq, dk, dv):
+        t.fill_(float("nan"))
+    prob = A._problem_from(q, k, v, A._strides(o), cu, cu)
+    ws = torch.full((A.gs_workspace_size(prob),), 0xFF, dtype=torch.uint8, device=q.device)
+    A.bwd(q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws, keep_gs=True, **pk)
+    torch.cuda.synchronize()
+    f64 = W.payload_to_f64
+    ref = oracle.attention_backward_packed(f64(Qp), f64(Kp), f64(Vp), f64(GOp), cu, cu, causal=True, offset=0)
+    errs = {"O": P.rel_err(P.to_f64(o), ref["O"]), "lse": P.rel_err(P.to_f64(lse), ref["lse"]),
+            "GQ": P.rel_err(P.to_f64(dq), ref["GQ"]), "GK": P.rel_err(P.to_f64(dk), ref["GK"]),
+            "GV": P.rel_err(P.to_f64(dv), ref["GV"])}
+    P.assert_within(errs, W.BF16, name)
+    for nm, buf in bufs.items():
+        assert (P.to_f64(buf[rows:]) == sentinel).all(), f"{nm} written past its rows"
