@@ -95,6 +95,68 @@ def test_forward_and_backward_replay_in_a_graph():
         P.say(f"[graph] replay {rep} matches")
 
 
+def test_gs_backward_replays_in_a_graph():
+    """attn_bwd_gs (G_S kept in the workspace, three launches, no memset)
+    captured with the forward: every replay reproduces the eager call."""
+    import torch
+    B, H_q, H_kv, n, d = 4, 32, 8, 800, 128
+    kw = dict(causal=True, offset=0, seqlens_q=[800, 513, 700, 64], seqlens_k=[800, 513, 700, 64])
+    prob0 = A.make_problem(B, H_q, H_kv, n, n, d, d, A.BF16)
+    assert A.gs_workspace_size(prob0) > A.workspace_size(prob0)  # the G_S path, not its fallback
+    P.say(f"[graph] G_S backward bf16 B={B} H_q={H_q} H_kv={H_kv} n={n} d={d}")
+    wl = W.custom_workload(W.BF16, B, H_q, H_kv, n, n, d, d, True, 0, "graph_gs")
+    sets = [W.make_custom_inputs(wl, seed=zlib.crc32(f"graph_gs{i}".encode()) % 10000,
+                                 seqlens_q=kw["seqlens_q"], seqlens_k=kw["seqlens_k"]) for i in range(2)]
+    host = [{k: P.to_device(getattr(s, k)) for k in ("Q", "K", "V", "GO")} for s in sets]
+    q, k, v, do = (torch.empty_like(host[0][x]) for x in ("Q", "K", "V", "GO"))
+    o = torch.empty_like(do)
+    lse = torch.empty(B, H_q, n, dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    prob = A._problem_from(q, k, v, A._strides(o))
+    ws = torch.empty(A.gs_workspace_size(prob), dtype=torch.uint8, device="cuda")
+
+    def step():
+        A.fwd(q, k, v, out=o, lse=lse, **kw)
+        A.bwd(q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws, keep_gs=True, **kw)
+
+    def load(i):
+        for dst, key in ((q, "Q"), (k, "K"), (v, "V"), (do, "GO")):
+            dst.copy_(host[i][key])
+        for t in (o, lse, dq, dk, dv):
+            P.poison(t)
+        ws.fill_(0xFF)  # stale G_S would show as NaN
+
+    outs = (o, lse, dq, dk, dv)
+    eager = []
+    for i in range(2):
+        load(i)
+        step()
+        torch.cuda.synchronize()
+        eager.append([t.clone() for t in outs])
+        sets[i].mask_kwargs = lambda: kw
+        errs, _ = P.compare_full(sets[i], {"O": o, "lse": lse, "GQ": dq, "GK": dk, "GV": dv})
+        P.assert_within(errs, W.BF16, f"G_S graph eager set {i}")
+
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep, i in enumerate([0, 1, 1, 0]):
+        load(i)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, got, want in zip(("O", "lse", "GQ", "GK", "GV"), outs, eager[i]):
+            assert torch.equal(got, want), f"replay {rep} (input set {i}): {name} differs from the eager call"
+        P.say(f"[graph] G_S replay {rep} matches")
+
+
 @pytest.mark.parametrize("dtype", [W.BF16, W.F32])
 def test_linear_backward_over_no_rows_gives_zero_weight_gradient(dtype):
     """With no rows, G_W = X^T G_Y is an empty sum: exactly zero (or left
