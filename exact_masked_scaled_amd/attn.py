@@ -447,8 +447,9 @@ NOALLOC_MAX_WORKSPACE = 64 << 20  # ATTN_BWD_NOALLOC_MAX_WORKSPACE
 
 
 class StagedBackward:
-    """The backward's two ABI passes bound to fixed tensors, for callers that
-    time or schedule them separately (dq() then dkdv() equals one bwd())."""
+    """The backward's ABI passes bound to fixed tensors, for callers that
+    time or schedule them separately: dq() then dkdv() equals one bwd();
+    gs_stage(0), (1), (2) equals one bwd(keep_gs=True)."""
 
     def __init__(self, q, k, v, o, lse, do, dq, dk, dv, workspace, *, causal=False, offset=0,
                  seqlens_q=None, seqlens_k=None, cu_seqlens_q=None, cu_seqlens_k=None,
